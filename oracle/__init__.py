@@ -1,0 +1,177 @@
+"""CPU oracle of the DFlash 2 path selector -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  It wraps ``liboracle.so`` (plain C,
+fp64, OpenMP; see ``oracle.h``) with numpy in / numpy out, and shares no code
+with the HIP path.
+
+Every function below is pinned by the ``-m "not gpu"`` tests against brute
+force, library routines, closed forms and invariants (``tests/test_oracle_*``).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from typing import Dict, Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+K = 16
+GREEDY, SAMPLED = 0, 1
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``liboracle.so`` with gcc (-O2, no fast-math)."""
+    if force or not os.path.exists(_SO):
+        cmd = ["gcc", "-O2", "-fopenmp", "-std=c11", "-Wall", "-shared", "-fPIC",
+               "-o", _SO, os.path.join(_HERE, "oracle.c"), "-lm"]
+        subprocess.run(cmd, check=True)
+    return _SO
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        lib = C.CDLL(_SO)
+        P, I64, I32, D = C.c_void_p, C.c_int64, C.c_int, C.c_double
+        sig = {
+            "ora_select_topk": [P, I32, I64, I64, I64, P, P],
+            "ora_project": [P, I64, I64, P, P, P, I64, P, P, P, I64, I64, P, P, P],
+            "ora_score_pairs": [P, P, P, P, I64, I64, I64, P],
+            "ora_step": [P, I32, I32, D, D, P, P, P],
+            "ora_walk": [P, P, P, D, I32, I64, I64, P, P, P, P, P],
+            "ora_step_table": [P, P, D, I32, I64, I64, P, P],
+        }
+        for name, args in sig.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = C.c_int
+        _lib = lib
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with status {rc}")
+
+
+def select_topk(logits: np.ndarray, vocab: Optional[int] = None):
+    """Top-16 of every row.  ``logits[..., ld]``: float32, or uint16 bf16 bits.
+
+    Returns ``cand_id`` int32 and ``cand_u`` float32, shape ``[..., 16]``.
+    """
+    x = np.ascontiguousarray(logits)
+    if x.dtype == np.float32:
+        dt = 0
+    elif x.dtype == np.uint16:
+        dt = 1
+    else:
+        raise TypeError("logits must be float32 or uint16 (bf16 bits)")
+    ld = x.shape[-1]
+    V = ld if vocab is None else int(vocab)
+    rows = int(np.prod(x.shape[:-1]))
+    cid = np.empty(x.shape[:-1] + (K,), np.int32)
+    cu = np.empty(x.shape[:-1] + (K,), np.float32)
+    _check(_load().ora_select_topk(_p(x), dt, rows, V, ld, _p(cid), _p(cu)), "select_topk")
+    return cid, cu
+
+
+def project(E, W_A, W_B, W_H, h, cand_id, verified):
+    """fp64 ``A_prev [B,L,16,r]``, ``B_cur [B,L,16,r]``, ``G [B,L,r]``."""
+    E = np.ascontiguousarray(E, np.uint16)
+    W_A, W_B, W_H = (np.ascontiguousarray(w, np.uint16) for w in (W_A, W_B, W_H))
+    h = np.ascontiguousarray(h, np.uint16)
+    cand_id = np.ascontiguousarray(cand_id, np.int32)
+    verified = np.ascontiguousarray(verified, np.int32)
+    V, d = E.shape
+    r = W_A.shape[0]
+    B, L = cand_id.shape[:2]
+    assert W_A.shape == W_B.shape == W_H.shape == (r, d) and h.shape == (B, L, d)
+    assert cand_id.shape == (B, L, K) and verified.shape == (B,)
+    A = np.empty((B, L, K, r), np.float64)
+    Bm = np.empty((B, L, K, r), np.float64)
+    G = np.empty((B, L, r), np.float64)
+    rc = _load().ora_project(_p(E), V, d, _p(W_A), _p(W_B), _p(W_H), r, _p(h), _p(cand_id),
+                             _p(verified), B, L, _p(A), _p(Bm), _p(G))
+    _check(rc, "project")
+    return A, Bm, G
+
+
+def score_pairs(cand_u, A_prev, B_cur, G):
+    """fp64 ``S [B,L,16,16]``."""
+    cand_u = np.ascontiguousarray(cand_u, np.float32)
+    A_prev = np.ascontiguousarray(A_prev, np.float64)
+    B_cur = np.ascontiguousarray(B_cur, np.float64)
+    G = np.ascontiguousarray(G, np.float64)
+    B, L, _, r = A_prev.shape
+    S = np.empty((B, L, K, K), np.float64)
+    _check(_load().ora_score_pairs(_p(cand_u), _p(A_prev), _p(B_cur), _p(G), B, L, r, _p(S)),
+           "score_pairs")
+    return S
+
+
+def step(S_bt, row: int, mode: int = GREEDY, u: float = 0.0, T: float = 1.0):
+    """One walk step from predecessor ``row`` of a 16x16 score table.
+
+    Returns ``(choice, aux, q)``: aux is the top-2 gap (greedy) or the CDF margin
+    over Z (sampled)."""
+    S_bt = np.ascontiguousarray(S_bt, np.float64)
+    assert S_bt.shape == (K, K)
+    ch = C.c_int(0)
+    aux = C.c_double(0)
+    q = np.empty(K, np.float64)
+    _check(_load().ora_step(_p(S_bt), int(row), int(mode), float(u), float(T), C.byref(ch),
+                            C.byref(aux), _p(q)), "step")
+    return ch.value, aux.value, q
+
+
+def walk(S, cand_id, mode: int = GREEDY, uniforms=None, T: float = 1.0):
+    """Walk every block from the verified token.
+
+    Returns dict with ``path_tok``, ``path_slot`` int32 ``[B,L]``, ``path_s``,
+    ``aux`` float64 ``[B,L]`` and ``q`` float64 ``[B,L,16]``."""
+    S = np.ascontiguousarray(S, np.float64)
+    cand_id = np.ascontiguousarray(cand_id, np.int32)
+    B, L = S.shape[:2]
+    u = None if uniforms is None else np.ascontiguousarray(uniforms, np.float32)
+    out = dict(path_tok=np.empty((B, L), np.int32), path_slot=np.empty((B, L), np.int32),
+               path_s=np.empty((B, L), np.float64), aux=np.empty((B, L), np.float64),
+               q=np.empty((B, L, K), np.float64))
+    rc = _load().ora_walk(_p(S), _p(cand_id), _p(u), float(T), int(mode), B, L,
+                          _p(out["path_tok"]), _p(out["path_slot"]), _p(out["path_s"]),
+                          _p(out["aux"]), _p(out["q"]))
+    _check(rc, "walk")
+    return out
+
+
+def step_table(S, mode: int = GREEDY, uniforms=None, T: float = 1.0):
+    """Choice and aux of the step from every predecessor row: ``[B,L,16]`` each."""
+    S = np.ascontiguousarray(S, np.float64)
+    B, L = S.shape[:2]
+    u = None if uniforms is None else np.ascontiguousarray(uniforms, np.float32)
+    choice = np.empty((B, L, K), np.int32)
+    aux = np.empty((B, L, K), np.float64)
+    _check(_load().ora_step_table(_p(S), _p(u), float(T), int(mode), B, L, _p(choice), _p(aux)),
+           "step_table")
+    return choice, aux
+
+
+def run(inp: Dict[str, np.ndarray], mode: int = GREEDY, T: float = 1.0, vocab: Optional[int] = None):
+    """The whole selector on one set of inputs (as drawn by ``synth.make``)."""
+    cand_id, cand_u = select_topk(inp["logits"], vocab)
+    A, Bm, G = project(inp["E"], inp["W_A"], inp["W_B"], inp["W_H"], inp["h"], cand_id,
+                       inp["verified"])
+    S = score_pairs(cand_u, A, Bm, G)
+    w = walk(S, cand_id, mode, inp.get("uniforms"), T)
+    return dict(cand_id=cand_id, cand_u=cand_u, A_prev=A, B_cur=Bm, G=G, S=S, **w)

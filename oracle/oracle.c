@@ -1,0 +1,252 @@
+/*
+ * CPU oracle of the DFlash 2 lightweight path selector -- TEST INFRASTRUCTURE.
+ * See oracle.h for the sources and the contract of every function.  Only the
+ * tests, the package smoke check and the benchmark's CPU-baseline leg use it.
+ *
+ * Plain loops, fp64 throughout, OpenMP over independent rows / positions.
+ * No blocking, fusion or reordering beyond the definitions on the pages.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <stddef.h>
+#include <string.h>
+
+static double bf16_to_f64(uint16_t u) {
+    uint32_t bits = (uint32_t)u << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static double logit_at(const void *logits, int dtype, int64_t idx) {
+    if (dtype == 0) return (double)((const float *)logits)[idx];
+    return bf16_to_f64(((const uint16_t *)logits)[idx]);
+}
+
+/* Total order of candidates: is (a, ia) ranked above (b, ib)?
+ * Non-NaN above NaN; larger value first (-0.0 == +0.0 under IEEE compare);
+ * equal values (or two NaNs) -> lower id first. */
+static int ranks_above(double a, int64_t ia, double b, int64_t ib) {
+    int an = isnan(a), bn = isnan(b);
+    if (an != bn) return bn;
+    if (!an && a != b) return a > b;
+    return ia < ib;
+}
+
+/* ---------------------------------------------------------------- top-16 --- */
+/* [P1 Method > Lightweight Path Selector; P3 "Selection beats correction"]:
+ * the selector keeps the 16 best candidates of each draft position.  The first
+ * 16 of the total order above, found by one pass of sorted insertion. */
+int ora_select_topk(const void *logits, int dtype, int64_t rows, int64_t V, int64_t ld,
+                    int32_t *cand_id, float *cand_u) {
+    if (!logits || !cand_id || !cand_u || rows < 0 || V < ORA_K || ld < V) return -1;
+    if (dtype != 0 && dtype != 1) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < rows; ++row) {
+        double val[ORA_K];
+        int64_t id[ORA_K];
+        int n = 0;
+        for (int64_t v = 0; v < V; ++v) {
+            double x = logit_at(logits, dtype, row * ld + v);
+            if (n == ORA_K && !ranks_above(x, v, val[ORA_K - 1], id[ORA_K - 1])) continue;
+            int pos = (n < ORA_K) ? n : ORA_K - 1;     /* slot that gets overwritten */
+            while (pos > 0 && ranks_above(x, v, val[pos - 1], id[pos - 1])) {
+                val[pos] = val[pos - 1];
+                id[pos] = id[pos - 1];
+                --pos;
+            }
+            val[pos] = x;
+            id[pos] = v;
+            if (n < ORA_K) ++n;
+        }
+        for (int k = 0; k < ORA_K; ++k) {
+            cand_id[row * ORA_K + k] = (int32_t)id[k];
+            cand_u[row * ORA_K + k] = (float)val[k];   /* exact: the value came from fp32/bf16 */
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------ projections --- */
+/* y[c] = sum_k W[c,k] x[k] in fp64 (linear-layer layout W[r,d]). */
+static void matvec(const uint16_t *W, const uint16_t *x, int64_t r, int64_t d, double *y) {
+    for (int64_t c = 0; c < r; ++c) {
+        double acc = 0.0;
+        for (int64_t k = 0; k < d; ++k) acc += bf16_to_f64(W[c * d + k]) * bf16_to_f64(x[k]);
+        y[c] = acc;
+    }
+}
+
+/* [P1 Method, eq. S_t and the paragraph after it; P3]: A and B map a token to a
+ * 256-d vector (here A(x) = W_A E[x], B(x) = W_B E[x]); H(h_t) is a gate from the
+ * drafter's hidden state at position t (here sigmoid(W_H h_t)).  Predecessors:
+ * the walk starts from the last verified token, so position 0 has one
+ * predecessor; position t >= 1 has the 16 candidates of position t-1. */
+int ora_project(const uint16_t *E, int64_t V, int64_t d,
+                const uint16_t *W_A, const uint16_t *W_B, const uint16_t *W_H, int64_t r,
+                const uint16_t *h, const int32_t *cand_id, const int32_t *verified,
+                int64_t B, int64_t L, double *A_prev, double *B_cur, double *G) {
+    if (!E || !W_A || !W_B || !W_H || !h || !cand_id || !verified || !A_prev || !B_cur || !G)
+        return -1;
+    if (V < 1 || d < 1 || r < 1 || B < 0 || L < 1) return -1;
+    for (int64_t b = 0; b < B; ++b)
+        if (verified[b] < 0 || verified[b] >= V) return -2;
+    for (int64_t i = 0; i < B * L * ORA_K; ++i)
+        if (cand_id[i] < 0 || cand_id[i] >= V) return -2;
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t bt = 0; bt < B * L; ++bt) {
+        int64_t b = bt / L, t = bt % L;
+        double *Ap = A_prev + bt * ORA_K * r;
+        double *Bc = B_cur + bt * ORA_K * r;
+        for (int i = 0; i < ORA_K; ++i) {
+            if (t == 0) {
+                if (i == 0) matvec(W_A, E + (int64_t)verified[b] * d, r, d, Ap);
+                else for (int64_t c = 0; c < r; ++c) Ap[i * r + c] = 0.0;
+            } else {
+                int32_t tok = cand_id[(bt - 1) * ORA_K + i];
+                matvec(W_A, E + (int64_t)tok * d, r, d, Ap + i * r);
+            }
+            matvec(W_B, E + (int64_t)cand_id[bt * ORA_K + i] * d, r, d, Bc + i * r);
+        }
+        double *g = G + bt * r;
+        matvec(W_H, h + bt * d, r, d, g);
+        for (int64_t c = 0; c < r; ++c) g[c] = 1.0 / (1.0 + exp(-g[c]));
+    }
+    return 0;
+}
+
+/* ----------------------------------------------------------------- scores --- */
+/* [P1 eq. S_t]: S_t(a,b) = U_t(b) + < A(a) (.) H(h_t), B(b) >, U_t(b) the
+ * drafter's raw logit of candidate b at position t. */
+int ora_score_pairs(const float *cand_u, const double *A_prev, const double *B_cur,
+                    const double *G, int64_t B, int64_t L, int64_t r, double *S) {
+    if (!cand_u || !A_prev || !B_cur || !G || !S || B < 0 || L < 1 || r < 1) return -1;
+#pragma omp parallel for schedule(static)
+    for (int64_t bt = 0; bt < B * L; ++bt) {
+        int64_t t = bt % L;
+        int n_t = (t == 0) ? 1 : ORA_K;
+        for (int i = 0; i < ORA_K; ++i)
+            for (int j = 0; j < ORA_K; ++j) {
+                double *s = S + (bt * ORA_K + i) * ORA_K + j;
+                if (i >= n_t) { *s = -INFINITY; continue; }
+                double acc = 0.0;
+                for (int64_t c = 0; c < r; ++c)
+                    acc += A_prev[(bt * ORA_K + i) * r + c] * G[bt * r + c] *
+                           B_cur[(bt * ORA_K + j) * r + c];
+                *s = (double)cand_u[bt * ORA_K + j] + acc;
+            }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------- walk --- */
+/* [P1 Method, last paragraph; P3 "Selection beats correction"]: the only
+ * sequential step walks the precomputed scores from the last verified token;
+ * greedy follows the best successor, sampling draws from the same scores. */
+int ora_step(const double *S_bt, int row, int mode, double u, double T,
+             int *choice, double *aux, double *q) {
+    if (!S_bt || !choice || !aux || row < 0 || row >= ORA_K) return -1;
+    const double *s = S_bt + row * ORA_K;
+    int best = 0;
+    for (int j = 1; j < ORA_K; ++j)
+        if (ranks_above(s[j], j, s[best], best)) best = j;
+
+    if (mode == 0) {
+        int second = (best == 0) ? 1 : 0;
+        for (int j = 0; j < ORA_K; ++j)
+            if (j != best && ranks_above(s[j], j, s[second], second)) second = j;
+        *choice = best;
+        *aux = s[best] - s[second];
+        if (q) for (int j = 0; j < ORA_K; ++j) q[j] = (j == best) ? 1.0 : 0.0;
+        return 0;
+    }
+    if (mode != 1 || !(T > 0.0)) return -1;
+
+    /* softmax(S_row / T) with NaN entries given zero weight. */
+    double m = -INFINITY;
+    for (int j = 0; j < ORA_K; ++j)
+        if (!isnan(s[j]) && s[j] > m) m = s[j];
+    double e[ORA_K];
+    if (m == -INFINITY) {            /* no entry has weight: fall back to the greedy pick */
+        *choice = best;
+        *aux = INFINITY;
+        if (q) for (int j = 0; j < ORA_K; ++j) q[j] = (j == best) ? 1.0 : 0.0;
+        return 0;
+    }
+    for (int j = 0; j < ORA_K; ++j) {
+        if (isnan(s[j])) e[j] = 0.0;
+        else if (m == INFINITY) e[j] = (s[j] == INFINITY) ? 1.0 : 0.0;
+        else e[j] = exp((s[j] - m) / T);
+    }
+    double Z = 0.0, C[ORA_K];
+    for (int j = 0; j < ORA_K; ++j) { Z += e[j]; C[j] = Z; }
+    double uz = u * Z;
+    int pick = -1;
+    for (int j = 0; j < ORA_K; ++j)
+        if (uz < C[j]) { pick = j; break; }
+    if (pick < 0)
+        for (int j = ORA_K - 1; j >= 0; --j)
+            if (e[j] > 0.0) { pick = j; break; }
+    double lo = (pick == 0) ? 0.0 : C[pick - 1];
+    double d0 = fabs(uz - C[pick]), d1 = fabs(uz - lo);
+    *choice = pick;
+    *aux = ((d0 < d1) ? d0 : d1) / Z;
+    if (q) for (int j = 0; j < ORA_K; ++j) q[j] = e[j] / Z;
+    return 0;
+}
+
+int ora_walk(const double *S, const int32_t *cand_id, const float *uniforms, double T,
+             int mode, int64_t B, int64_t L, int32_t *path_tok, int32_t *path_slot,
+             double *path_s, double *aux, double *q) {
+    if (!S || !cand_id || !path_tok || !path_slot || !path_s || !aux || B < 0 || L < 1) return -1;
+    if (mode == 1 && (!uniforms || !(T > 0.0))) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t b = 0; b < B; ++b) {
+        int row = 0;                                   /* the last verified token */
+        for (int64_t t = 0; t < L; ++t) {
+            int64_t bt = b * L + t;
+            const double *S_bt = S + bt * ORA_K * ORA_K;
+            int j = 0;
+            double a = 0.0;
+            double u = (mode == 1) ? (double)uniforms[bt] : 0.0;
+            if (ora_step(S_bt, row, mode, u, T, &j, &a, q ? q + bt * ORA_K : NULL) != 0) {
+                bad = 1;
+                break;
+            }
+            path_slot[bt] = j;
+            path_tok[bt] = cand_id[bt * ORA_K + j];
+            path_s[bt] = S_bt[row * ORA_K + j];
+            aux[bt] = a;
+            row = j;
+        }
+    }
+    return bad ? -1 : 0;
+}
+
+int ora_step_table(const double *S, const float *uniforms, double T, int mode,
+                   int64_t B, int64_t L, int32_t *choice, double *aux) {
+    if (!S || !choice || !aux || B < 0 || L < 1) return -1;
+    if (mode == 1 && (!uniforms || !(T > 0.0))) return -1;
+    int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+    for (int64_t bt = 0; bt < B * L; ++bt) {
+        int n_t = (bt % L == 0) ? 1 : ORA_K;
+        for (int row = 0; row < ORA_K; ++row) {
+            if (row >= n_t) {
+                choice[bt * ORA_K + row] = -1;
+                aux[bt * ORA_K + row] = NAN;
+                continue;
+            }
+            int j = 0;
+            double a = 0.0;
+            double u = (mode == 1) ? (double)uniforms[bt] : 0.0;
+            if (ora_step(S + bt * ORA_K * ORA_K, row, mode, u, T, &j, &a, NULL) != 0) bad = 1;
+            choice[bt * ORA_K + row] = j;
+            aux[bt * ORA_K + row] = a;
+        }
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,76 @@
+/*
+ * CPU oracle of the DFlash 2 lightweight path selector -- TEST INFRASTRUCTURE.
+ *
+ * Only the test suite, the package smoke check and the CPU-baseline leg of the
+ * benchmark may load this library.  The product path (the HIP library and its
+ * binding) never links, imports or calls it, and the two share no code.
+ *
+ * Sources (web pages):
+ *   [P1] "DFlash 2: Keep Drafting Parallel" (papercache.org summary):
+ *        Quick read; Method > Lightweight Path Selector (eq. S_t, Table 2).
+ *   [P3] "DFlash 2: The Drafter Stopped Guessing Alone" (rohitghumare.com):
+ *        section "Selection beats correction".
+ *
+ * All arithmetic is fp64; bf16 inputs are widened exactly (bf16 -> f32 -> f64).
+ * Arrays are host memory, row-major, owned by the caller.
+ * Every function returns 0 on success, -1 on a bad size/pointer, -2 on a token
+ * id outside [0, vocab).
+ */
+#ifndef DSEL_ORACLE_H
+#define DSEL_ORACLE_H
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORA_K 16
+
+/* [P1 Method, P3]: keep the 16 highest-scoring candidates of every draft
+ * position.  Order: value descending, ties to the lower token id; -0.0 equals
+ * +0.0; NaN ranks below -inf.  logits: rows x ld elements (fp32 when dtype==0,
+ * bf16 bit patterns when dtype==1), first V of each row used. */
+int ora_select_topk(const void *logits, int dtype, int64_t rows, int64_t V, int64_t ld,
+                    int32_t *cand_id, float *cand_u);
+
+/* [P1 Method, eq. S_t; P3]: A(x)=W_A.E[x], B(x)=W_B.E[x], H(h)=sigmoid(W_H.h).
+ * A_prev[b,t,i,:] = A(pred_i(b,t)) with pred(b,0) = {verified[b]} (rows i>=1 of
+ * t=0 are zero) and pred(b,t>=1) = cand_id[b,t-1,:];  B_cur[b,t,j,:] =
+ * B(cand_id[b,t,j]);  G[b,t,:] = H(h[b,t,:]).
+ * E [V,d], W_* [r,d], h [B,L,d] bf16 bits; outputs fp64
+ * A_prev/B_cur [B,L,16,r], G [B,L,r]. */
+int ora_project(const uint16_t *E, int64_t V, int64_t d,
+                const uint16_t *W_A, const uint16_t *W_B, const uint16_t *W_H, int64_t r,
+                const uint16_t *h, const int32_t *cand_id, const int32_t *verified,
+                int64_t B, int64_t L, double *A_prev, double *B_cur, double *G);
+
+/* [P1 eq. S_t]: S[b,t,i,j] = U[b,t,j] + sum_c A_prev[b,t,i,c] G[b,t,c] B_cur[b,t,j,c]
+ * for i < n_t (n_0 = 1, n_t = 16); S[b,0,i>=1,:] = -inf.  U = cand_u. */
+int ora_score_pairs(const float *cand_u, const double *A_prev, const double *B_cur,
+                    const double *G, int64_t B, int64_t L, int64_t r, double *S);
+
+/* One step of the walk from predecessor row `row` of S[b,t] (16x16).
+ * mode 0 (greedy, [P1 Method; P3]): the highest score, ties to the lowest slot,
+ *   NaN below -inf; aux = best minus runner-up.
+ * mode 1 (sampled): inverse-CDF draw from softmax(S_row / T) in slot order with
+ *   the caller's uniform u: the first j with u*Z < C_j; aux = distance of u*Z to
+ *   the nearest CDF edge of the chosen slot, divided by Z.
+ * q (16 entries, nullable) receives the step's distribution (one-hot for greedy). */
+int ora_step(const double *S_bt, int row, int mode, double u, double T,
+             int *choice, double *aux, double *q);
+
+/* Walk every block from row 0: path_tok/path_slot [B,L] int32, path_s/aux [B,L],
+ * q [B,L,16] nullable.  uniforms [B,L] used only in mode 1. */
+int ora_walk(const double *S, const int32_t *cand_id, const float *uniforms, double T,
+             int mode, int64_t B, int64_t L, int32_t *path_tok, int32_t *path_slot,
+             double *path_s, double *aux, double *q);
+
+/* Decision table: the step's choice and aux for every predecessor row:
+ * choice/aux [B,L,16] (rows >= n_t are filled with -1 / NaN). */
+int ora_step_table(const double *S, const float *uniforms, double T, int mode,
+                   int64_t B, int64_t L, int32_t *choice, double *aux);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
