@@ -1,0 +1,255 @@
+"""draft_selection_amd -- the DFlash 2 lightweight path selector on MI355X.
+
+Thin ctypes binding over ``libdsel.so`` (C ABI in ``include/dsel.h``).  Every
+function takes and returns ``torch`` tensors on the GPU; the binding only checks
+shapes, allocates outputs with torch and passes raw pointers plus the current
+HIP stream.  Every step of the selector runs in the library's HIP kernels: there
+is no CPU fallback, and a missing library is an error.
+
+Entry points (same names as the C ABI):
+  select_topk(logits, vocab=None)                   -> cand_id, cand_u
+  project(E, W_A, W_B, W_H, h, cand_id, verified)   -> A_prev, B_cur, G
+  score_pairs(cand_u, A_prev, B_cur, G, ...)        -> S and/or the walk
+  walk(S, cand_id, ...)                             -> the walk alone
+  device_error()                                    -> sticky device error bits
+and ``select_path`` running the whole selector.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdsel.so")
+K = 16
+MAX_BLOCK = 64
+GREEDY, SAMPLED = 0, 1
+F32, BF16 = 0, 1
+
+_STATUS = {0: "DSEL_OK", -1: "DSEL_E_ARG", -2: "DSEL_E_DTYPE", -3: "DSEL_E_ALIGN",
+           -4: "DSEL_E_WORKSPACE", -5: "DSEL_E_HIP"}
+
+
+class DselError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {_STATUS.get(status, status)}")
+        self.status = status
+
+
+class WalkArgs(C.Structure):
+    _fields_ = [("mode", C.c_int32), ("temperature", C.c_float), ("uniforms", C.c_void_p),
+                ("cand_id", C.c_void_p), ("path_tok", C.c_void_p), ("path_slot", C.c_void_p),
+                ("path_s", C.c_void_p), ("q", C.c_void_p)]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it first (python -c "
+                              "'import __graft_entry__ as g; g.build()')")
+        lib = C.CDLL(LIB_PATH)
+        P, I64, I32, SZ = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
+        sig = {
+            "dsel_topk_workspace_bytes": ([I64, I64, I32], SZ),
+            "dsel_select_topk": ([P, I32, I64, I64, I64, I64, P, P, P, SZ, P], I32),
+            "dsel_project": ([P, I64, I64, P, P, P, I64, P, P, P, I64, I64, P, P, P, P], I32),
+            "dsel_score_pairs": ([P, P, P, P, I64, I64, I64, P, C.POINTER(WalkArgs), P], I32),
+            "dsel_walk": ([P, I64, I64, C.POINTER(WalkArgs), P], I32),
+            "dsel_device_error": ([C.POINTER(C.c_int32), P], I32),
+            "dsel_status_string": ([I32], C.c_char_p),
+            "dsel_version": ([], I32),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(lib, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = lib
+    return _lib
+
+
+def lib():
+    """The loaded ``libdsel.so`` (ctypes handle)."""
+    return _load()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return C.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise DselError(status, what)
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def topk_workspace_bytes(rows: int, vocab: int, dtype: torch.dtype) -> int:
+    dt = BF16 if dtype == torch.bfloat16 else F32
+    return int(_load().dsel_topk_workspace_bytes(rows, vocab, dt))
+
+
+def select_topk(logits: torch.Tensor, vocab: Optional[int] = None, out=None, workspace=None,
+                stream=None):
+    """Top-16 of every draft position.  ``logits [batch, block, ld]`` fp32 or bf16
+    with unit stride in the last dim; the first ``vocab`` (default ``ld``) entries
+    of each row are used.  Returns ``cand_id [B,L,16] int32``, ``cand_u [B,L,16] fp32``."""
+    if logits.dim() != 3:
+        raise ValueError("logits must be [batch, block, ld]")
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("logits must be float32 or bfloat16")
+    B, L, ld_shape = logits.shape
+    if logits.stride(2) != 1 and ld_shape > 1:
+        raise ValueError("logits must have unit stride in the last dim")
+    if L > 1:
+        ld = logits.stride(1)
+        if B > 1 and logits.stride(0) != L * ld:
+            raise ValueError("logits rows must be evenly spaced")
+    elif B > 1:
+        ld = logits.stride(0)
+    else:
+        ld = ld_shape
+    if ld < ld_shape:
+        raise ValueError("overlapping logits rows")
+    V = ld_shape if vocab is None else int(vocab)
+    if V > ld_shape:
+        raise ValueError("vocab exceeds the logits width")
+    dt = BF16 if logits.dtype == torch.bfloat16 else F32
+    dev = logits.device
+    if out is None:
+        cand_id = torch.empty((B, L, K), dtype=torch.int32, device=dev)
+        cand_u = torch.empty((B, L, K), dtype=torch.float32, device=dev)
+    else:
+        cand_id, cand_u = out
+        _need(cand_id, "cand_id", torch.int32, (B, L, K))
+        _need(cand_u, "cand_u", torch.float32, (B, L, K))
+    need = int(_load().dsel_topk_workspace_bytes(B * L, V, dt))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().dsel_select_topk(_ptr(logits), dt, B, L, V, ld, _ptr(cand_id), _ptr(cand_u),
+                                  _ptr(workspace), wsb, _stream(stream))
+    _check(st, "dsel_select_topk")
+    return cand_id, cand_u
+
+
+def project(E, W_A, W_B, W_H, h, cand_id, verified, out=None, stream=None):
+    """``A_prev [B,L,16,r]``, ``B_cur [B,L,16,r]``, ``G [B,L,r]`` (fp32) from bf16
+    ``E [V,d]``, ``W_* [r,d]``, ``h [B,L,d]``, int32 ``cand_id``, ``verified [B]``."""
+    V, d = E.shape
+    r = W_A.shape[0]
+    B, L = cand_id.shape[:2]
+    for t, n, shp in ((E, "E", (V, d)), (W_A, "W_A", (r, d)), (W_B, "W_B", (r, d)),
+                      (W_H, "W_H", (r, d)), (h, "h", (B, L, d))):
+        _need(t, n, torch.bfloat16, shp)
+    _need(cand_id, "cand_id", torch.int32, (B, L, K))
+    _need(verified, "verified", torch.int32, (B,))
+    dev = E.device
+    if out is None:
+        A_prev = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+        B_cur = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+        G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
+    else:
+        A_prev, B_cur, G = out
+    st = _load().dsel_project(_ptr(E), V, d, _ptr(W_A), _ptr(W_B), _ptr(W_H), r, _ptr(h),
+                              _ptr(cand_id), _ptr(verified), B, L, _ptr(A_prev), _ptr(B_cur),
+                              _ptr(G), _stream(stream))
+    _check(st, "dsel_project")
+    return A_prev, B_cur, G
+
+
+def _walk_args(cand_id, mode, temperature, uniforms, want_q, want_s):
+    B, L = cand_id.shape[:2]
+    dev = cand_id.device
+    res = dict(path_tok=torch.empty((B, L), dtype=torch.int32, device=dev),
+               path_slot=torch.empty((B, L), dtype=torch.int32, device=dev))
+    if want_s:
+        res["path_s"] = torch.empty((B, L), dtype=torch.float32, device=dev)
+    if want_q:
+        res["q"] = torch.empty((B, L, K), dtype=torch.float32, device=dev)
+    if mode == SAMPLED:
+        if uniforms is None:
+            raise ValueError("the sampled walk needs uniforms [batch, block]")
+        _need(uniforms, "uniforms", torch.float32, (B, L))
+    a = WalkArgs(int(mode), float(temperature),
+                 uniforms.data_ptr() if (uniforms is not None and mode == SAMPLED) else None,
+                 cand_id.data_ptr(), res["path_tok"].data_ptr(), res["path_slot"].data_ptr(),
+                 res["path_s"].data_ptr() if want_s else None,
+                 res["q"].data_ptr() if want_q else None)
+    return a, res
+
+
+def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Optional[int] = None,
+                cand_id=None, temperature: float = 1.0, uniforms=None, want_q: bool = False,
+                stream=None):
+    """Pair scores ``S [B,L,16,16]`` (if ``want_S``) and, when ``walk_mode`` is
+    given, the fused walk.  Returns a dict."""
+    B, L, _, r = A_prev.shape
+    _need(cand_u, "cand_u", torch.float32, (B, L, K))
+    _need(A_prev, "A_prev", torch.float32, (B, L, K, r))
+    _need(B_cur, "B_cur", torch.float32, (B, L, K, r))
+    _need(G, "G", torch.float32, (B, L, r))
+    res = {}
+    S = torch.empty((B, L, K, K), dtype=torch.float32, device=A_prev.device) if want_S else None
+    wa = None
+    if walk_mode is not None:
+        if cand_id is None:
+            raise ValueError("the walk needs cand_id")
+        _need(cand_id, "cand_id", torch.int32, (B, L, K))
+        wa, res = _walk_args(cand_id, walk_mode, temperature, uniforms, want_q, True)
+    st = _load().dsel_score_pairs(_ptr(cand_u), _ptr(A_prev), _ptr(B_cur), _ptr(G), B, L, r,
+                                  _ptr(S), C.byref(wa) if wa is not None else None, _stream(stream))
+    _check(st, "dsel_score_pairs")
+    if S is not None:
+        res["S"] = S
+    return res
+
+
+def walk(S, cand_id, mode: int = GREEDY, temperature: float = 1.0, uniforms=None,
+         want_q: bool = False, stream=None):
+    """The walk alone over ``S [B,L,16,16]`` fp32."""
+    B, L = S.shape[:2]
+    _need(S, "S", torch.float32, (B, L, K, K))
+    _need(cand_id, "cand_id", torch.int32, (B, L, K))
+    wa, res = _walk_args(cand_id, mode, temperature, uniforms, want_q, True)
+    _check(_load().dsel_walk(_ptr(S), B, L, C.byref(wa), _stream(stream)), "dsel_walk")
+    return res
+
+
+def device_error(stream=None) -> int:
+    """Synchronise, then read and clear the device error word."""
+    v = C.c_int32(0)
+    _check(_load().dsel_device_error(C.byref(v), _stream(stream)), "dsel_device_error")
+    return int(v.value)
+
+
+def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
+                temperature: float = 1.0, uniforms=None, vocab: Optional[int] = None,
+                want_S: bool = False, want_q: bool = False, stream=None):
+    """The whole selector: top-16, projections, pair scores and the fused walk."""
+    cand_id, cand_u = select_topk(logits, vocab, stream=stream)
+    A_prev, B_cur, G = project(E, W_A, W_B, W_H, h, cand_id, verified, stream=stream)
+    res = score_pairs(cand_u, A_prev, B_cur, G, want_S=want_S, walk_mode=mode, cand_id=cand_id,
+                      temperature=temperature, uniforms=uniforms, want_q=want_q, stream=stream)
+    res.update(cand_id=cand_id, cand_u=cand_u, A_prev=A_prev, B_cur=B_cur, G=G)
+    return res

@@ -1,0 +1,93 @@
+// Device helpers shared by the selector kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsel {
+
+constexpr int kK = 16;       // candidates per draft position
+constexpr int kWave = 64;    // CDNA wavefront width
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+__device__ __forceinline__ uint32_t shfl_idx32(uint32_t x, uint32_t src_lane) {
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(src_lane << 2), (int)x);
+}
+
+__device__ __forceinline__ uint64_t shfl_idx64(uint64_t x, uint32_t src_lane) {
+    uint32_t lo = shfl_idx32((uint32_t)x, src_lane);
+    uint32_t hi = shfl_idx32((uint32_t)(x >> 32), src_lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t readlane64(uint64_t x, uint32_t l) {
+    uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, (int)l);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), (int)l);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float shfl_idxf(float x, uint32_t src_lane) {
+    return __uint_as_float(shfl_idx32(__float_as_uint(x), src_lane));
+}
+
+// Monotone 32-bit image of a float for the candidate order: larger = ranks
+// higher.  -0.0 maps like +0.0 and every NaN maps to 0, below -inf (0x007FFFFF).
+__device__ __forceinline__ uint32_t order_bits(float v) {
+    uint32_t b = __float_as_uint(v);
+    if (v != v) return 0u;
+    if (b == 0x80000000u) b = 0u;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Candidate key: (order_bits(value), ~id).  A larger key ranks higher; equal
+// values rank the lower id higher.  Key 0 is an empty slot (every real key has a
+// low word >= 2^31 because ids are < 2^31).
+__device__ __forceinline__ uint64_t cand_key(float v, uint32_t id) {
+    return ((uint64_t)order_bits(v) << 32) | (uint32_t)(~id);
+}
+
+__device__ __forceinline__ uint32_t key_id(uint64_t k) { return ~(uint32_t)k; }
+
+// The float a key's value part stands for, used as the fast filter threshold:
+// empty or NaN-level keys give -inf so that every element (NaN included, since
+// !(NaN < -inf) holds) goes on to the exact key compare.
+__device__ __forceinline__ float key_threshold(uint64_t k) {
+    uint32_t hi = (uint32_t)(k >> 32);
+    if (hi <= 0x007FFFFFu) return -__builtin_inff();
+    uint32_t b = (hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi;
+    return __uint_as_float(b);
+}
+
+// Bitonic sort of one 64-bit key per lane across the wave, descending
+// (lane 0 receives the largest key).
+__device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t key) {
+    const uint32_t lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= kWave; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            uint64_t other = shfl_idx64(key, lane ^ (uint32_t)j);
+            bool lower = (lane & (uint32_t)j) == 0;
+            bool desc = (lane & (uint32_t)k) == 0;
+            uint64_t mx = key > other ? key : other;
+            uint64_t mn = key > other ? other : key;
+            key = (lower == desc) ? mx : mn;
+        }
+    }
+    return key;
+}
+
+// Sticky device error word (bits DSEL_DEVERR_*), one per device.  The library
+// is a single translation unit, so this is its only definition.
+__device__ int g_device_error = 0;
+
+}  // namespace dsel

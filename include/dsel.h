@@ -1,0 +1,174 @@
+/*
+ * dsel -- the DFlash 2 lightweight path selector on AMD MI355X (gfx950).
+ *
+ * C ABI of libdsel.so.  Sources (web pages):
+ *   [P1] "DFlash 2: Keep Drafting Parallel" (papercache.org summary),
+ *        Quick read; Method > Lightweight Path Selector (eq. S_t, Table 2).
+ *   [P3] "DFlash 2: The Drafter Stopped Guessing Alone" (rohitghumare.com),
+ *        section "Selection beats correction".
+ *
+ * The selector keeps the top-16 candidates of every draft position, scores
+ * every adjacent candidate pair with
+ *     S_t(a, b) = U_t(b) + < A(a) (.) H(h_t), B(b) >
+ * in one parallel pass, and walks the precomputed scores from the last verified
+ * token, greedily or by sampling.  Here A(x) = W_A E[x], B(x) = W_B E[x] and
+ * H(h) = sigmoid(W_H h) (three r x d matrices: the shape whose parameter count
+ * matches the 2.0M of [P1] Table 2 at d = 2560, r = 256).
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller; layouts are
+ *     contiguous row-major unless a leading dimension is given.  bf16 tensors
+ *     are passed as their 16-bit patterns (uint16_t).
+ *   - The library allocates nothing and keeps no pointer after a call returns.
+ *     Inputs are never written; outputs must not alias inputs.
+ *   - Every argument is validated on the host before anything is launched.  On
+ *     a validation failure the call returns a negative status and writes
+ *     nothing.  A failed launch returns DSEL_E_HIP.  A call with no work
+ *     (batch * block == 0) returns DSEL_OK after checking its sizes; its
+ *     pointers may then be NULL.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream); results are valid once the stream has been synchronised.  No
+ *     C++ exception crosses the boundary.  Calls on different streams may run
+ *     concurrently, except that the device error word (dsel_device_error) is
+ *     shared by all calls on one device.
+ */
+#ifndef DSEL_H
+#define DSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSEL_K 16          /* candidates kept per draft position ([P1] Method) */
+#define DSEL_MAX_BLOCK 64  /* longest draft block accepted by score_pairs / walk */
+#define DSEL_MAX_RANK 256  /* largest selector rank r ([P1]: 256-d token vectors) */
+
+typedef void *dsel_stream_t; /* a hipStream_t */
+
+typedef enum {
+    DSEL_OK = 0,
+    DSEL_E_ARG = -1,       /* null pointer, bad size or out-of-range scalar */
+    DSEL_E_DTYPE = -2,     /* unknown dtype or walk mode */
+    DSEL_E_ALIGN = -3,     /* pointer or leading dimension misaligned */
+    DSEL_E_WORKSPACE = -4, /* workspace missing or too small */
+    DSEL_E_HIP = -5        /* a HIP runtime call or kernel launch failed */
+} dsel_status;
+
+typedef enum { DSEL_F32 = 0, DSEL_BF16 = 1 } dsel_dtype;
+typedef enum { DSEL_GREEDY = 0, DSEL_SAMPLED = 1 } dsel_walk_mode;
+
+/* Device error word bits (see dsel_device_error). */
+#define DSEL_DEVERR_TOKEN_RANGE 1 /* dsel_project met a token id outside [0, vocab) */
+
+/* Bytes of device workspace dsel_select_topk needs for `rows` = batch*block rows
+ * of `vocab` logits of type `dt` (0 when it needs none).  Returns 0 for
+ * invalid arguments too; dsel_select_topk validates. */
+size_t dsel_topk_workspace_bytes(int64_t rows, int64_t vocab, dsel_dtype dt);
+
+/* select_topk -- [P1] Method > Lightweight Path Selector, [P3]: keep the 16
+ * best candidates of every draft position.
+ *   logits   [batch*block rows][ld] of dtype `dt` (fp32, or bf16 bits); the
+ *            first `vocab` entries of each row are the position's raw logits.
+ *            Pointer aligned to the element size; any ld >= vocab.  Only the
+ *            first vocab elements of each row are read.
+ *   cand_id  out [batch, block, 16] int32: token ids, ordered by logit
+ *            descending, ties to the lower id; -0.0 equals +0.0 and NaN ranks
+ *            below -inf.  The ordered list is unique, so results are bit-exact.
+ *   cand_u   out [batch, block, 16] fp32: the logit of each candidate, widened
+ *            exactly (these are U_t(b) of eq. S_t).
+ *   workspace  device scratch of at least dsel_topk_workspace_bytes() bytes
+ *            (may be NULL when that is 0); contents need no initialisation.
+ * Requirements: 16 <= vocab < 2^31, ld >= vocab, batch*block >= 0. */
+dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t batch, int64_t block,
+                             int64_t vocab, int64_t ld, int32_t *cand_id, float *cand_u,
+                             void *workspace, size_t workspace_bytes, dsel_stream_t stream);
+
+/* project -- [P1] Method (the paragraph after eq. S_t), [P3]: the compact token
+ * vectors and the context gate, for every candidate and predecessor.
+ *   E        [vocab, d] bf16: the drafter's token embedding table.
+ *   W_A, W_B, W_H  [r, d] bf16 (linear-layer layout: y = W x).
+ *   h        [batch, block, d] bf16: drafter hidden state of every position.
+ *   cand_id  [batch, block, 16] int32 (from dsel_select_topk).
+ *   verified [batch] int32: last verified token of every block (the walk's
+ *            start, [P1] Method last paragraph).
+ *   A_prev   out [batch, block, 16, r] fp32: A of each predecessor.  Position 0
+ *            has one predecessor (row 0 = A(verified)); rows 1..15 of position
+ *            0 are written as zeros.  Position t >= 1: row i = A(cand_id[t-1][i]).
+ *   B_cur    out [batch, block, 16, r] fp32: row j = B(cand_id[t][j]).
+ *   G        out [batch, block, r] fp32: sigmoid(W_H h[t]).
+ * Products are bf16 x bf16 with fp32 accumulation (MFMA).  A token id outside
+ * [0, vocab) reads a zero embedding row and sets DSEL_DEVERR_TOKEN_RANGE in the
+ * device error word.  Requirements: d % 64 == 0, r % 32 == 0, 32 <= r <= 256,
+ * 1 <= block, batch >= 0, 1 <= vocab < 2^31; all pointers 16-byte aligned. */
+dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                         const uint16_t *W_B, const uint16_t *W_H, int64_t r, const uint16_t *h,
+                         const int32_t *cand_id, const int32_t *verified, int64_t batch,
+                         int64_t block, float *A_prev, float *B_cur, float *G,
+                         dsel_stream_t stream);
+
+/* Walk arguments ([P1] Method last paragraph, [P3]: the only sequential step;
+ * greedy follows the best successor, sampling draws from the same scores).
+ *   mode        DSEL_GREEDY: at each position take the highest score in the row
+ *               of the previous pick (row 0 at position 0), ties to the lowest
+ *               slot, NaN below -inf.
+ *               DSEL_SAMPLED: draw from softmax(S_row / temperature) by inverse
+ *               CDF in slot order: the first slot j with u*Z < C_j (Z the sum
+ *               of the exponentials, C_j their running sum, u the caller's
+ *               uniform); NaN scores get zero weight; a row with no weight
+ *               falls back to the greedy pick.
+ *   temperature > 0 (SAMPLED only).
+ *   uniforms    [batch, block] fp32 in [0, 1) (SAMPLED only, else may be NULL).
+ *   cand_id     [batch, block, 16] int32.
+ *   path_tok    out [batch, block] int32: the chosen token at every position.
+ *   path_slot   out [batch, block] int32: its slot in cand_id.
+ *   path_s      out [batch, block] fp32: its score (nullable).
+ *   q           out [batch, block, 16] fp32: the step's distribution over the
+ *               16 successors (one-hot for greedy) (nullable). */
+typedef struct {
+    int32_t mode;
+    float temperature;
+    const float *uniforms;
+    const int32_t *cand_id;
+    int32_t *path_tok;
+    int32_t *path_slot;
+    float *path_s;
+    float *q;
+} dsel_walk_args;
+
+/* score_pairs -- [P1] eq. S_t, [P3]: every adjacent candidate pair scored in one
+ * parallel pass:
+ *   S[b,t,i,j] = cand_u[b,t,j] + sum_c A_prev[b,t,i,c] G[b,t,c] B_cur[b,t,j,c]
+ * for i < n_t (n_0 = 1, n_t = 16 for t >= 1); S[b,0,i>=1,:] = -inf.
+ * fp32 arithmetic.  Inputs as produced by dsel_project / dsel_select_topk.
+ *   S     out [batch, block, 16, 16] fp32; may be NULL when `walk` is given.
+ *   walk  nullable: when given, the walk runs fused in the same launch.
+ * Requirements: 1 <= block <= DSEL_MAX_BLOCK, r % 32 == 0, 32 <= r <= 256;
+ * pointers 16-byte aligned. */
+dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const float *B_cur,
+                             const float *G, int64_t batch, int64_t block, int64_t r, float *S,
+                             const dsel_walk_args *walk, dsel_stream_t stream);
+
+/* walk -- the walk alone over given scores S [batch, block, 16, 16] fp32 (same
+ * rules as the fused walk of dsel_score_pairs; row 0 is the predecessor at
+ * position 0).  Requirements: 1 <= block <= DSEL_MAX_BLOCK. */
+dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const dsel_walk_args *walk,
+                      dsel_stream_t stream);
+
+/* Synchronise `stream`, then read and clear the device error word of the
+ * current device (bits DSEL_DEVERR_*; 0 = no error). */
+dsel_status dsel_device_error(int32_t *out_code, dsel_stream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char *dsel_status_string(dsel_status s);
+
+/* ABI version of this header (major * 100 + minor). */
+int32_t dsel_version(void);
+#define DSEL_VERSION 100
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSEL_H */

@@ -211,3 +211,28 @@ def make(cfg: Config, seed: int = 0) -> Dict[str, np.ndarray]:
         verified=make_verified(cfg, seed),
         uniforms=make_uniforms(cfg, seed),
     )
+
+
+def sub_blocks(inp: Dict[str, np.ndarray], blocks) -> Dict[str, np.ndarray]:
+    """The inputs of a subset of blocks (blocks are independent of each other)."""
+    blocks = np.asarray(blocks)
+    out = dict(inp)
+    for k in ("logits", "h", "verified", "uniforms"):
+        out[k] = np.ascontiguousarray(inp[k][blocks])
+    return out
+
+
+def to_device(inp: Dict[str, np.ndarray], dev):
+    """Upload drawn inputs as torch tensors: bf16 bit patterns become bfloat16."""
+    import torch
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    lg = inp["logits"]
+    out = dict(logits=bf(lg) if lg.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(lg)).to(dev))
+    for k in ("E", "W_A", "W_B", "W_H", "h"):
+        out[k] = bf(inp[k])
+    out["verified"] = torch.from_numpy(np.ascontiguousarray(inp["verified"], np.int32)).to(dev)
+    out["uniforms"] = torch.from_numpy(np.ascontiguousarray(inp["uniforms"], np.float32)).to(dev)
+    return out

@@ -18,3 +18,24 @@ def ora():
 
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture(scope="session")
+def dev():
+    import torch
+
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible: the gpu-marked tests need an MI355X")
+    import draft_selection_amd as ds
+
+    ds.lib()
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    # name the case before it touches the GPU, so a fault can be traced to it
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.stderr.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.stderr.flush()
+    yield

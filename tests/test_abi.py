@@ -1,0 +1,87 @@
+"""The C ABI library loads and exports every function include/dsel.h declares,
+and its host-side validation rejects bad arguments before any launch.
+
+CPU only: every call below either needs no device or fails validation, which
+happens on the host before anything is launched."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsel.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsel_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import draft_selection_amd as ds
+
+    if not os.path.exists(ds.LIB_PATH):
+        pytest.fail("libdsel.so is not built (run __graft_entry__.build())")
+    return ds.lib()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for want in ("dsel_select_topk", "dsel_project", "dsel_score_pairs", "dsel_walk"):
+        assert want in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared():
+        assert hasattr(lib, name), f"{name} missing from libdsel.so"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dsel_version() == 100
+    for code in (0, -1, -2, -3, -4, -5):
+        assert lib.dsel_status_string(code).startswith(b"DSEL_")
+
+
+def test_topk_workspace_sizing(lib):
+    # one block of 16 over a 152k vocabulary is split across workgroups
+    assert lib.dsel_topk_workspace_bytes(16, 151936, 1) > 0
+    assert lib.dsel_topk_workspace_bytes(1024, 151936, 1) == 0
+    assert lib.dsel_topk_workspace_bytes(16, 15, 1) == 0
+
+
+def test_validation_rejects_before_launch(lib):
+    import draft_selection_amd as ds
+
+    P = C.c_void_p
+    fake = P(0x100000)  # never dereferenced: each call fails validation first
+    odd = P(0x100001)
+    # select_topk
+    assert lib.dsel_select_topk(None, 1, 1, 1, 1024, 1024, fake, fake, None, 0, None) == -1
+    assert lib.dsel_select_topk(fake, 7, 1, 1, 1024, 1024, fake, fake, None, 0, None) == -2
+    assert lib.dsel_select_topk(fake, 1, 1, 1, 15, 15, fake, fake, None, 0, None) == -1
+    assert lib.dsel_select_topk(fake, 1, 1, 1, 64, 32, fake, fake, None, 0, None) == -1
+    assert lib.dsel_select_topk(odd, 1, 1, 1, 64, 64, fake, fake, None, 0, None) == -3
+    assert lib.dsel_select_topk(fake, 1, 1, 16, 151936, 151936, fake, fake, None, 0, None) == -4
+    # project
+    args = [fake, 1000, 64, fake, fake, fake, 32, fake, fake, fake, 2, 4, fake, fake, fake, None]
+    bad_d = list(args); bad_d[2] = 96
+    bad_r = list(args); bad_r[6] = 48
+    big_r = list(args); big_r[6] = 512
+    mis = list(args); mis[0] = P(0x100008)
+    nul = list(args); nul[7] = None
+    for a, code in ((bad_d, -1), (bad_r, -1), (big_r, -1), (mis, -3), (nul, -1)):
+        assert lib.dsel_project(*a) == code
+    # score_pairs / walk
+    w = ds.WalkArgs(5, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, 32, fake, C.byref(w), None) == -2
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 65, 32, fake, None, None) == -1
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, 32, None, None, None) == -1
+    w = ds.WalkArgs(1, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)  # sampled, no uniforms
+    assert lib.dsel_walk(fake, 1, 8, C.byref(w), None) == -1
+    w = ds.WalkArgs(1, 0.0, 0x100000, 0x100000, 0x100000, 0x100000, None, None)  # T = 0
+    assert lib.dsel_walk(fake, 1, 8, C.byref(w), None) == -1
+    assert lib.dsel_walk(fake, 1, 0, C.byref(w), None) == -1
+    assert lib.dsel_device_error(None, None) == -1
