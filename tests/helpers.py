@@ -46,25 +46,12 @@ def bf16_dev(a, dev):
 
 def to_dev(inp, dev):
     """Host arrays drawn by synth (or built by a test) -> device tensors."""
-    import torch
-
-    lg = inp["logits"]
-    logits = bf16_dev(lg, dev) if lg.dtype == np.uint16 else torch.from_numpy(np.ascontiguousarray(lg)).to(dev)
-    out = dict(logits=logits)
-    for k in ("E", "W_A", "W_B", "W_H", "h"):
-        out[k] = bf16_dev(inp[k], dev)
-    out["verified"] = torch.from_numpy(np.ascontiguousarray(inp["verified"], np.int32)).to(dev)
-    out["uniforms"] = torch.from_numpy(np.ascontiguousarray(inp["uniforms"], np.float32)).to(dev)
-    return out
+    return synth.to_device(inp, dev)
 
 
 def sub_inputs(inp, blocks):
     """The inputs of a subset of blocks (every block is independent)."""
-    blocks = np.asarray(blocks)
-    out = dict(inp)
-    for k in ("logits", "h", "verified", "uniforms"):
-        out[k] = np.ascontiguousarray(inp[k][blocks])
-    return out
+    return synth.sub_blocks(inp, blocks)
 
 
 def ulp32(x):
