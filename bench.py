@@ -39,10 +39,11 @@ def algorithmic(cfg):
     es = 2 if cfg.logits_dtype == "bf16" else 4
     rows = cfg.batch * cfg.block
     topk_bytes = rows * cfg.vocab * es + rows * K * 8
-    a_rows = cfg.batch * (K * (cfg.block - 1) + 1)   # predecessors that need A
-    b_rows = cfg.batch * cfg.block * K               # candidates that need B
-    proj_flop = 2.0 * cfg.d * cfg.r * (a_rows + b_rows + rows)
-    return dict(topk_bytes=topk_bytes, proj_flop=proj_flop)
+    a_rows = cfg.batch * K * (cfg.block - 1)  # candidates that are someone's predecessor
+    b_rows = cfg.batch * cfg.block * K        # candidates that need B
+    cand_flop = 2.0 * cfg.d * cfg.r * (a_rows + b_rows)
+    gate_flop = 2.0 * cfg.d * cfg.r * (rows + cfg.batch)  # gate rows + verified tokens
+    return dict(topk_bytes=topk_bytes, cand_flop=cand_flop, gate_flop=gate_flop)
 
 
 def kernel_source_hash(names):
@@ -97,6 +98,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate", default="serial", choices=["serial", "overlap"],
+                    help="run the gate GEMM before the top-16 or beside it on a second stream")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the selector is block-parallel and this build runs on "
@@ -125,53 +128,93 @@ def main():
     G = torch.empty((B, L, cfg.r), dtype=torch.float32, device=dev)
     wsb = ds.topk_workspace_bytes(B * L, V, d["logits"].dtype)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    pwsb = ds.project_workspace_bytes(B, L, cfg.d, cfg.r)
+    pws = torch.empty(max(pwsb, 1), dtype=torch.uint8, device=dev)
+    S = torch.empty((B, L, K, K), dtype=torch.float32, device=dev)
     wargs, wres = ds._walk_args(cand_id, mode, cfg.temperature, d["uniforms"], False, True)
 
     import ctypes as C
     lib = ds.lib()
-    sp = C.c_void_p(stream.cuda_stream)
     P = ds._ptr
     dt = ds.BF16 if cfg.logits_dtype == "bf16" else ds.F32
 
-    def step(ev=None):
+    side = ds.side_stream(dev)
+    ss = C.c_void_p(side.cuda_stream)
+    fork = [torch.cuda.Event() for _ in range(2)]
+
+    def step(strm, ev=None):
+        # the gate GEMM needs no candidates: either it runs first, or on a side
+        # stream beside the top-16 (the side stream first waits for the
+        # previous step).
+        sp = C.c_void_p(strm.cuda_stream)
+        if args.gate == "overlap":
+            fork[0].record(strm)
+            side.wait_event(fork[0])
+        s0 = lib.dsel_project_gate(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
+                                   P(d["verified"]), B, L, P(A_prev), P(G), P(pws), pwsb,
+                                   ss if args.gate == "overlap" else sp)
+        if args.gate == "overlap":
+            fork[1].record(side)
         if ev is not None:
-            ev[0].record(stream)
+            ev[0].record(strm)
         s1 = lib.dsel_select_topk(P(d["logits"]), dt, B, L, V, V, P(cand_id), P(cand_u), P(ws), wsb, sp)
         if ev is not None:
-            ev[1].record(stream)
-        s2 = lib.dsel_project(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_B"]), P(d["W_H"]), cfg.r,
-                              P(d["h"]), P(cand_id), P(d["verified"]), B, L, P(A_prev), P(B_cur),
-                              P(G), sp)
+            ev[1].record(strm)
+        if args.gate == "overlap":
+            strm.wait_event(fork[1])
+        s2 = lib.dsel_project_cand(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_B"]), cfg.r, P(cand_id),
+                                   B, L, P(A_prev), P(B_cur), sp)
         if ev is not None:
-            ev[2].record(stream)
-        s3 = lib.dsel_score_pairs(P(cand_u), P(A_prev), P(B_cur), P(G), B, L, cfg.r, None,
+            ev[2].record(strm)
+        s3 = lib.dsel_score_pairs(P(cand_u), P(A_prev), P(B_cur), P(G), B, L, cfg.r, P(S),
                                   C.byref(wargs), sp)
         if ev is not None:
-            ev[3].record(stream)
-        if s1 or s2 or s3:
-            raise RuntimeError(f"dsel status {s1} {s2} {s3}")
+            ev[3].record(strm)
+        if s0 or s1 or s2 or s3:
+            raise RuntimeError(f"dsel status {s0} {s1} {s2} {s3}")
 
     for _ in range(args.warmup):
-        step()
+        step(stream)
     torch.cuda.synchronize()
 
-    # timed region: exactly K steps, per-stage HIP events on the launch stream
+    # (1) eager timed region: K steps with HIP events around every stage on the
+    # stream the kernels run on (per-kernel durations for the roofline)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(stream, evs[i])
+    torch.cuda.synchronize()
+    wall_eager = time.perf_counter() - t0
+
+    # (2) the step captured once as a HIP graph (launch overhead removed),
+    # replayed K times: the throughput figure
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        step(cap)
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step(torch.cuda.current_stream())
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     assert ds.device_error() == 0
 
     ms_step = wall * 1e3 / args.steps
     st_topk = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3   # us
-    st_proj = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3
+    st_proj = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3  # project_cand (+ any wait for the gate)
     st_pair = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
     alg = algorithmic(cfg)
     topk_gbs = alg["topk_bytes"] / (st_topk * 1e-6) / 1e9
-    proj_tfs = alg["proj_flop"] / (st_proj * 1e-6) / 1e12
+    proj_tfs = alg["cand_flop"] / (st_proj * 1e-6) / 1e12
 
     traffic = traffic_from_profile(cfg.name)
     if st_topk >= st_proj:
@@ -179,7 +222,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(topk_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic}
     else:
-        roof = {"kernel": "project", "bound": "mfma", "achieved": round(proj_tfs, 2),
+        roof = {"kernel": "project_cand", "bound": "mfma", "achieved": round(proj_tfs, 2),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None}
 
@@ -199,10 +242,13 @@ def main():
         "config": {"workload": describe(cfg), "batch": B, "block": L, "vocab": V, "d": cfg.d,
                    "r": cfg.r, "logits": cfg.logits_dtype, "walk": "sampled" if mode else "greedy"},
         "us_per_block": round(ms_step * 1e3 / B, 4),
-        "stages_us": {"select_topk": round(st_topk, 2), "project": round(st_proj, 2),
+        "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 5),
+        "timing": "value: the step as one HIP graph replayed K times; stages: eager launches with HIP events",
+        "stages_us": {"select_topk": round(st_topk, 2), "project_cand": round(st_proj, 2),
                       "score_pairs_walk": round(st_pair, 2)},
         "select_topk_hbm": {"GB/s": round(topk_gbs, 1), "frac": round(topk_gbs / HBM_PEAK_GBS, 4)},
-        "project_mfma": {"TFLOP/s": round(proj_tfs, 2), "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4)},
+        "project_cand_mfma": {"TFLOP/s": round(proj_tfs, 2), "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4)},
+        "project_gate": args.gate,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

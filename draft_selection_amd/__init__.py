@@ -25,7 +25,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdsel.so")
 K = 16
-MAX_BLOCK = 64
+MAX_BLOCK = 32
 GREEDY, SAMPLED = 0, 1
 F32, BF16 = 0, 1
 
@@ -59,7 +59,10 @@ def _load():
         sig = {
             "dsel_topk_workspace_bytes": ([I64, I64, I32], SZ),
             "dsel_select_topk": ([P, I32, I64, I64, I64, I64, P, P, P, SZ, P], I32),
-            "dsel_project": ([P, I64, I64, P, P, P, I64, P, P, P, I64, I64, P, P, P, P], I32),
+            "dsel_project": ([P, I64, I64, P, P, P, I64, P, P, P, I64, I64, P, P, P, P, SZ, P], I32),
+            "dsel_project_workspace_bytes": ([I64, I64, I64, I64], SZ),
+            "dsel_project_gate": ([P, I64, I64, P, P, I64, P, P, I64, I64, P, P, P, SZ, P], I32),
+            "dsel_project_cand": ([P, I64, I64, P, P, I64, P, I64, I64, P, P, P], I32),
             "dsel_score_pairs": ([P, P, P, P, I64, I64, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_walk": ([P, I64, I64, C.POINTER(WalkArgs), P], I32),
             "dsel_device_error": ([C.POINTER(C.c_int32), P], I32),
@@ -171,11 +174,66 @@ def project(E, W_A, W_B, W_H, h, cand_id, verified, out=None, stream=None):
         G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
     else:
         A_prev, B_cur, G = out
+    ws = _project_workspace(B, L, d, r, dev)
+    wsb = 0 if ws is None else ws.numel()
     st = _load().dsel_project(_ptr(E), V, d, _ptr(W_A), _ptr(W_B), _ptr(W_H), r, _ptr(h),
                               _ptr(cand_id), _ptr(verified), B, L, _ptr(A_prev), _ptr(B_cur),
-                              _ptr(G), _stream(stream))
+                              _ptr(G), _ptr(ws), wsb, _stream(stream))
     _check(st, "dsel_project")
     return A_prev, B_cur, G
+
+
+def project_workspace_bytes(batch: int, block: int, d: int, r: int) -> int:
+    return int(_load().dsel_project_workspace_bytes(batch, block, d, r))
+
+
+def _project_workspace(B, L, d, r, dev):
+    n = project_workspace_bytes(B, L, d, r)
+    return torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+
+
+def project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=None, stream=None):
+    """G and the position-0 predecessor rows of A_prev (needs no candidates)."""
+    V, d = E.shape
+    r = W_A.shape[0]
+    B, L = h.shape[:2]
+    for t, n, shp in ((E, "E", (V, d)), (W_A, "W_A", (r, d)), (W_H, "W_H", (r, d)), (h, "h", (B, L, d))):
+        _need(t, n, torch.bfloat16, shp)
+    _need(verified, "verified", torch.int32, (B,))
+    _need(A_prev, "A_prev", torch.float32, (B, L, K, r))
+    _need(G, "G", torch.float32, (B, L, r))
+    if workspace is None:
+        workspace = _project_workspace(B, L, d, r, E.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _load().dsel_project_gate(_ptr(E), V, d, _ptr(W_A), _ptr(W_H), r, _ptr(h), _ptr(verified),
+                                   B, L, _ptr(A_prev), _ptr(G), _ptr(workspace), wsb, _stream(stream))
+    _check(st, "dsel_project_gate")
+
+
+def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, stream=None):
+    """B_cur and the predecessor rows of A_prev for positions >= 1."""
+    V, d = E.shape
+    r = W_A.shape[0]
+    B, L = cand_id.shape[:2]
+    for t, n, shp in ((E, "E", (V, d)), (W_A, "W_A", (r, d)), (W_B, "W_B", (r, d))):
+        _need(t, n, torch.bfloat16, shp)
+    _need(cand_id, "cand_id", torch.int32, (B, L, K))
+    _need(A_prev, "A_prev", torch.float32, (B, L, K, r))
+    _need(B_cur, "B_cur", torch.float32, (B, L, K, r))
+    st = _load().dsel_project_cand(_ptr(E), V, d, _ptr(W_A), _ptr(W_B), r, _ptr(cand_id), B, L,
+                                   _ptr(A_prev), _ptr(B_cur), _stream(stream))
+    _check(st, "dsel_project_cand")
+
+
+_side = {}
+
+
+def side_stream(device) -> "torch.cuda.Stream":
+    """A second stream (default priority) per device for work that overlaps."""
+    idx = torch.device(device).index or 0
+    if idx not in _side:
+        _side[idx] = torch.cuda.Stream(device=idx)
+    return _side[idx]
 
 
 def _walk_args(cand_id, mode, temperature, uniforms, want_q, want_s):
@@ -202,15 +260,15 @@ def _walk_args(cand_id, mode, temperature, uniforms, want_q, want_s):
 def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Optional[int] = None,
                 cand_id=None, temperature: float = 1.0, uniforms=None, want_q: bool = False,
                 stream=None):
-    """Pair scores ``S [B,L,16,16]`` (if ``want_S``) and, when ``walk_mode`` is
-    given, the fused walk.  Returns a dict."""
+    """Pair scores ``S [B,L,16,16]`` (returned if ``want_S``) and, when
+    ``walk_mode`` is given, the walk over them.  Returns a dict."""
     B, L, _, r = A_prev.shape
     _need(cand_u, "cand_u", torch.float32, (B, L, K))
     _need(A_prev, "A_prev", torch.float32, (B, L, K, r))
     _need(B_cur, "B_cur", torch.float32, (B, L, K, r))
     _need(G, "G", torch.float32, (B, L, r))
     res = {}
-    S = torch.empty((B, L, K, K), dtype=torch.float32, device=A_prev.device) if want_S else None
+    S = torch.empty((B, L, K, K), dtype=torch.float32, device=A_prev.device)
     wa = None
     if walk_mode is not None:
         if cand_id is None:
@@ -220,7 +278,7 @@ def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Option
     st = _load().dsel_score_pairs(_ptr(cand_u), _ptr(A_prev), _ptr(B_cur), _ptr(G), B, L, r,
                                   _ptr(S), C.byref(wa) if wa is not None else None, _stream(stream))
     _check(st, "dsel_score_pairs")
-    if S is not None:
+    if want_S:
         res["S"] = S
     return res
 
@@ -245,11 +303,30 @@ def device_error(stream=None) -> int:
 
 def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
                 temperature: float = 1.0, uniforms=None, vocab: Optional[int] = None,
-                want_S: bool = False, want_q: bool = False, stream=None):
-    """The whole selector: top-16, projections, pair scores and the fused walk."""
-    cand_id, cand_u = select_topk(logits, vocab, stream=stream)
-    A_prev, B_cur, G = project(E, W_A, W_B, W_H, h, cand_id, verified, stream=stream)
+                want_S: bool = False, want_q: bool = False, overlap: bool = False, stream=None):
+    """The whole selector: top-16, projections, pair scores and the fused walk.
+
+    With ``overlap`` the gate GEMM (which needs no candidates) runs on a side
+    stream while the top-16 runs on the caller's stream; by default it runs
+    first, which measures faster on MI355X (the two contend for the CUs)."""
+    main = torch.cuda.current_stream() if stream is None else stream
+    B, L = h.shape[:2]
+    r = W_A.shape[0]
+    dev = E.device
+    A_prev = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+    B_cur = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+    G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
+    if overlap:
+        side = side_stream(dev)
+        side.wait_stream(main)
+        project_gate(E, W_A, W_H, h, verified, A_prev, G, stream=side)
+        cand_id, cand_u = select_topk(logits, vocab, stream=main)
+        main.wait_stream(side)
+    else:
+        project_gate(E, W_A, W_H, h, verified, A_prev, G, stream=main)
+        cand_id, cand_u = select_topk(logits, vocab, stream=main)
+    project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, stream=main)
     res = score_pairs(cand_u, A_prev, B_cur, G, want_S=want_S, walk_mode=mode, cand_id=cand_id,
-                      temperature=temperature, uniforms=uniforms, want_q=want_q, stream=stream)
+                      temperature=temperature, uniforms=uniforms, want_q=want_q, stream=main)
     res.update(cand_id=cand_id, cand_u=cand_u, A_prev=A_prev, B_cur=B_cur, G=G)
     return res

@@ -10,6 +10,7 @@ constexpr int kK = 16;       // candidates per draft position
 constexpr int kWave = 64;    // CDNA wavefront width
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 

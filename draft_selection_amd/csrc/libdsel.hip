@@ -27,7 +27,10 @@ inline dsel_status launch(const void *kernel, dim3 grid, dim3 block, void *arg, 
     return e == hipSuccess ? DSEL_OK : DSEL_E_HIP;
 }
 
-constexpr int kTopkUnroll = 4;
+#ifndef DSEL_TOPK_UNROLL
+#define DSEL_TOPK_UNROLL 4
+#endif
+constexpr int kTopkUnroll = DSEL_TOPK_UNROLL;  // 16-byte vectors in flight per lane
 
 dsel_status check_walk(const dsel_walk_args *w, WalkParams *out) {
     if (!w) return DSEL_E_ARG;
@@ -94,76 +97,168 @@ DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t
     return launch(k2, dim3((unsigned)rows), dim3(64), &p, 0, stream);
 }
 
-DSEL_API dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
-                                  const uint16_t *W_B, const uint16_t *W_H, int64_t r,
-                                  const uint16_t *h, const int32_t *cand_id,
-                                  const int32_t *verified, int64_t batch, int64_t block,
-                                  float *A_prev, float *B_cur, float *G, dsel_stream_t stream) {
+namespace {
+
+dsel_status check_project_common(const uint16_t *E, int64_t vocab, int64_t d, int64_t r,
+                                 int64_t batch, int64_t block) {
     if (vocab < 1 || vocab >= (int64_t)INT_MAX || d < 64 || d % 64 != 0 || d > (1 << 20)) return DSEL_E_ARG;
     if (r < 32 || r > DSEL_MAX_RANK || r % 32 != 0) return DSEL_E_ARG;
     if (batch < 0 || block < 1 || batch > (1 << 24) || block > (1 << 16)) return DSEL_E_ARG;
-    if (batch == 0) return DSEL_OK;  // nothing to read or write; pointers may be NULL
-    if (!E || !W_A || !W_B || !W_H || !h || !cand_id || !verified || !A_prev || !B_cur || !G)
-        return DSEL_E_ARG;
-    if (!aligned(E, 16) || !aligned(W_A, 16) || !aligned(W_B, 16) || !aligned(W_H, 16) ||
-        !aligned(h, 16) || !aligned(cand_id, 4) || !aligned(verified, 4) || !aligned(A_prev, 4) ||
-        !aligned(B_cur, 4) || !aligned(G, 4))
-        return DSEL_E_ALIGN;
+    if (batch > 0 && !E) return DSEL_E_ARG;
+    if (!aligned(E, 16)) return DSEL_E_ALIGN;
+    return DSEL_OK;
+}
 
-    const bool big = (r % 128) == 0;
-    const int BM = big ? 128 : 64, BN = big ? 128 : 32;
-    ProjParams p;
+}  // namespace
+
+DSEL_API size_t dsel_project_workspace_bytes(int64_t batch, int64_t block, int64_t d, int64_t r) {
+    if (batch <= 0 || block < 1 || d < 64 || d % 64 != 0 || r < 32 || r > DSEL_MAX_RANK || r % 32 != 0)
+        return 0;
+    return gate_workspace_bytes(batch, block, d, r);
+}
+
+DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d,
+                                       const uint16_t *W_A, const uint16_t *W_H, int64_t r,
+                                       const uint16_t *h, const int32_t *verified, int64_t batch,
+                                       int64_t block, float *A_prev, float *G, void *workspace,
+                                       size_t workspace_bytes, dsel_stream_t stream) {
+    dsel_status st = check_project_common(E, vocab, d, r, batch, block);
+    if (st != DSEL_OK || batch == 0) return st;
+    if (!W_A || !W_H || !h || !verified || !A_prev || !G) return DSEL_E_ARG;
+    if (!aligned(W_A, 16) || !aligned(W_H, 16) || !aligned(h, 16) || !aligned(verified, 4) ||
+        !aligned(A_prev, 4) || !aligned(G, 4))
+        return DSEL_E_ALIGN;
+    const size_t need = gate_workspace_bytes(batch, block, d, r);
+    if (need && (!workspace || workspace_bytes < need)) return DSEL_E_WORKSPACE;
+    if (need && !aligned(workspace, 16)) return DSEL_E_ALIGN;
+    GateParams p;
+    p.E = E;
+    p.V = vocab;
+    p.d = (int)d;
+    p.r = (int)r;
+    p.WA = W_A;
+    p.WH = W_H;
+    p.h = h;
+    p.ver = verified;
+    p.B = (int)batch;
+    p.L = (int)block;
+    p.A_prev = A_prev;
+    p.G = G;
+    p.part = (float *)workspace;
+    const int BN = r % 256 == 0 ? 256 : r % 128 == 0 ? 128 : r % 64 == 0 ? 64 : 32;
+    p.nside = (int)(r / BN);
+    p.mt_gate = (int)((batch * block + 127) / 128);
+    p.mt_ver = (int)((batch + 127) / 128);
+    p.nsplit = gate_nsplit(batch, block, d, r);
+    const int64_t grid = (int64_t)(p.mt_gate + p.mt_ver) * p.nside * p.nsplit;
+    if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
+    const void *k = BN == 256 ? (const void *)project_gate_kernel<256>
+                  : BN == 128 ? (const void *)project_gate_kernel<128>
+                  : BN == 64  ? (const void *)project_gate_kernel<64>
+                              : (const void *)project_gate_kernel<32>;
+    const int nt = BN == 256 ? CandTile<256>::NT : CandTile<128>::NT;
+    st = launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
+    if (st != DSEL_OK || p.nsplit == 1) return st;
+    const int64_t elems = (batch * block + batch) * r;
+    return launch((const void *)project_gate_reduce_kernel, dim3((unsigned)((elems + 255) / 256)), dim3(256),
+                  &p, 0, stream);
+}
+
+DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d,
+                                       const uint16_t *W_A, const uint16_t *W_B, int64_t r,
+                                       const int32_t *cand_id, int64_t batch, int64_t block,
+                                       float *A_prev, float *B_cur, dsel_stream_t stream) {
+    dsel_status st = check_project_common(E, vocab, d, r, batch, block);
+    if (st != DSEL_OK || batch == 0) return st;
+    if (!W_A || !W_B || !cand_id || !A_prev || !B_cur) return DSEL_E_ARG;
+    if (!aligned(W_A, 16) || !aligned(W_B, 16) || !aligned(cand_id, 4) || !aligned(A_prev, 4) ||
+        !aligned(B_cur, 4))
+        return DSEL_E_ALIGN;
+    CandParams p;
     p.E = E;
     p.V = vocab;
     p.d = (int)d;
     p.r = (int)r;
     p.WA = W_A;
     p.WB = W_B;
-    p.WH = W_H;
-    p.h = h;
     p.cand = cand_id;
-    p.ver = verified;
-    p.B = (int)batch;
     p.L = (int)block;
+    p.M = batch * block * kK;
     p.A_prev = A_prev;
     p.B_cur = B_cur;
-    p.G = G;
-    p.m_cand = batch * block * kK;
-    p.m_ver = batch;
-    p.m_gate = batch * block;
-    p.nt_cand = (int)(2 * r / BN);
-    p.nt_ver = p.nt_gate = (int)(r / BN);
-    p.mt_cand = (int)((p.m_cand + BM - 1) / BM);
-    p.mt_cand_pad = (p.mt_cand + 7) / 8 * 8;
-    p.mt_ver = (int)((p.m_ver + BM - 1) / BM);
-    p.mt_gate = (int)((p.m_gate + BM - 1) / BM);
-    p.wg_cand = (int64_t)p.mt_cand_pad * p.nt_cand;
-    p.wg_ver = (int64_t)p.mt_ver * p.nt_ver;
-    const int64_t grid = p.wg_cand + p.wg_ver + (int64_t)p.mt_gate * p.nt_gate;
+    const int BM = 128;
+    const int BN = r % 256 == 0 ? 256 : r % 128 == 0 ? 128 : r % 64 == 0 ? 64 : 32;
+    p.nside = (int)(r / BN);
+    p.mt = (int)((p.M + BM - 1) / BM);
+    p.mt_pad = (p.mt + 7) / 8 * 8;
+    const int64_t grid = (int64_t)p.mt_pad * 2 * p.nside;
     if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
-    const void *k = big ? (const void *)project_kernel<128, 128> : (const void *)project_kernel<64, 32>;
-    return launch(k, dim3((unsigned)grid), dim3(256), &p, 0, stream);
+    const void *k = BN == 256 ? (const void *)project_cand_kernel<256>
+                  : BN == 128 ? (const void *)project_cand_kernel<128>
+                  : BN == 64  ? (const void *)project_cand_kernel<64>
+                              : (const void *)project_cand_kernel<32>;
+    const int nt = BN == 256 ? CandTile<256>::NT : CandTile<128>::NT;
+    return launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
 }
+
+DSEL_API dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                                  const uint16_t *W_B, const uint16_t *W_H, int64_t r,
+                                  const uint16_t *h, const int32_t *cand_id,
+                                  const int32_t *verified, int64_t batch, int64_t block,
+                                  float *A_prev, float *B_cur, float *G, void *workspace,
+                                  size_t workspace_bytes, dsel_stream_t stream) {
+    dsel_status st = check_project_common(E, vocab, d, r, batch, block);
+    if (st != DSEL_OK || batch == 0) return st;
+    if (!W_A || !W_B || !W_H || !h || !cand_id || !verified || !A_prev || !B_cur || !G)
+        return DSEL_E_ARG;
+    const size_t need = gate_workspace_bytes(batch, block, d, r);
+    if (need && (!workspace || workspace_bytes < need)) return DSEL_E_WORKSPACE;
+    st = dsel_project_gate(E, vocab, d, W_A, W_H, r, h, verified, batch, block, A_prev, G, workspace,
+                           workspace_bytes, stream);
+    if (st != DSEL_OK) return st;
+    return dsel_project_cand(E, vocab, d, W_A, W_B, r, cand_id, batch, block, A_prev, B_cur, stream);
+}
+
+namespace {
+
+const void *pair_kernel_for(int64_t r) {
+    switch (r) {
+        case 32: return (const void *)pair_kernel<32>;
+        case 64: return (const void *)pair_kernel<64>;
+        case 96: return (const void *)pair_kernel<96>;
+        case 128: return (const void *)pair_kernel<128>;
+        case 160: return (const void *)pair_kernel<160>;
+        case 192: return (const void *)pair_kernel<192>;
+        case 224: return (const void *)pair_kernel<224>;
+        case 256: return (const void *)pair_kernel<256>;
+    }
+    return nullptr;
+}
+
+dsel_status launch_walk(PairParams &p, dsel_stream_t stream) {
+    const int waves = p.L < 16 ? p.L : 16;
+    const size_t shmem = pair_walk_shmem(p.L, p.w.q != nullptr);
+    return launch((const void *)walk_kernel, dim3((unsigned)p.B), dim3(waves * kWave), &p, shmem, stream);
+}
+
+}  // namespace
 
 DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const float *B_cur,
                                       const float *G, int64_t batch, int64_t block, int64_t r,
                                       float *S, const dsel_walk_args *walk, dsel_stream_t stream) {
-    if (batch < 0 || batch >= (int64_t)INT_MAX || block < 1 || block > DSEL_MAX_BLOCK) return DSEL_E_ARG;
+    if (batch < 0 || batch >= (int64_t)INT_MAX / DSEL_MAX_BLOCK || block < 1 || block > DSEL_MAX_BLOCK)
+        return DSEL_E_ARG;
     if (r < 32 || r > DSEL_MAX_RANK || r % 32 != 0) return DSEL_E_ARG;
     if (walk && walk->mode != DSEL_GREEDY && walk->mode != DSEL_SAMPLED) return DSEL_E_DTYPE;
     if (batch == 0) return DSEL_OK;  // nothing to read or write; pointers may be NULL
-    if (!cand_u || !A_prev || !B_cur || !G) return DSEL_E_ARG;
-    if (!S && !walk) return DSEL_E_ARG;
+    if (!cand_u || !A_prev || !B_cur || !G || !S) return DSEL_E_ARG;
     if (!aligned(A_prev, 16) || !aligned(B_cur, 16) || !aligned(G, 16) || !aligned(cand_u, 4) ||
         !aligned(S, 4))
         return DSEL_E_ALIGN;
-    PairParams p;
-    p.do_walk = walk != nullptr;
+    PairParams p = {};
     if (walk) {
         dsel_status s = check_walk(walk, &p.w);
         if (s != DSEL_OK) return s;
-    } else {
-        p.w = WalkParams{};
     }
     p.cand_u = cand_u;
     p.A_prev = A_prev;
@@ -173,32 +268,28 @@ DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, 
     p.L = (int)block;
     p.r = (int)r;
     p.S = S;
-    const int waves = block < 16 ? (int)block : 16;
-    const size_t shmem = (size_t)block * kK * kK * sizeof(float);
-    return launch((const void *)pair_walk_kernel, dim3((unsigned)batch), dim3(waves * kWave), &p,
-                  shmem, stream);
+    p.S_in = S;
+    const int64_t positions = batch * block;
+    dsel_status st = launch(pair_kernel_for(r), dim3((unsigned)((positions + 3) / 4)), dim3(256), &p, 0, stream);
+    if (st != DSEL_OK || !walk) return st;
+    return launch_walk(p, stream);
 }
 
 DSEL_API dsel_status dsel_walk(const float *S, int64_t batch, int64_t block,
                                const dsel_walk_args *walk, dsel_stream_t stream) {
     if (!walk) return DSEL_E_ARG;
-    if (batch < 0 || batch >= (int64_t)INT_MAX / 4 || block < 1 || block > DSEL_MAX_BLOCK) return DSEL_E_ARG;
+    if (batch < 0 || batch >= (int64_t)INT_MAX || block < 1 || block > DSEL_MAX_BLOCK) return DSEL_E_ARG;
     if (walk->mode != DSEL_GREEDY && walk->mode != DSEL_SAMPLED) return DSEL_E_DTYPE;
     if (batch == 0) return DSEL_OK;  // nothing to read or write; pointers may be NULL
     if (!S) return DSEL_E_ARG;
     if (!aligned(S, 4)) return DSEL_E_ALIGN;
-    WalkParams w;
-    dsel_status s = check_walk(walk, &w);
+    PairParams p = {};
+    dsel_status s = check_walk(walk, &p.w);
     if (s != DSEL_OK) return s;
-    struct {
-        const float *S;
-        int B, L;
-        WalkParams w;
-    } a = {S, (int)batch, (int)block, w};
-    void *args[] = {&a.S, &a.B, &a.L, &a.w};
-    hipError_t e = hipLaunchKernel((const void *)walk_kernel, dim3((unsigned)((batch + 3) / 4)),
-                                   dim3(256), args, 0, (hipStream_t)stream);
-    return e == hipSuccess ? DSEL_OK : DSEL_E_HIP;
+    p.S_in = S;
+    p.B = (int)batch;
+    p.L = (int)block;
+    return launch_walk(p, stream);
 }
 
 DSEL_API dsel_status dsel_device_error(int32_t *out_code, dsel_stream_t stream) {

@@ -5,12 +5,22 @@
 // greedily or by sampling.  "DFlash 2: The Drafter Stopped Guessing Alone",
 // "Selection beats correction", says the same.)
 //
-// One workgroup per draft block.  Wave w scores positions t = w, w + nw, ...:
-// the 16 x 16 table P[i][j] = sum_c A_prev[i][c] G[c] B_cur[j][c] is one fp32
-// MFMA accumulation (v_mfma_f32_16x16x4_f32, r/4 steps); every lane streams
-// 16-byte slices of its own A and B row straight from global memory, so the
-// operands need no LDS staging.  S = U + P goes to LDS (and to global memory
-// when asked); then wave 0 walks the block.
+// Two kernels:
+//  pair_kernel: one wave per position (b, t), four per workgroup, so the loads
+//     spread over the whole chip.  The 16 x 16 table
+//     P[i][j] = sum_c A_prev[i][c] G[c] B_cur[j][c] is one fp32 MFMA
+//     accumulation (v_mfma_f32_16x16x4_f32, r/4 steps); each lane streams
+//     16-byte slices of its own A and B row, two slices ahead of the MFMAs.
+//     S = U + P (row i >= 1 of position 0 is -inf) is written out.
+//  walk_kernel: one workgroup per draft block, wave w loading the score tables
+//     of positions t = w, w + nw, ... (16 KB per block), then:
+//  1. Decisions, in parallel for every predecessor row of every position: the
+//     greedy successor (highest score, ties to the lowest slot, NaN lowest), or
+//     the sampled one (inverse CDF of softmax(S_row / T) with the position's
+//     uniform).  In the MFMA output layout a row's 16 scores sit in one 16-lane
+//     DPP row, so every reduction and scan is four DPP steps.
+//  2. The walk itself is then a chain of L table look-ups from row 0 (the
+//     verified token), after which all lanes write the outputs.
 #pragma once
 
 #include "common.h"
@@ -18,7 +28,7 @@
 namespace dsel {
 
 struct WalkParams {
-    int mode;          // 0 greedy, 1 sampled
+    int mode;  // 0 greedy, 1 sampled
     float temperature;
     const float *uniforms;
     const int32_t *cand_id;
@@ -28,130 +38,206 @@ struct WalkParams {
 
 struct PairParams {
     const float *cand_u, *A_prev, *B_cur, *G;
+    const float *S_in;  // stand-alone walk: scores to walk
     int B, L, r;
-    float *S;        // nullable
-    int do_walk;
+    float *S;  // scores out
     WalkParams w;
 };
 
-// One walk step over the 16 scores s (lanes 0..15 hold slot j = lane).
-// Returns the chosen slot (wave-uniform) and writes q (lanes 0..15) if asked.
-__device__ __forceinline__ int walk_step(float s, int mode, float T, float u, float *q_out) {
-    const uint32_t lane = lane_id();
-    const bool act = lane < (uint32_t)kK;
-    // greedy pick: highest score, ties to the lowest slot, NaN lowest
-    uint64_t key = act ? (((uint64_t)order_bits(s) << 32) | (uint32_t)(31 - lane)) : 0ull;
-#pragma unroll
-    for (int o = 1; o < kK; o <<= 1) {
-        uint64_t other = shfl_idx64(key, lane ^ (uint32_t)o);
-        key = other > key ? other : key;
-    }
-    const int greedy = 31 - (int)(readlane64(key, 0) & 0xFFu);
-    if (mode == 0) {
-        if (q_out && act) *q_out = (lane == (uint32_t)greedy) ? 1.0f : 0.0f;
-        return greedy;
-    }
-    // sampled: softmax(s / T) over the 16 slots, NaN given zero weight
-    float sv = (act && s == s) ? s : -__builtin_inff();
-    float m = sv;
-#pragma unroll
-    for (int o = 1; o < kK; o <<= 1) m = fmaxf(m, shfl_idxf(m, lane ^ (uint32_t)o));
-    m = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(m), 0));  // lane 0 holds the 16-slot max
-    if (m == -__builtin_inff()) {
-        if (q_out && act) *q_out = (lane == (uint32_t)greedy) ? 1.0f : 0.0f;
-        return greedy;
-    }
-    float e;
-    if (!act || !(s == s)) e = 0.0f;
-    else if (m == __builtin_inff()) e = (s == __builtin_inff()) ? 1.0f : 0.0f;
-    else e = expf((s - m) / T);
-    // inclusive prefix sum over lanes 0..15 in slot order
-    float c = e;
-#pragma unroll
-    for (int o = 1; o < kK; o <<= 1) {
-        float y = shfl_idxf(c, lane >= (uint32_t)o ? lane - o : lane);
-        if ((lane & 15u) >= (uint32_t)o) c += y;
-    }
-    const float Z = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(c), kK - 1));
-    const float uz = u * Z;
-    uint64_t hit = ballot(act && uz < c);
-    int pick;
-    const uint64_t pos = ballot(act && e > 0.0f);  // never empty: the max has weight 1
-    if (hit) pick = (int)__builtin_ctzll(hit);
-    else if (pos) pick = 63 - (int)__builtin_clzll(pos);
-    else pick = greedy;
-    if (q_out && act) *q_out = e / Z;
-    return pick;
+// DPP controls (gfx9): quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror; row_shr:n is 0x110 + n.
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, false);
 }
 
-// Walk one block; S_row(t, row) returns lane j's score S[b,t,row,j].
-template <typename RowFn>
-__device__ __forceinline__ void walk_block(const WalkParams &w, int b, int L, RowFn S_row) {
+// Max over each 16-lane row, result in every lane of the row.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t x) {
+    x = max(x, dpp_u32<kDppXor1>(x));
+    x = max(x, dpp_u32<kDppXor2>(x));
+    x = max(x, dpp_u32<kDppHalfMirror>(x));
+    x = max(x, dpp_u32<kDppMirror>(x));
+    return x;
+}
+
+__device__ __forceinline__ float row16_max_f(float x) {
+    x = fmaxf(x, __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(x))));
+    x = fmaxf(x, __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(x))));
+    return x;
+}
+
+// Inclusive prefix sum over each 16-lane row (slot order): DPP row_shr with
+// zeros shifted in at the row start.
+template <int SH>
+__device__ __forceinline__ float shr_row(float x) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(x), 0x110 + SH, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float row16_scan(float x) {
+    x += shr_row<1>(x);
+    x += shr_row<2>(x);
+    x += shr_row<4>(x);
+    x += shr_row<8>(x);
+    return x;
+}
+
+// Per-block LDS: for each position the chosen slot of every predecessor row,
+// its score, and (when q is requested) every row's step distribution.
+struct BlockShared {
+    float *Q;     // [L][16][16] (only when q is requested)
+    float *sc;    // [L][16] score of the chosen slot of each row
+    uint8_t *ch;  // [L][16] chosen slot of each row
+    int *row;     // [L] predecessor row of the walk at each position
+};
+
+// Decisions of one position from its score table held in the MFMA layout:
+// s[v] = S[i = 4 g + v][j = lane & 15] with g = lane >> 4.
+__device__ __forceinline__ void decide_position(const float (&s)[4], int t, const WalkParams &w,
+                                                float u, bool want_q, BlockShared &sh) {
     const uint32_t lane = lane_id();
-    int row = 0;  // the last verified token
-    for (int t = 0; t < L; ++t) {
-        const int64_t bt = (int64_t)b * L + t;
-        float s = lane < (uint32_t)kK ? S_row(t, row, (int)lane) : 0.0f;
-        float u = w.mode == 1 ? w.uniforms[bt] : 0.0f;
-        float *qp = w.q ? w.q + bt * kK + lane : nullptr;
-        int j = walk_step(s, w.mode, w.temperature, u, qp);
-        float sj = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(s), j));
-        if (lane == 0) {
-            w.path_slot[bt] = j;
-            w.path_tok[bt] = w.cand_id[bt * kK + j];
-            if (w.path_s) w.path_s[bt] = sj;
+    const int g = (int)(lane >> 4), j = (int)(lane & 15);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int i = 4 * g + v;
+        // greedy successor of row i: highest order key, lowest slot among ties
+        const uint32_t ob = order_bits(s[v]);
+        const uint32_t mx = row16_max_u32(ob);
+        const uint32_t seg_eq = (uint32_t)(ballot(ob == mx) >> (16 * g)) & 0xFFFFu;
+        int pick = __builtin_ctz(seg_eq);
+        if (w.mode == 1) {
+            const bool isnum = s[v] == s[v];
+            const float m = row16_max_f(isnum ? s[v] : -__builtin_inff());
+            float e;
+            if (m == -__builtin_inff()) e = (j == pick) ? 1.0f : 0.0f;  // no weight: greedy pick
+            else if (!isnum) e = 0.0f;
+            else if (m == __builtin_inff()) e = (s[v] == __builtin_inff()) ? 1.0f : 0.0f;
+            else e = expf((s[v] - m) / w.temperature);
+            const float c = row16_scan(e);
+            const float Z = shfl_idxf(c, (lane & ~15u) | 15u);
+            const uint32_t seg_hit = (uint32_t)(ballot(u * Z < c) >> (16 * g)) & 0xFFFFu;
+            const uint32_t seg_pos = (uint32_t)(ballot(e > 0.0f) >> (16 * g)) & 0xFFFFu;
+            if (seg_hit) pick = __builtin_ctz(seg_hit);
+            else if (seg_pos) pick = 31 - __builtin_clz(seg_pos);
+            if (want_q) sh.Q[(t * kK + i) * kK + j] = e / Z;
+        } else if (want_q) {
+            sh.Q[(t * kK + i) * kK + j] = (j == pick) ? 1.0f : 0.0f;
         }
-        row = j;
+        const float sp = shfl_idxf(s[v], (lane & ~15u) | (uint32_t)pick);
+        if (j == 0) {
+            sh.ch[t * kK + i] = (uint8_t)pick;
+            sh.sc[t * kK + i] = sp;
+        }
     }
 }
 
-__global__ __launch_bounds__(1024) void pair_walk_kernel(PairParams p) {
-    extern __shared__ float Ssh[];  // [L][16][16]
+// Step 1 for one position: the score table in registers (MFMA layout).
+template <int R>
+__device__ __forceinline__ void score_position(const PairParams &p, int64_t bt, int t, float (&s)[4]) {
+    const uint32_t lane = lane_id();
+    const int fr = lane & 15, fg = lane >> 4;
+    const float *Ap = p.A_prev + (bt * kK + fr) * R + 4 * fg;
+    const float *Bp = p.B_cur + (bt * kK + fr) * R + 4 * fg;
+    const float *Gp = p.G + bt * R + 4 * fg;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    constexpr int NS = R / 16;  // 16-wide slices of the rank (even: R % 32 == 0)
+    float4 a[2][2], g[2][2], b[2][2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        a[0][q] = *(const float4 *)(Ap + 16 * q);
+        g[0][q] = *(const float4 *)(Gp + 16 * q);
+        b[0][q] = *(const float4 *)(Bp + 16 * q);
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < NS; s0 += 2) {
+        const int cur = (s0 / 2) & 1, nxt = cur ^ 1;
+        if (s0 + 2 < NS) {
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                a[nxt][q] = *(const float4 *)(Ap + 16 * (s0 + 2 + q));
+                g[nxt][q] = *(const float4 *)(Gp + 16 * (s0 + 2 + q));
+                b[nxt][q] = *(const float4 *)(Bp + 16 * (s0 + 2 + q));
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cur][q].x * g[cur][q].x, b[cur][q].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cur][q].y * g[cur][q].y, b[cur][q].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cur][q].z * g[cur][q].z, b[cur][q].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cur][q].w * g[cur][q].w, b[cur][q].w, acc, 0, 0, 0);
+        }
+    }
+    const float u = p.cand_u[bt * kK + fr];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int i = 4 * fg + v;
+        s[v] = (t == 0 && i >= 1) ? -__builtin_inff() : u + acc[v];
+    }
+}
+
+// Scores of one position per wave.
+template <int R>
+__global__ __launch_bounds__(256) void pair_kernel(PairParams p) {
+    const int64_t bt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (bt >= (int64_t)p.B * p.L) return;
+    const int t = (int)(bt % p.L);
+    const uint32_t lane = lane_id();
+    float s[4];
+    score_position<R>(p, bt, t, s);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) p.S[(bt * kK + 4 * (lane >> 4) + v) * kK + (lane & 15)] = s[v];
+}
+
+// The walk over scores in global memory: one workgroup per block.
+__global__ __launch_bounds__(1024) void walk_kernel(PairParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    const int L = p.L;
+    const bool want_q = p.w.q != nullptr;
+    BlockShared sh;
+    sh.Q = (float *)smem;
+    sh.sc = sh.Q + (want_q ? L * kK * kK : 0);
+    sh.row = (int *)(sh.sc + L * kK);
+    sh.ch = (uint8_t *)(sh.row + L);
+
     const int b = blockIdx.x;
     const int nwave = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave;
     const uint32_t lane = lane_id();
-    const int r = p.r;
-    const int fr = lane & 15, fg = lane >> 4;
-
-    for (int t = wave; t < p.L; t += nwave) {
-        const int64_t bt = (int64_t)b * p.L + t;
-        const float *Ap = p.A_prev + (bt * kK + fr) * r + 4 * fg;
-        const float *Bp = p.B_cur + (bt * kK + fr) * r + 4 * fg;
-        const float *Gp = p.G + bt * r + 4 * fg;
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int c0 = 0; c0 < r; c0 += 16) {
-            const float4 a = *(const float4 *)(Ap + c0);
-            const float4 g = *(const float4 *)(Gp + c0);
-            const float4 bb = *(const float4 *)(Bp + c0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.x * g.x, bb.x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.y * g.y, bb.y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.z * g.z, bb.z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.w * g.w, bb.w, acc, 0, 0, 0);
-        }
-        // acc[v] = P[i = 4 fg + v][j = fr]
-        const float u = p.cand_u[bt * kK + fr];
+    for (int t = wave; t < L; t += nwave) {
+        const int64_t bt = (int64_t)b * L + t;
+        float s[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int i = 4 * fg + v;
-            const float sv = (t == 0 && i >= 1) ? -__builtin_inff() : u + acc[v];
-            Ssh[(t * kK + i) * kK + fr] = sv;
-            if (p.S) p.S[(bt * kK + i) * kK + fr] = sv;
+        for (int v = 0; v < 4; ++v) s[v] = p.S_in[(bt * kK + 4 * (lane >> 4) + v) * kK + (lane & 15)];
+        const float u = p.w.mode == 1 ? p.w.uniforms[bt] : 0.0f;
+        decide_position(s, t, p.w, u, want_q, sh);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int row = 0;  // the last verified token
+        for (int t = 0; t < L; ++t) {
+            sh.row[t] = row;
+            row = sh.ch[t * kK + row];
         }
     }
-    if (!p.do_walk) return;
     __syncthreads();
-    if (wave == 0)
-        walk_block(p.w, b, p.L, [&](int t, int row, int j) { return Ssh[(t * kK + row) * kK + j]; });
+    for (int e = threadIdx.x; e < L * kK; e += blockDim.x) {
+        const int t = e / kK, j = e % kK;
+        const int64_t bt = (int64_t)b * L + t;
+        const int row = sh.row[t];
+        if (j == 0) {
+            const int c = sh.ch[t * kK + row];
+            p.w.path_slot[bt] = c;
+            p.w.path_tok[bt] = p.w.cand_id[bt * kK + c];
+            if (p.w.path_s) p.w.path_s[bt] = sh.sc[t * kK + row];
+        }
+        if (want_q) p.w.q[bt * kK + j] = sh.Q[(t * kK + row) * kK + j];
+    }
 }
 
-// The walk alone over scores in global memory: one wave per block.
-__global__ __launch_bounds__(256) void walk_kernel(const float *S, int B, int L, WalkParams w) {
-    const int b = blockIdx.x * 4 + (int)(threadIdx.x / kWave);
-    if (b >= B) return;
-    walk_block(w, b, L, [&](int t, int row, int j) {
-        return S[((((int64_t)b * L + t) * kK) + row) * kK + j];
-    });
+inline size_t pair_walk_shmem(int L, bool want_q) {
+    return (size_t)L * ((want_q ? kK * kK * sizeof(float) : 0) + kK * sizeof(float) + sizeof(int) + kK);
 }
 
 }  // namespace dsel

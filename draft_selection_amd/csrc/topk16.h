@@ -232,9 +232,12 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(TopkParams p) {
 
 // Workgroups per row: enough rows x splits to fill 256 CUs several times over,
 // but never slices shorter than 4096 elements.
+#ifndef DSEL_TOPK_TARGET_WG
+#define DSEL_TOPK_TARGET_WG 1024
+#endif
 inline int topk_nsplit(int64_t rows, int64_t V) {
     if (rows <= 0) return 1;
-    int64_t want = (1024 + rows - 1) / rows;
+    int64_t want = (DSEL_TOPK_TARGET_WG + rows - 1) / rows;
     int64_t cap = V / 4096;
     if (cap < 1) cap = 1;
     if (want > cap) want = cap;

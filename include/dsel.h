@@ -43,7 +43,7 @@ extern "C" {
 #endif
 
 #define DSEL_K 16          /* candidates kept per draft position ([P1] Method) */
-#define DSEL_MAX_BLOCK 64  /* longest draft block accepted by score_pairs / walk */
+#define DSEL_MAX_BLOCK 32  /* longest draft block accepted by score_pairs / walk */
 #define DSEL_MAX_RANK 256  /* largest selector rank r ([P1]: 256-d token vectors) */
 
 typedef void *dsel_stream_t; /* a hipStream_t */
@@ -101,13 +101,37 @@ dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t batch, i
  *   G        out [batch, block, r] fp32: sigmoid(W_H h[t]).
  * Products are bf16 x bf16 with fp32 accumulation (MFMA).  A token id outside
  * [0, vocab) reads a zero embedding row and sets DSEL_DEVERR_TOKEN_RANGE in the
- * device error word.  Requirements: d % 64 == 0, r % 32 == 0, 32 <= r <= 256,
- * 1 <= block, batch >= 0, 1 <= vocab < 2^31; all pointers 16-byte aligned. */
+ * device error word.
+ *   workspace  device scratch of at least dsel_project_workspace_bytes() bytes
+ *            (may be NULL when that is 0); contents need no initialisation.
+ * Requirements: d % 64 == 0, r % 32 == 0, 32 <= r <= 256, 1 <= block,
+ * batch >= 0, 1 <= vocab < 2^31; all pointers 16-byte aligned. */
 dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
                          const uint16_t *W_B, const uint16_t *W_H, int64_t r, const uint16_t *h,
                          const int32_t *cand_id, const int32_t *verified, int64_t batch,
-                         int64_t block, float *A_prev, float *B_cur, float *G,
-                         dsel_stream_t stream);
+                         int64_t block, float *A_prev, float *B_cur, float *G, void *workspace,
+                         size_t workspace_bytes, dsel_stream_t stream);
+
+/* Bytes of device workspace dsel_project / dsel_project_gate need (0 when none;
+ * also 0 for invalid arguments, which the calls themselves reject). */
+size_t dsel_project_workspace_bytes(int64_t batch, int64_t block, int64_t d, int64_t r);
+
+/* The two halves of dsel_project, for callers that schedule them apart:
+ * project_gate needs no candidates (G and position 0's predecessor rows of
+ * A_prev), so it may run while dsel_select_topk is still running, e.g. on a
+ * second stream; project_cand computes B_cur and A_prev of positions >= 1 from
+ * the candidates and needs no workspace.  Arguments, layouts and requirements
+ * as for dsel_project; each writes only the outputs named here (and
+ * project_gate its workspace). */
+dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                              const uint16_t *W_H, int64_t r, const uint16_t *h,
+                              const int32_t *verified, int64_t batch, int64_t block, float *A_prev,
+                              float *G, void *workspace, size_t workspace_bytes,
+                              dsel_stream_t stream);
+dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                              const uint16_t *W_B, int64_t r, const int32_t *cand_id,
+                              int64_t batch, int64_t block, float *A_prev, float *B_cur,
+                              dsel_stream_t stream);
 
 /* Walk arguments ([P1] Method last paragraph, [P3]: the only sequential step;
  * greedy follows the best successor, sampling draws from the same scores).
@@ -143,8 +167,8 @@ typedef struct {
  *   S[b,t,i,j] = cand_u[b,t,j] + sum_c A_prev[b,t,i,c] G[b,t,c] B_cur[b,t,j,c]
  * for i < n_t (n_0 = 1, n_t = 16 for t >= 1); S[b,0,i>=1,:] = -inf.
  * fp32 arithmetic.  Inputs as produced by dsel_project / dsel_select_topk.
- *   S     out [batch, block, 16, 16] fp32; may be NULL when `walk` is given.
- *   walk  nullable: when given, the walk runs fused in the same launch.
+ *   S     out [batch, block, 16, 16] fp32 (required: the walk reads it).
+ *   walk  nullable: when given, the walk over S follows on the same stream.
  * Requirements: 1 <= block <= DSEL_MAX_BLOCK, r % 32 == 0, 32 <= r <= 256;
  * pointers 16-byte aligned. */
 dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const float *B_cur,

@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for want in ("dsel_select_topk", "dsel_project", "dsel_score_pairs", "dsel_walk"):
+    for want in ("dsel_select_topk", "dsel_project", "dsel_project_gate", "dsel_project_cand",
+                 "dsel_score_pairs", "dsel_walk"):
         assert want in names
 
 
@@ -43,6 +44,16 @@ def test_version_and_status_strings(lib):
     assert lib.dsel_version() == 100
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.dsel_status_string(code).startswith(b"DSEL_")
+
+
+def test_project_workspace_sizing(lib):
+    # the gate GEMM of 64 blocks of 16 is split along K across workgroups
+    assert lib.dsel_project_workspace_bytes(64, 16, 2560, 256) > 0
+    assert lib.dsel_project_workspace_bytes(64, 16, 96, 256) == 0  # d % 64 != 0: invalid
+    fake = C.c_void_p(0x100000)
+    args = [fake, 151936, 2560, fake, fake, fake, 256, fake, fake, fake, 64, 16, fake, fake, fake,
+            None, 0, None]
+    assert lib.dsel_project(*args) == -4  # workspace missing
 
 
 def test_topk_workspace_sizing(lib):
@@ -66,7 +77,7 @@ def test_validation_rejects_before_launch(lib):
     assert lib.dsel_select_topk(odd, 1, 1, 1, 64, 64, fake, fake, None, 0, None) == -3
     assert lib.dsel_select_topk(fake, 1, 1, 16, 151936, 151936, fake, fake, None, 0, None) == -4
     # project
-    args = [fake, 1000, 64, fake, fake, fake, 32, fake, fake, fake, 2, 4, fake, fake, fake, None]
+    args = [fake, 1000, 64, fake, fake, fake, 32, fake, fake, fake, 2, 4, fake, fake, fake, None, 0, None]
     bad_d = list(args); bad_d[2] = 96
     bad_r = list(args); bad_r[6] = 48
     big_r = list(args); big_r[6] = 512
@@ -77,8 +88,10 @@ def test_validation_rejects_before_launch(lib):
     # score_pairs / walk
     w = ds.WalkArgs(5, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)
     assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, 32, fake, C.byref(w), None) == -2
-    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 65, 32, fake, None, None) == -1
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 33, 32, fake, None, None) == -1
     assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, 32, None, None, None) == -1
+    w = ds.WalkArgs(0, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, 32, None, C.byref(w), None) == -1
     w = ds.WalkArgs(1, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)  # sampled, no uniforms
     assert lib.dsel_walk(fake, 1, 8, C.byref(w), None) == -1
     w = ds.WalkArgs(1, 0.0, 0x100000, 0x100000, 0x100000, 0x100000, None, None)  # T = 0
