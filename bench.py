@@ -26,6 +26,16 @@ METRIC = "draft blocks/s through selector + achieved HBM GB/s & MFMA % of peak"
 HBM_PEAK_GBS = 8000.0      # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 K = 16
+# HBM byte counters against a plain 1 GiB device copy (--calibrate-copy): per
+# copied GiB FETCH_SIZE reads 0.5 GiB and WRITE_SIZE 1 GiB, so the counters'
+# KiB are multiplied by these factors to give bytes moved.
+FETCH_FACTOR = 2.0
+WRITE_FACTOR = 1.0
+# kernels whose traffic is recorded, and the sources each is built from
+TRAFFIC_KERNELS = {
+    "topk16": ("topk16_kernel", ["common.h", "topk16.h"]),
+    "project_cand": ("project_cand_kernel", ["common.h", "project.h"]),
+}
 
 
 def describe(cfg):
@@ -67,6 +77,59 @@ def traffic_from_profile(workload, kernel="topk16"):
     return float(t["fetch_bytes"]) + float(t["write_bytes"])
 
 
+def _counter_per_dispatch(run_dir, match):
+    """Mean Counter_Value over the dispatches whose kernel name contains `match`
+    in a rocprofv3 --pmc CSV directory (one counter per run)."""
+    import csv
+    import glob
+
+    vals = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if match in row["Kernel_Name"]:
+                    key = (path, row["Dispatch_Id"])
+                    vals[key] = vals.get(key, 0.0) + float(row["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no dispatch of {match} in {run_dir}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def record_traffic(workload, fetch_dir, write_dir, command):
+    """Write profiles/<kernel>_<workload>_traffic.json from a FETCH_SIZE run and
+    a WRITE_SIZE run of this script (KiB per dispatch, scaled by the copy
+    calibration), stamped with a hash of the kernel's sources."""
+    for kernel, (match, sources) in TRAFFIC_KERNELS.items():
+        f_kib, nf = _counter_per_dispatch(fetch_dir, match)
+        w_kib, nw = _counter_per_dispatch(write_dir, match)
+        rec = {"kernel": match, "workload": workload, "command": command,
+               "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+               "dispatches": [nf, nw], "fetch_factor": FETCH_FACTOR, "write_factor": WRITE_FACTOR,
+               "fetch_bytes": round(f_kib * 1024 * FETCH_FACTOR),
+               "write_bytes": round(w_kib * 1024 * WRITE_FACTOR),
+               "sources": sources, "source_hash": kernel_source_hash(sources)}
+        out = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+        with open(out, "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+        print(out, rec["fetch_bytes"], rec["write_bytes"])
+
+
+def calibrate_copy():
+    """Three plain device copies of 1 GiB: the reference dispatch for the HBM
+    byte counters."""
+    import torch
+
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print("copied 3 x 1 GiB", flush=True)
+
+
 def cpu_baseline(cfg, inp, budget_s=15.0):
     """The oracle as it stands, on the host cores, over as many blocks as fit in
     about `budget_s` seconds (at least one)."""
@@ -91,6 +154,15 @@ def cpu_baseline(cfg, inp, budget_s=15.0):
                       f"(top-16, fp64 projections, scores, walk), {t_total:.1f} s"}
 
 
+def stage_means(evs):
+    """Mean microseconds between consecutive stage events over the steps."""
+    names = ("project_gate", "select_topk", "project_cand", "score_pairs_walk")
+    out = {n: round(float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) * 1e3, 2)
+           for i, n in enumerate(names)}
+    out["step"] = round(float(np.mean([e[0].elapsed_time(e[4]) for e in evs])) * 1e3, 2)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -100,7 +172,19 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--gate", default="serial", choices=["serial", "overlap"],
                     help="run the gate GEMM before the top-16 or beside it on a second stream")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the pass that evicts the caches before every step")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
+                    help="write profiles/*_traffic.json for --workload from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the selector is block-parallel and this build runs on "
               "a single MI355X; run it with --gpus 1", file=sys.stderr)
@@ -147,6 +231,8 @@ def main():
         # stream beside the top-16 (the side stream first waits for the
         # previous step).
         sp = C.c_void_p(strm.cuda_stream)
+        if ev is not None:
+            ev[0].record(strm)
         if args.gate == "overlap":
             fork[0].record(strm)
             side.wait_event(fork[0])
@@ -156,20 +242,20 @@ def main():
         if args.gate == "overlap":
             fork[1].record(side)
         if ev is not None:
-            ev[0].record(strm)
+            ev[1].record(strm)
         s1 = lib.dsel_select_topk(P(d["logits"]), dt, B, L, V, V, P(cand_id), P(cand_u), P(ws), wsb, sp)
         if ev is not None:
-            ev[1].record(strm)
+            ev[2].record(strm)
         if args.gate == "overlap":
             strm.wait_event(fork[1])
         s2 = lib.dsel_project_cand(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_B"]), cfg.r, P(cand_id),
                                    B, L, P(A_prev), P(B_cur), sp)
         if ev is not None:
-            ev[2].record(strm)
+            ev[3].record(strm)
         s3 = lib.dsel_score_pairs(P(cand_u), P(A_prev), P(B_cur), P(G), B, L, cfg.r, P(S),
                                   C.byref(wargs), sp)
         if ev is not None:
-            ev[3].record(strm)
+            ev[4].record(strm)
         if s0 or s1 or s2 or s3:
             raise RuntimeError(f"dsel status {s0} {s1} {s2} {s3}")
 
@@ -179,7 +265,7 @@ def main():
 
     # (1) eager timed region: K steps with HIP events around every stage on the
     # stream the kernels run on (per-kernel durations for the roofline)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -208,23 +294,35 @@ def main():
     wall = time.perf_counter() - t0
     assert ds.device_error() == 0
 
+    # (3) cold caches: before every step a 1 GiB write evicts L2 and the
+    # Infinity Cache; the stage events exclude that write
+    cold = None
+    if not args.no_cold:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(float(i))
+            step(stream, cevs[i])
+        torch.cuda.synchronize()
+        del flush
+        cold = stage_means(cevs)
+
     ms_step = wall * 1e3 / args.steps
-    st_topk = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3   # us
-    st_proj = float(np.mean([e[1].elapsed_time(e[2]) for e in evs])) * 1e3  # project_cand (+ any wait for the gate)
-    st_pair = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) * 1e3
+    warm = stage_means(evs)
+    st_topk, st_proj, st_pair = warm["select_topk"], warm["project_cand"], warm["score_pairs_walk"]
     alg = algorithmic(cfg)
     topk_gbs = alg["topk_bytes"] / (st_topk * 1e-6) / 1e9
     proj_tfs = alg["cand_flop"] / (st_proj * 1e-6) / 1e12
 
-    traffic = traffic_from_profile(cfg.name)
     if st_topk >= st_proj:
         roof = {"kernel": "topk16", "bound": "hbm", "achieved": round(topk_gbs, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(topk_gbs / HBM_PEAK_GBS, 4),
-                "traffic": traffic}
+                "traffic": traffic_from_profile(cfg.name, "topk16")}
     else:
         roof = {"kernel": "project_cand", "bound": "mfma", "achieved": round(proj_tfs, 2),
                 "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4),
+                "traffic": traffic_from_profile(cfg.name, "project_cand")}
 
     out = {
         "metric": METRIC,
@@ -243,9 +341,10 @@ def main():
                    "r": cfg.r, "logits": cfg.logits_dtype, "walk": "sampled" if mode else "greedy"},
         "us_per_block": round(ms_step * 1e3 / B, 4),
         "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 5),
-        "timing": "value: the step as one HIP graph replayed K times; stages: eager launches with HIP events",
-        "stages_us": {"select_topk": round(st_topk, 2), "project_cand": round(st_proj, 2),
-                      "score_pairs_walk": round(st_pair, 2)},
+        "timing": "value: the step as one HIP graph replayed K times; stages: eager launches with "
+                  "HIP events on the launch stream (stages_us_cold: after a 1 GiB cache-evicting write)",
+        "stages_us": warm,
+        "stages_us_cold": cold,
         "select_topk_hbm": {"GB/s": round(topk_gbs, 1), "frac": round(topk_gbs / HBM_PEAK_GBS, 4)},
         "project_cand_mfma": {"TFLOP/s": round(proj_tfs, 2), "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4)},
         "project_gate": args.gate,

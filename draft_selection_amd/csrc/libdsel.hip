@@ -156,7 +156,7 @@ DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t
                   : BN == 128 ? (const void *)project_gate_kernel<128>
                   : BN == 64  ? (const void *)project_gate_kernel<64>
                               : (const void *)project_gate_kernel<32>;
-    const int nt = BN == 256 ? CandTile<256>::NT : CandTile<128>::NT;
+    const int nt = tile_threads(BN);
     st = launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
     if (st != DSEL_OK || p.nsplit == 1) return st;
     const int64_t elems = (batch * block + batch) * r;
@@ -197,7 +197,7 @@ DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t
                   : BN == 128 ? (const void *)project_cand_kernel<128>
                   : BN == 64  ? (const void *)project_cand_kernel<64>
                               : (const void *)project_cand_kernel<32>;
-    const int nt = BN == 256 ? CandTile<256>::NT : CandTile<128>::NT;
+    const int nt = tile_threads(BN);
     return launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
 }
 

@@ -22,8 +22,11 @@
 // Main loop (mma_tile_dma): a K step is 64 deep (128 bytes of every row).
 // Tiles move from global memory straight into a three-stage LDS ring
 // (global_load_lds_dwordx4, no staging registers), two steps ahead of the
-// MFMAs.  In LDS the 16-byte chunks of each row are XOR-swizzled by (row & 7)
-// so the fragment reads are bank-conflict free.  The waves of a workgroup form
+// MFMAs.  In LDS the 16-byte chunk c of tile row `row` sits at chunk
+// c ^ key(row), key(row) = (row / 2) % 8: a fragment read serves 16 lanes (16
+// consecutive rows, one chunk each, 256 bytes) per LDS pass, and the 8 even and
+// the 8 odd rows of such a group (lower and upper 32 banks) then hit 8
+// distinct chunks each, free of bank conflicts.  The waves of a workgroup form
 // a GM x GN grid, each owning (BM/GM) x (BN/GN) of the tile as 32 x 32 MFMA
 // blocks.
 #pragma once
@@ -34,8 +37,6 @@ namespace dsel {
 
 constexpr int kBK = 64;  // K elements per step (128 bytes per row)
 
-// Element offset of 16-byte chunk `ch` (0..7) of tile row `row` in one buffer.
-__device__ __forceinline__ int lds_off(int row, int ch) { return row * kBK + ((ch ^ (row & 7)) << 3); }
 
 // BM x BN tile computed by GM x GN waves, each owning WM x WN as 32 x 32 MFMA
 // blocks (v_mfma_f32_32x32x16_bf16: one wave keeps the matrix core near its
@@ -78,7 +79,23 @@ __device__ __forceinline__ void lds_dma16(const void *src, uint16_t *lds_base) {
                  : "memory", "m0");
 }
 
-// acc += X * W^T over K steps [k0, k1) (64-deep steps).
+// s_waitcnt vmcnt(N) lgkmcnt(0): own LDS reads done and all but the last N
+// vector-memory loads landed.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | ((N >> 4) << 14));
+}
+
+// acc += X * W^T over K steps [k0, k1) (64-deep steps), k1 > k0.
+//
+// Schedule of one step (four 16-deep slices): while slice s multiplies, the
+// fragments of slice s+1 are read from LDS into the other register buffer.  At
+// the last slice the wave first waits for its own reads and for its DMA of the
+// next step, then meets the others at the barrier (after which every wave is
+// done with this stage and the next stage is complete), refills this stage
+// three steps ahead and reads the first fragments of the next step, all ahead
+// of the last slice's MFMAs, so no LDS latency is exposed at a step boundary.
 template <class T>
 __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DXI], const uint16_t *wbase,
                                              int64_t wstride, int k0, int k1, uint16_t *Xs,
@@ -88,20 +105,30 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
     static_assert(XI >= 1 && WI >= 1 && XI * NW * 8 == BM && WI * NW * 8 == BN, "DMA tile shape");
     constexpr int PER = XI + WI;  // loads per wave per step
     constexpr int NS = 3;
+    constexpr int KS = kBK / 16;  // 16-deep slices per step
     const int tid = threadIdx.x;
     const uint32_t lane = lane_id();
     const int wave = tid >> 6;
     const int wm = wave / T::GNv, wn = wave % T::GNv;
     const int fr = lane & 31, fk = lane >> 5;  // fragment row / column, 8-element K half
     // this lane's W source rows 8 (wave + NW u) + lane / 8; physical chunk
-    // lane % 8 of row `row` holds logical chunk (lane % 8) ^ (row & 7).
+    // lane % 8 of row `row` holds logical chunk (lane % 8) ^ key(row).
     const int lrow = (int)(lane >> 3), pch = (int)(lane & 7);
     const uint16_t *wsrc[WI];
 #pragma unroll
     for (int u = 0; u < WI; ++u) {
         const int row = 8 * (wave + NW * u) + lrow;
-        wsrc[u] = wbase + (int64_t)row * wstride + ((pch ^ (row & 7)) << 3);
+        wsrc[u] = wbase + (int64_t)row * wstride + ((pch ^ ((row >> 1) & 7)) << 3);
     }
+    // LDS element offsets of the rows of this lane's fragments, relative to a
+    // stage; every such row is = fr (mod 32), so chunk (2 s + fk) of it sits
+    // at physical chunk (2 s + fk) ^ key(fr)
+    int aoff[T::TM], boff[T::TN];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) aoff[i] = (wm * T::WM + i * 32 + fr) * kBK;
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) boff[j] = (wn * T::WN + j * 32 + fr) * kBK;
+    const int rsw = (fr >> 1) & 7;
 #define DSEL_ISSUE(k, stage)                                                                   \
     do {                                                                                       \
         const int kk_ = ((k) < k1 ? (k) : k1 - 1) * kBK;                                       \
@@ -110,32 +137,37 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
         _Pragma("unroll") for (int u = 0; u < WI; ++u)                                         \
             lds_dma16(wsrc[u] + kk_, Ws + (stage) * BN * kBK + (8 * (wave + NW * u)) * kBK);   \
     } while (0)
+#define DSEL_FRAG(buf, xb_, wb_, s_)                                                           \
+    do {                                                                                       \
+        const int ch_ = (((s_) * 2 + fk) ^ rsw) << 3;                                          \
+        _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                      \
+            a[buf][i] = *(const bf16x8 *)((xb_) + aoff[i] + ch_);                              \
+        _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                      \
+            b[buf][j] = *(const bf16x8 *)((wb_) + boff[j] + ch_);                              \
+    } while (0)
 
+    bf16x8 a[2][T::TM], b[2][T::TN];
     DSEL_ISSUE(k0, 0);
     DSEL_ISSUE(k0 + 1, 1);
+    DSEL_ISSUE(k0 + 2, 2);
+    wait_vmcnt<2 * PER>();
+    wg_barrier();
+    DSEL_FRAG(0, Xs, Ws, 0);
     int cur = 0;
     for (int kt = k0; kt < k1; ++kt) {
-        wait_vmcnt<PER>();  // this wave's loads of step kt have landed
-        wg_barrier();       // ... everyone's have, and step kt-1 is no longer read
-        DSEL_ISSUE(kt + 2, cur == 0 ? 2 : cur - 1);
+        const int nxt = cur == NS - 1 ? 0 : cur + 1;
         const uint16_t *xb = Xs + cur * BM * kBK;
         const uint16_t *wb = Ws + cur * BN * kBK;
-        // fragments of K slice kk+1 are read while slice kk multiplies
-        bf16x8 a[2][T::TM], b[2][T::TN];
 #pragma unroll
-        for (int i = 0; i < T::TM; ++i) a[0][i] = *(const bf16x8 *)(xb + lds_off(wm * T::WM + i * 32 + fr, fk));
-#pragma unroll
-        for (int j = 0; j < T::TN; ++j) b[0][j] = *(const bf16x8 *)(wb + lds_off(wn * T::WN + j * 32 + fr, fk));
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int c = kk & 1, n = c ^ 1;
-            if (kk + 1 < kBK / 16) {
-#pragma unroll
-                for (int i = 0; i < T::TM; ++i)
-                    a[n][i] = *(const bf16x8 *)(xb + lds_off(wm * T::WM + i * 32 + fr, (kk + 1) * 2 + fk));
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    b[n][j] = *(const bf16x8 *)(wb + lds_off(wn * T::WN + j * 32 + fr, (kk + 1) * 2 + fk));
+        for (int s = 0; s < KS; ++s) {
+            const int c = s & 1, n = c ^ 1;
+            if (s + 1 < KS) {
+                DSEL_FRAG(n, xb, wb, s + 1);
+            } else {
+                wait_vmcnt_lgkm0<PER>();  // own reads of this stage done, own DMA of kt+1 landed
+                wg_barrier();             // everyone's: the stage is free, step kt+1 is complete
+                DSEL_ISSUE(kt + 3, cur);
+                DSEL_FRAG(n, Xs + nxt * BM * kBK, Ws + nxt * BN * kBK, 0);
             }
 #pragma unroll
             for (int i = 0; i < T::TM; ++i)
@@ -143,10 +175,33 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
                 for (int j = 0; j < T::TN; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
         }
-        cur = cur == NS - 1 ? 0 : cur + 1;
+        cur = nxt;
     }
     wait_vmcnt<0>();  // drain the redundant tail loads before LDS is released
 #undef DSEL_ISSUE
+#undef DSEL_FRAG
+}
+
+// Valid-row mask of a BM-row tile, shared through LDS.  Rows are loaded by
+// lanes with lane % 8 == 0 of wave w as rows 8 (w + NW u) + lane / 8, u < XI;
+// bit u of `xok` says the row's source was valid.  Each (wave, u) pair owns one
+// byte of the mask, so word q of `lds` (read as uint32) afterwards holds rows
+// 32 q .. 32 q + 31.  Call after the main loop: LDS is reused, and the leading
+// barrier also retires every wave's last LDS-DMA.
+template <int NW, int XI>
+__device__ __forceinline__ void tile_row_mask(uint32_t xok, uint16_t *lds) {
+    uint8_t *bytes = (uint8_t *)lds;
+    const int wave = threadIdx.x >> 6;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+        const uint64_t b = ballot(((xok >> u) & 1u) != 0);
+        uint32_t byte = 0;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) byte |= (uint32_t)((b >> (8 * k)) & 1u) << k;
+        if (lane_id() == 0) bytes[wave + NW * u] = (uint8_t)byte;
+    }
+    __syncthreads();
 }
 
 struct CandParams {
@@ -162,13 +217,18 @@ struct CandParams {
     float *A_prev, *B_cur;
 };
 
-// Column tile BN of one side on 4 waves: 2 x 2 (wave tile 64 x BN/2), or 4 x 1
-// when BN = 32.
+// Column tile BN of one side: BN = 256 on 8 waves (2 x 4, wave tile 64 x 64:
+// two waves per SIMD hide each other's LDS latency), BN = 128 and 64 on 4 waves
+// (2 x 2), BN = 32 on 4 waves (4 x 1).
 #ifndef DSEL_CAND_GN256
 #define DSEL_CAND_GN256 4
 #endif
 template <int BN>
 using CandTile = TileShape<128, BN, (BN == 32 ? 4 : 2), (BN == 32 ? 1 : BN == 256 ? DSEL_CAND_GN256 : 2)>;
+inline int tile_threads(int BN) {
+    return BN == 256 ? CandTile<256>::NT : BN == 128 ? CandTile<128>::NT : BN == 64 ? CandTile<64>::NT
+                                                                                 : CandTile<32>::NT;
+}
 
 template <int BN>
 __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandParams p) {
@@ -213,7 +273,7 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
                 atomicOr(&g_device_error, 1);
             }
         }
-        xsrc[u] = p.E + tok * d + (((lane & 7) ^ (row & 7)) << 3);
+        xsrc[u] = p.E + tok * d + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
     }
     const uint16_t *W = (side == 0 ? p.WA : p.WB) + (int64_t)n0 * d;
 
@@ -226,39 +286,41 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     mma_tile_dma<T>(xsrc, W, d, 0, d / kBK, Xs, Ws, acc);
 
-    // Row validity for the epilogue, through LDS (a global re-load per row
-    // would put one memory round trip per output row on the critical path).
-    __syncthreads();
-    uint8_t *rowok = (uint8_t *)Xs;
-    if ((lane & 7) == 0) {
-#pragma unroll
-        for (int u = 0; u < XI; ++u) rowok[8 * (wave + NW * u) + (lane >> 3)] = (xok >> u) & 1u;
-    }
-    __syncthreads();
-
-    // acc[i][j][e] = C[row, col]: row = wm*WM + 32 i + 8 (e / 4) + 4 (lane / 32)
-    // + e % 4, col = wn*WN + 32 j + lane % 32.
+    // Epilogue.  Row validity comes from the tile's mask; "position t is the
+    // last of its block" from an 8-bit mask of the tile's 8 positions.
+    tile_row_mask<NW, XI>(xok, Xs);
     const int wm = wave / T::GNv, wn = wave % T::GNv;
+    uint32_t okw[T::TM];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) okw[i] = ((const uint32_t *)Xs)[wm * T::TM + i];
+    uint32_t lastq = 0;
+    {
+        const int64_t bt0 = m0 / kK;
+        int pos = (int)(bt0 % p.L);
+#pragma unroll
+        for (int q = 0; q < BM / kK; ++q) {
+            if (pos == p.L - 1) lastq |= 1u << q;
+            pos = pos + 1 == p.L ? 0 : pos + 1;
+        }
+    }
+    // acc[i][j][e] = C[row, col]: row = wm*WM + 32 i + 8 (e / 4) + 4 (lane / 32)
+    // + e % 4, col = wn*WN + 32 j + lane % 32.  Candidate row m = (b t) * 16 + j
+    // of side 0 becomes predecessor row j of position t + 1: output row m + 16.
+    float *const out = side == 0 ? p.A_prev + (int64_t)kK * r : p.B_cur;
+    const int col = n0 + wn * T::WN + (int)(lane & 31);
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int rl = wm * T::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int rw = 8 * (v >> 2) + 4 * (int)(lane >> 5) + (v & 3);  // row within the 32-row block
+            const int rl = wm * T::WM + i * 32 + rw;
             const int64_t m = m0 + rl;
             if (m >= p.M) continue;
-            const bool ok = rowok[rl] != 0;
-            const int64_t bt = m / kK;
-            const int slotj = (int)(m % kK);
-            float *dst;
-            if (side == 0) {
-                if ((bt % p.L) + 1 >= p.L) continue;  // the last position has no successor
-                dst = p.A_prev + ((bt + 1) * kK + slotj) * r;
-            } else {
-                dst = p.B_cur + (bt * kK + slotj) * r;
-            }
+            if (side == 0 && ((lastq >> (rl >> 4)) & 1u)) continue;  // no successor position
+            const bool ok = (okw[i] >> rw) & 1u;
+            float *dst = out + m * r + col;
 #pragma unroll
-            for (int j = 0; j < T::TN; ++j)
-                dst[n0 + wn * T::WN + j * 32 + (lane & 31)] = ok ? acc[i][j][v] : 0.0f;
+            for (int j = 0; j < T::TN; ++j) dst[j * 32] = ok ? acc[i][j][v] : 0.0f;
         }
 }
 
@@ -322,7 +384,7 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
                 else if ((lane & 7) == 0 && ks == 0 && n0 == 0) atomicOr(&g_device_error, 1);
             }
         }
-        xsrc[u] = base + (((lane & 7) ^ (row & 7)) << 3);
+        xsrc[u] = base + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
     }
     const uint16_t *W = (gate ? p.WH : p.WA) + (int64_t)n0 * d;
 
@@ -335,24 +397,21 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     if (k1 > k0) mma_tile_dma<T>(xsrc, W, d, k0, k1, Xs, Ws, acc);
 
-    __syncthreads();
-    uint8_t *rowok = (uint8_t *)Xs;
-    if ((lane & 7) == 0) {
-#pragma unroll
-        for (int u = 0; u < XI; ++u) rowok[8 * (wave + NW * u) + (lane >> 3)] = (xok >> u) & 1u;
-    }
-    __syncthreads();
-
+    tile_row_mask<NW, XI>(xok, Xs);
     const int wm = wave / T::GNv, wn = wave % T::GNv;
+    uint32_t okw[T::TM];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) okw[i] = ((const uint32_t *)Xs)[wm * T::TM + i];
     const int64_t rows_all = (int64_t)p.B * p.L + p.B;
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
-            const int rl = wm * T::WM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int rw = 8 * (v >> 2) + 4 * (int)(lane >> 5) + (v & 3);
+            const int rl = wm * T::WM + i * 32 + rw;
             const int64_t m = m0 + rl;
             if (m >= M) continue;
-            const bool ok = rowok[rl] != 0;
+            const bool ok = (okw[i] >> rw) & 1u;
 #pragma unroll
             for (int j = 0; j < T::TN; ++j) {
                 const int n = n0 + wn * T::WN + j * 32 + (int)(lane & 31);
