@@ -58,6 +58,16 @@ __device__ __forceinline__ uint64_t cand_key(float v, uint32_t id) {
 
 __device__ __forceinline__ uint32_t key_id(uint64_t k) { return ~(uint32_t)k; }
 
+// The value a key was made from, when its order bits identify it exactly:
+// false for the two codes that merge several inputs (every NaN, and +0.0 with
+// -0.0), whose bits must be read back from the input.
+__device__ __forceinline__ bool key_value(uint64_t k, float *v) {
+    const uint32_t hi = (uint32_t)(k >> 32);
+    if (hi == 0u || hi == 0x80000000u) return false;
+    *v = __uint_as_float((hi & 0x80000000u) ? (hi & 0x7FFFFFFFu) : ~hi);
+    return true;
+}
+
 // The float a key's value part stands for, used as the fast filter threshold:
 // empty or NaN-level keys give -inf so that every element (NaN included, since
 // !(NaN < -inf) holds) goes on to the exact key compare.

@@ -10,11 +10,16 @@
 // value of its 16th key: almost every element fails that single compare, and
 // the rare survivors are inserted one at a time with a cross-lane shift.  The
 // first 64 x U elements of a wave seed the list with the sorted lane maxima
-// (the 16 best of them bound the rest).  Waves merge through LDS with a 64-key
+// (the 16 best of them bound the rest).  Loads are double-buffered in
+// registers, so a chunk's HBM latency hides behind the previous chunk's filter.  Waves merge through LDS with a 64-key
 // bitonic sort; split rows merge in a second, one-wave-per-row kernel.
 #pragma once
 
 #include "common.h"
+
+#ifndef DSEL_TOPK_INTERLEAVE
+#define DSEL_TOPK_INTERLEAVE 1
+#endif
 
 namespace dsel {
 
@@ -83,62 +88,105 @@ struct WaveTop {
     }
 };
 
-template <bool BF16, int U, bool CHECK, bool FIRST>
-__device__ __forceinline__ void topk_chunk(WaveTop &st, const u32x4 *vbase, int64_t v0, int64_t ve,
-                                           int64_t h0) {
-    constexpr int EPV = BF16 ? 8 : 4;
+// One chunk = U vectors of 16 bytes per lane (U x 64 vectors per wave), at
+// vector index v0 + u * 64 + lane.  Loads are always issued (indices past the
+// wave's range `ve` are clamped to its last vector and flagged in `ok`) so the
+// compiler's wait counts never depend on a branch, and the next chunk's loads
+// can be in flight while this one is filtered.
+template <int U>
+__device__ __forceinline__ void load_chunk(u32x4 (&w)[U], const u32x4 *vbase, int64_t v0, int64_t ve) {
     const uint32_t lane = lane_id();
-    u32x4 w[U];
-    bool ok[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         int64_t vi = v0 + u * kWave + lane;
-        ok[u] = !CHECK || vi < ve;
-        if (ok[u]) w[u] = __builtin_nontemporal_load(vbase + vi);
-        else w[u] = u32x4{0u, 0u, 0u, 0u};
+        vi = vi < ve ? vi : ve - 1;
+        w[u] = __builtin_nontemporal_load(vbase + vi);
     }
-    int skip = -1;
-    if constexpr (FIRST) {
-        // Seed: the 16 best lane maxima are real elements, so they bound the
-        // rest; each lane's maximum is then not offered again.
-        uint64_t best = 0;
+}
+
+// Largest element of the lane's chunk (invalid vectors excluded), as a float.
+// v_max ignores NaN, so a NaN-only chunk gives NaN, which passes the
+// `!(max < thr)` screen like NaN itself would.
+template <bool BF16, int U>
+__device__ __forceinline__ float chunk_max(const u32x4 (&w)[U], int64_t v0, int64_t ve) {
+    const uint32_t lane = lane_id();
+    float m = -__builtin_inff();
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                uint64_t k = cand_key(vec_elem<BF16>(w[u], e),
-                                      (uint32_t)(h0 + (v0 + u * kWave + lane) * EPV + e));
-                if (ok[u] && k > best) {
-                    best = k;
-                    skip = u * EPV + e;
-                }
-            }
-        uint64_t srt = wave_sort64_desc(best);
-        st.key = lane < (uint32_t)kK ? srt : 0ull;
-        st.refresh();
-    }
-    bool any = false;
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int e = 0; e < EPV; ++e) {
-            bool p = !(vec_elem<BF16>(w[u], e) < st.thr_f);
-            if (CHECK) p = p && ok[u];
-            if (FIRST) p = p && (u * EPV + e != skip);
-            any |= p;
+    for (int u = 0; u < U; ++u) {
+        const bool ok = v0 + u * kWave + lane < ve;
+        float mu;
+        if constexpr (BF16) {
+            const float a0 = __uint_as_float(w[u].x << 16), a1 = __uint_as_float(w[u].x & 0xFFFF0000u);
+            const float b0 = __uint_as_float(w[u].y << 16), b1 = __uint_as_float(w[u].y & 0xFFFF0000u);
+            const float c0 = __uint_as_float(w[u].z << 16), c1 = __uint_as_float(w[u].z & 0xFFFF0000u);
+            const float d0 = __uint_as_float(w[u].w << 16), d1 = __uint_as_float(w[u].w & 0xFFFF0000u);
+            mu = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(a0, a1), __builtin_fmaxf(b0, b1)),
+                                 __builtin_fmaxf(__builtin_fmaxf(c0, c1), __builtin_fmaxf(d0, d1)));
+        } else {
+            mu = __builtin_fmaxf(__builtin_fmaxf(__uint_as_float(w[u].x), __uint_as_float(w[u].y)),
+                                 __builtin_fmaxf(__uint_as_float(w[u].z), __uint_as_float(w[u].w)));
         }
-    if (ballot(any) == 0) return;
+        m = ok ? __builtin_fmaxf(m, mu) : m;
+    }
+    return m;
+}
+
+// Offer every element of the chunk that passes the threshold (exact path).
+// `skip` (first chunk only) is the element the seed already holds.
+template <bool BF16, int U>
+__device__ __forceinline__ void chunk_offer(WaveTop &st, const u32x4 (&w)[U], int64_t v0, int64_t ve,
+                                            int64_t h0, int skip) {
+    constexpr int EPV = BF16 ? 8 : 4;
+    const uint32_t lane = lane_id();
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+        const bool ok = v0 + u * kWave + lane < ve;
 #pragma unroll
         for (int e = 0; e < EPV; ++e) {
-            float x = vec_elem<BF16>(w[u], e);
-            bool p = !(x < st.thr_f);
-            if (CHECK) p = p && ok[u];
-            if (FIRST) p = p && (u * EPV + e != skip);
+            const float x = vec_elem<BF16>(w[u], e);
+            const bool p = ok && !(x < st.thr_f) && (u * EPV + e != skip);
             const int64_t vrow = v0 + u * kWave;
             st.offer(x, p, [&](uint32_t src) { return (uint32_t)(h0 + (vrow + src) * EPV + e); });
         }
+    }
+}
+
+// Filter one chunk: a single compare of the lane's chunk maximum screens out
+// (almost) every chunk once the list has filled.
+template <bool BF16, int U>
+__device__ __forceinline__ void chunk_filter(WaveTop &st, const u32x4 (&w)[U], int64_t v0, int64_t ve,
+                                             int64_t h0) {
+    const float m = chunk_max<BF16, U>(w, v0, ve);
+    if (ballot(!(m < st.thr_f)) == 0) return;
+    chunk_offer<BF16, U>(st, w, v0, ve, h0, -1);
+}
+
+// First chunk of a wave: seed the list with the 16 best lane maxima (real
+// elements, so they bound the rest), then offer the remaining elements.
+template <bool BF16, int U>
+__device__ __forceinline__ void chunk_seed(WaveTop &st, const u32x4 (&w)[U], int64_t v0, int64_t ve,
+                                           int64_t h0) {
+    constexpr int EPV = BF16 ? 8 : 4;
+    const uint32_t lane = lane_id();
+    uint64_t best = 0;
+    int skip = -1;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool ok = v0 + u * kWave + lane < ve;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+            const uint64_t k = cand_key(vec_elem<BF16>(w[u], e),
+                                        (uint32_t)(h0 + (v0 + u * kWave + lane) * EPV + e));
+            if (ok && k > best) {
+                best = k;
+                skip = u * EPV + e;
+            }
+        }
+    }
+    const uint64_t srt = wave_sort64_desc(best);
+    st.key = lane < (uint32_t)kK ? srt : 0ull;
+    st.refresh();
+    chunk_offer<BF16, U>(st, w, v0, ve, h0, skip);
 }
 
 template <bool BF16, int U>
@@ -159,23 +207,47 @@ __global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
     const int64_t tail0 = h0 + nvec * EPV;
     const u32x4 *vbase = (const u32x4 *)(rowp + h0 * ES);
 
+#if DSEL_TOPK_INTERLEAVE
+    // The workgroup owns vectors [wb, we) of the row; its waves take turns
+    // chunk by chunk, so the four waves sweep one contiguous stretch together.
+    const int64_t wb = nvec * split / p.nsplit, we = nvec * (split + 1) / p.nsplit;
+    const int64_t gw = (int64_t)split * 4 + wave;
+#else
     const int64_t nw = (int64_t)p.nsplit * 4;
     const int64_t gw = (int64_t)split * 4 + wave;
     const int64_t vb = nvec * gw / nw, ve = nvec * (gw + 1) / nw;
+#endif
 
     WaveTop st;
     st.key = 0ull;
     st.thr = 0ull;
     st.thr_f = -__builtin_inff();
 
+    // Stream the wave's range chunk by chunk, the next chunk's loads always in
+    // flight while the current one is filtered (two register buffers).
     constexpr int STEP = U * kWave;
-    int64_t v0 = vb;
-    if (v0 < ve) {
-        if (v0 + STEP <= ve) topk_chunk<BF16, U, false, true>(st, vbase, v0, ve, h0);
-        else topk_chunk<BF16, U, true, true>(st, vbase, v0, ve, h0);
-        v0 += STEP;
-        for (; v0 + STEP <= ve; v0 += STEP) topk_chunk<BF16, U, false, false>(st, vbase, v0, ve, h0);
-        if (v0 < ve) topk_chunk<BF16, U, true, false>(st, vbase, v0, ve, h0);
+#if DSEL_TOPK_INTERLEAVE
+    constexpr int64_t CS = 4 * STEP;  // distance between a wave's chunks
+    const int64_t vb = wb + wave * STEP, ve = we;
+    if (vb < ve) {
+        const int64_t nch = (ve - vb + CS - 1) / CS;
+#else
+    constexpr int64_t CS = STEP;
+    if (vb < ve) {
+        const int64_t nch = (ve - vb + CS - 1) / CS;
+#endif
+        u32x4 wa[U], wb2[U];
+        load_chunk<U>(wa, vbase, vb, ve);
+        load_chunk<U>(wb2, vbase, vb + CS, ve);
+        chunk_seed<BF16, U>(st, wa, vb, ve, h0);
+        for (int64_t c = 1; c < nch; c += 2) {
+            const int64_t v0 = vb + c * CS;
+            load_chunk<U>(wa, vbase, v0 + CS, ve);
+            chunk_filter<BF16, U>(st, wb2, v0, ve, h0);
+            if (c + 1 >= nch) break;
+            load_chunk<U>(wb2, vbase, v0 + 2 * CS, ve);
+            chunk_filter<BF16, U>(st, wa, v0 + CS, ve, h0);
+        }
     }
     if (gw == 0) {  // head and tail elements outside the whole vectors
         int64_t idx = -1;
@@ -197,7 +269,9 @@ __global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
             if (p.nsplit == 1) {
                 uint32_t id = key_id(srt);  // always < V: every row has >= 16 real keys
                 p.cand_id[row * kK + lane] = (int32_t)id;
-                p.cand_u[row * kK + lane] = (int64_t)id < p.V ? load_elem<BF16>(rowp, id) : __builtin_nanf("");
+                float u;  // the logit, from the key (no memory round trip) unless it is 0 or NaN
+                if (!key_value(srt, &u)) u = (int64_t)id < p.V ? load_elem<BF16>(rowp, id) : __builtin_nanf("");
+                p.cand_u[row * kK + lane] = u;
             } else {
                 p.partial[(row * p.nsplit + split) * kK + lane] = srt;
             }
@@ -226,7 +300,9 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(TopkParams p) {
         const char *rowp = p.logits + row * p.ld * ES;
         uint32_t id = key_id(best);
         p.cand_id[row * kK + lane] = (int32_t)id;
-        p.cand_u[row * kK + lane] = (int64_t)id < p.V ? load_elem<BF16>(rowp, id) : __builtin_nanf("");
+        float u;
+        if (!key_value(best, &u)) u = (int64_t)id < p.V ? load_elem<BF16>(rowp, id) : __builtin_nanf("");
+        p.cand_u[row * kK + lane] = u;
     }
 }
 
