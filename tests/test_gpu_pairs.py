@@ -34,7 +34,8 @@ def _dev(*arrs, dev):
 
 
 @pytest.mark.parametrize("B,L,r", [(1, 1, 32), (3, 3, 32), (5, 8, 64), (4, 16, 256), (2, 17, 128),
-                                   (2, 32, 256), (37, 16, 256)])
+                                   (2, 32, 256), (37, 16, 256), (3, 5, 96), (2, 9, 160),
+                                   (7, 12, 224), (1, 32, 192)])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_pairs_and_fused_walk(ora, dev, B, L, r, mode):
     cand_u, A, Bm, G, cand_id, u = _inputs(B * 100 + L + r, B, L, r)

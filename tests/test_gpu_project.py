@@ -83,6 +83,11 @@ def _rand_inputs(seed, B, L, V, d, r, e_std=1.0):
     (2, 16, 3000, 192, 64),
     (5, 8, 4000, 256, 128),   # big-tile path
     (9, 7, 20000, 320, 256),  # big-tile path, ragged M, several K steps
+    (2, 3, 700, 448, 96),     # r = 96: three 32-column tiles, 7 K steps
+    (4, 32, 5000, 256, 160),  # longest block, five 32-column tiles
+    (6, 1, 1000, 512, 192),   # one position per block, three 64-column tiles
+    (40, 16, 30000, 128, 256),  # 80 row tiles, gate split along K
+    (70, 9, 9000, 640, 224),  # 79 row tiles (not a multiple of the 8 XCDs), 7 column tiles
 ])
 def test_project_matches_oracle(ora, dev, B, L, V, d, r):
     inp, cand = _rand_inputs(B * 1000 + L, B, L, V, d, r)
