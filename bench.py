@@ -249,7 +249,7 @@ def main():
         if args.gate == "overlap":
             strm.wait_event(fork[1])
         s2 = lib.dsel_project_cand(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_B"]), cfg.r, P(cand_id),
-                                   B, L, P(A_prev), P(B_cur), sp)
+                                   B, L, P(A_prev), P(B_cur), P(pws), pwsb, sp)
         if ev is not None:
             ev[3].record(strm)
         s3 = lib.dsel_score_pairs(P(cand_u), P(A_prev), P(B_cur), P(G), B, L, cfg.r, P(S),

@@ -62,7 +62,7 @@ def _load():
             "dsel_project": ([P, I64, I64, P, P, P, I64, P, P, P, I64, I64, P, P, P, P, SZ, P], I32),
             "dsel_project_workspace_bytes": ([I64, I64, I64, I64], SZ),
             "dsel_project_gate": ([P, I64, I64, P, P, I64, P, P, I64, I64, P, P, P, SZ, P], I32),
-            "dsel_project_cand": ([P, I64, I64, P, P, I64, P, I64, I64, P, P, P], I32),
+            "dsel_project_cand": ([P, I64, I64, P, P, I64, P, I64, I64, P, P, P, SZ, P], I32),
             "dsel_score_pairs": ([P, P, P, P, I64, I64, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_walk": ([P, I64, I64, C.POINTER(WalkArgs), P], I32),
             "dsel_device_error": ([C.POINTER(C.c_int32), P], I32),
@@ -210,7 +210,7 @@ def project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=None, stream=Non
     _check(st, "dsel_project_gate")
 
 
-def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, stream=None):
+def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=None, stream=None):
     """B_cur and the predecessor rows of A_prev for positions >= 1."""
     V, d = E.shape
     r = W_A.shape[0]
@@ -220,8 +220,11 @@ def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, stream=None):
     _need(cand_id, "cand_id", torch.int32, (B, L, K))
     _need(A_prev, "A_prev", torch.float32, (B, L, K, r))
     _need(B_cur, "B_cur", torch.float32, (B, L, K, r))
+    if workspace is None:
+        workspace = _project_workspace(B, L, d, r, E.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _load().dsel_project_cand(_ptr(E), V, d, _ptr(W_A), _ptr(W_B), r, _ptr(cand_id), B, L,
-                                   _ptr(A_prev), _ptr(B_cur), _stream(stream))
+                                   _ptr(A_prev), _ptr(B_cur), _ptr(workspace), wsb, _stream(stream))
     _check(st, "dsel_project_cand")
 
 
@@ -316,16 +319,17 @@ def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
     A_prev = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
     B_cur = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
     G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
+    ws = _project_workspace(B, L, E.shape[1], r, dev)  # one workspace serves both halves
     if overlap:
         side = side_stream(dev)
         side.wait_stream(main)
-        project_gate(E, W_A, W_H, h, verified, A_prev, G, stream=side)
+        project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=ws, stream=side)
         cand_id, cand_u = select_topk(logits, vocab, stream=main)
         main.wait_stream(side)
     else:
-        project_gate(E, W_A, W_H, h, verified, A_prev, G, stream=main)
+        project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=ws, stream=main)
         cand_id, cand_u = select_topk(logits, vocab, stream=main)
-    project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, stream=main)
+    project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=ws, stream=main)
     res = score_pairs(cand_u, A_prev, B_cur, G, want_S=want_S, walk_mode=mode, cand_id=cand_id,
                       temperature=temperature, uniforms=uniforms, want_q=want_q, stream=main)
     res.update(cand_id=cand_id, cand_u=cand_u, A_prev=A_prev, B_cur=B_cur, G=G)

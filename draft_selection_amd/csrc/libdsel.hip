@@ -109,12 +109,20 @@ dsel_status check_project_common(const uint16_t *E, int64_t vocab, int64_t d, in
     return DSEL_OK;
 }
 
+// Workspace layout shared by dsel_project, dsel_project_gate and
+// dsel_project_cand: the gate's partial tiles first, then (256-byte aligned)
+// the candidate job's, so the two halves never touch each other's part.
+size_t cand_workspace_offset(int64_t batch, int64_t block, int64_t d, int64_t r) {
+    return (gate_workspace_bytes(batch, block, d, r) + 255) / 256 * 256;
+}
+
 }  // namespace
 
 DSEL_API size_t dsel_project_workspace_bytes(int64_t batch, int64_t block, int64_t d, int64_t r) {
     if (batch <= 0 || block < 1 || d < 64 || d % 64 != 0 || r < 32 || r > DSEL_MAX_RANK || r % 32 != 0)
         return 0;
-    return gate_workspace_bytes(batch, block, d, r);
+    const size_t c = cand_workspace_bytes(batch, block, d, r);
+    return c ? cand_workspace_offset(batch, block, d, r) + c : gate_workspace_bytes(batch, block, d, r);
 }
 
 DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d,
@@ -167,13 +175,18 @@ DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t
 DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d,
                                        const uint16_t *W_A, const uint16_t *W_B, int64_t r,
                                        const int32_t *cand_id, int64_t batch, int64_t block,
-                                       float *A_prev, float *B_cur, dsel_stream_t stream) {
+                                       float *A_prev, float *B_cur, void *workspace,
+                                       size_t workspace_bytes, dsel_stream_t stream) {
     dsel_status st = check_project_common(E, vocab, d, r, batch, block);
     if (st != DSEL_OK || batch == 0) return st;
     if (!W_A || !W_B || !cand_id || !A_prev || !B_cur) return DSEL_E_ARG;
     if (!aligned(W_A, 16) || !aligned(W_B, 16) || !aligned(cand_id, 4) || !aligned(A_prev, 4) ||
         !aligned(B_cur, 4))
         return DSEL_E_ALIGN;
+    const size_t cneed = cand_workspace_bytes(batch, block, d, r);
+    const size_t coff = cand_workspace_offset(batch, block, d, r);
+    if (cneed && (!workspace || workspace_bytes < coff + cneed)) return DSEL_E_WORKSPACE;
+    if (cneed && !aligned(workspace, 16)) return DSEL_E_ALIGN;
     CandParams p;
     p.E = E;
     p.V = vocab;
@@ -191,14 +204,23 @@ DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t
     p.nside = (int)(r / BN);
     p.mt = (int)((p.M + BM - 1) / BM);
     p.mt_pad = (p.mt + 7) / 8 * 8;
-    const int64_t grid = (int64_t)p.mt_pad * 2 * p.nside;
-    if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
+    p.nsplit = cand_nsplit(batch, block, d, r);
+    p.part = cneed ? (float *)((char *)workspace + coff) : nullptr;
+    const int64_t grid = (int64_t)p.mt_pad * 2 * p.nside * p.nsplit;
+    if (grid >= (int64_t)INT_MAX || p.M * 2 * r >= (int64_t)INT_MAX * 256) return DSEL_E_ARG;
     const void *k = BN == 256 ? (const void *)project_cand_kernel<256>
                   : BN == 128 ? (const void *)project_cand_kernel<128>
                   : BN == 64  ? (const void *)project_cand_kernel<64>
                               : (const void *)project_cand_kernel<32>;
     const int nt = tile_threads(BN);
-    return launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
+    st = launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
+    if (st != DSEL_OK || p.nsplit == 1) return st;
+    const int64_t elems = p.M * 2 * r;
+    const void *kr = BN == 256 ? (const void *)project_cand_reduce_kernel<256>
+                   : BN == 128 ? (const void *)project_cand_reduce_kernel<128>
+                   : BN == 64  ? (const void *)project_cand_reduce_kernel<64>
+                               : (const void *)project_cand_reduce_kernel<32>;
+    return launch(kr, dim3((unsigned)((elems + 255) / 256)), dim3(256), &p, 0, stream);
 }
 
 DSEL_API dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
@@ -211,12 +233,13 @@ DSEL_API dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, c
     if (st != DSEL_OK || batch == 0) return st;
     if (!W_A || !W_B || !W_H || !h || !cand_id || !verified || !A_prev || !B_cur || !G)
         return DSEL_E_ARG;
-    const size_t need = gate_workspace_bytes(batch, block, d, r);
+    const size_t need = dsel_project_workspace_bytes(batch, block, d, r);
     if (need && (!workspace || workspace_bytes < need)) return DSEL_E_WORKSPACE;
     st = dsel_project_gate(E, vocab, d, W_A, W_H, r, h, verified, batch, block, A_prev, G, workspace,
                            workspace_bytes, stream);
     if (st != DSEL_OK) return st;
-    return dsel_project_cand(E, vocab, d, W_A, W_B, r, cand_id, batch, block, A_prev, B_cur, stream);
+    return dsel_project_cand(E, vocab, d, W_A, W_B, r, cand_id, batch, block, A_prev, B_cur, workspace,
+                             workspace_bytes, stream);
 }
 
 namespace {

@@ -214,6 +214,8 @@ struct CandParams {
     int64_t M;        // batch * block * 16 gathered rows
     int mt, mt_pad;   // row tiles (mt_pad: rounded up to a multiple of 8)
     int nside;        // column tiles per side (r / BN)
+    int nsplit;       // K splits (small batches); > 1: partial tiles go to `part`
+    float *part;      // [nsplit][mt * 2 * nside][128][BN] partial tiles
     float *A_prev, *B_cur;
 };
 
@@ -240,10 +242,13 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
     __shared__ __attribute__((aligned(16))) uint16_t Ws[3 * BN * kBK];
 
     // XCD-aware tile order: workgroups w and w + 8 share an XCD; consecutive
-    // slots of one XCD take the column tiles of one row tile.
-    const int w = blockIdx.x;
-    const int xcd = w & 7, slot = w >> 3;
+    // slots of one XCD take the column tiles of one row tile.  With K splits
+    // the grid repeats that order once per split.
     const int ncol = 2 * p.nside;
+    const int per_split = p.mt_pad * ncol;
+    const int ks = (int)(blockIdx.x / per_split);
+    const int w = (int)(blockIdx.x % per_split);
+    const int xcd = w & 7, slot = w >> 3;
     const int ct = slot % ncol;
     const int mt = (slot / ncol) * 8 + xcd;
     if (mt >= p.mt) return;
@@ -284,7 +289,25 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    mma_tile_dma<T>(xsrc, W, d, 0, d / kBK, Xs, Ws, acc);
+    const int nk = d / kBK;
+    const int k0 = (int)((int64_t)nk * ks / p.nsplit), k1 = (int)((int64_t)nk * (ks + 1) / p.nsplit);
+    if (k1 > k0) mma_tile_dma<T>(xsrc, W, d, k0, k1, Xs, Ws, acc);
+
+    if (p.nsplit > 1) {
+        // partial tile, row-major; validity and placement are the reduce's
+        const int wm = wave / T::GNv, wn = wave % T::GNv;
+        float *tp = p.part + ((int64_t)ks * p.mt * ncol + (int64_t)mt * ncol + ct) * (BM * BN);
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int rl = wm * T::WM + i * 32 + 8 * (v >> 2) + 4 * (int)(lane >> 5) + (v & 3);
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    tp[rl * BN + wn * T::WN + j * 32 + (int)(lane & 31)] = acc[i][j][v];
+            }
+        return;
+    }
 
     // Epilogue.  Row validity comes from the tile's mask; "position t is the
     // last of its block" from an 8-bit mask of the tile's 8 positions.
@@ -322,6 +345,55 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
 #pragma unroll
             for (int j = 0; j < T::TN; ++j) dst[j * 32] = ok ? acc[i][j][v] : 0.0f;
         }
+}
+
+// Sum the K splits of the candidate job in split order, then the epilogue of
+// project_cand_kernel: one thread per output element (row m, side, column n).
+template <int BN>
+__global__ __launch_bounds__(256) void project_cand_reduce_kernel(CandParams p) {
+    constexpr int BM = 128;
+    const int r = p.r;
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= p.M * 2 * r) return;
+    const int n = (int)(e % r);
+    const int side = (int)((e / r) & 1);
+    const int64_t m = e / (2 * r);
+    const int ncol = 2 * p.nside;
+    const int mt = (int)(m / BM), rl = (int)(m % BM);
+    const int ct = side * p.nside + n / BN;
+    const int64_t stride = (int64_t)p.mt * ncol * BM * BN;
+    const float *src = p.part + ((int64_t)mt * ncol + ct) * (BM * BN) + rl * BN + (n % BN);
+    float sum = 0.0f;
+    for (int ks = 0; ks < p.nsplit; ++ks) sum += src[ks * stride];
+    const int32_t t = p.cand[m];
+    const bool ok = t >= 0 && (int64_t)t < p.V;
+    if (side == 0) {
+        if ((m / kK) % p.L == p.L - 1) return;  // the last position has no successor
+        p.A_prev[(m + kK) * r + n] = ok ? sum : 0.0f;
+    } else {
+        p.B_cur[m * r + n] = ok ? sum : 0.0f;
+    }
+}
+
+// K splits of the candidate job: only when its tiles cannot fill the chip,
+// keeping at least DSEL_CAND_MIN_STEPS K steps per split.
+#ifndef DSEL_CAND_MIN_STEPS
+#define DSEL_CAND_MIN_STEPS 4
+#endif
+inline int cand_nsplit(int64_t batch, int64_t block, int64_t d, int64_t r) {
+    const int64_t BN = r % 256 == 0 ? 256 : r % 128 == 0 ? 128 : r % 64 == 0 ? 64 : 32;
+    const int64_t tiles = (batch * block * kK + 127) / 128 * 2 * (r / BN);
+    if (tiles >= 128) return 1;
+    const int64_t nk = d / kBK;
+    int64_t s = 256 / (tiles > 0 ? tiles : 1);
+    if (s > nk / DSEL_CAND_MIN_STEPS) s = nk / DSEL_CAND_MIN_STEPS;
+    return (int)(s < 1 ? 1 : s);
+}
+
+inline size_t cand_workspace_bytes(int64_t batch, int64_t block, int64_t d, int64_t r) {
+    const int s = cand_nsplit(batch, block, d, r);
+    const int64_t mt = (batch * block * kK + 127) / 128;
+    return s > 1 ? (size_t)s * (size_t)mt * 128 * 2 * (size_t)r * sizeof(float) : 0;
 }
 
 struct GateParams {

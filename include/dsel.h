@@ -112,17 +112,20 @@ dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, const uint
                          int64_t block, float *A_prev, float *B_cur, float *G, void *workspace,
                          size_t workspace_bytes, dsel_stream_t stream);
 
-/* Bytes of device workspace dsel_project / dsel_project_gate need (0 when none;
- * also 0 for invalid arguments, which the calls themselves reject). */
+/* Bytes of device workspace dsel_project needs (0 when none; also 0 for
+ * invalid arguments, which the calls themselves reject).  Small GEMMs are split
+ * along d across workgroups and their partial sums kept here. */
 size_t dsel_project_workspace_bytes(int64_t batch, int64_t block, int64_t d, int64_t r);
 
 /* The two halves of dsel_project, for callers that schedule them apart:
  * project_gate needs no candidates (G and position 0's predecessor rows of
  * A_prev), so it may run while dsel_select_topk is still running, e.g. on a
  * second stream; project_cand computes B_cur and A_prev of positions >= 1 from
- * the candidates and needs no workspace.  Arguments, layouts and requirements
- * as for dsel_project; each writes only the outputs named here (and
- * project_gate its workspace). */
+ * the candidates.  Arguments, layouts and requirements as for dsel_project;
+ * each writes only the outputs named here.  Both take a workspace sized by
+ * dsel_project_workspace_bytes and use disjoint parts of it, so one workspace
+ * can serve both calls, even while they run concurrently on two streams (two
+ * calls of the same half must not share one workspace concurrently). */
 dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
                               const uint16_t *W_H, int64_t r, const uint16_t *h,
                               const int32_t *verified, int64_t batch, int64_t block, float *A_prev,
@@ -131,7 +134,7 @@ dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d, const
 dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
                               const uint16_t *W_B, int64_t r, const int32_t *cand_id,
                               int64_t batch, int64_t block, float *A_prev, float *B_cur,
-                              dsel_stream_t stream);
+                              void *workspace, size_t workspace_bytes, dsel_stream_t stream);
 
 /* Walk arguments ([P1] Method last paragraph, [P3]: the only sequential step;
  * greedy follows the best successor, sampling draws from the same scores).

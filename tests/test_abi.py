@@ -50,10 +50,17 @@ def test_project_workspace_sizing(lib):
     # the gate GEMM of 64 blocks of 16 is split along K across workgroups
     assert lib.dsel_project_workspace_bytes(64, 16, 2560, 256) > 0
     assert lib.dsel_project_workspace_bytes(64, 16, 96, 256) == 0  # d % 64 != 0: invalid
+    # one block: the candidate GEMM is split too, so the workspace grows
+    assert lib.dsel_project_workspace_bytes(1, 16, 2560, 256) > lib.dsel_project_workspace_bytes(64, 16, 2560, 256) / 64
     fake = C.c_void_p(0x100000)
     args = [fake, 151936, 2560, fake, fake, fake, 256, fake, fake, fake, 64, 16, fake, fake, fake,
             None, 0, None]
     assert lib.dsel_project(*args) == -4  # workspace missing
+    # the candidate half of one block needs its part of the workspace
+    cand_args = [fake, 151936, 2560, fake, fake, 256, fake, 1, 16, fake, fake, None, 0, None]
+    assert lib.dsel_project_cand(*cand_args) == -4
+    small = list(cand_args); small[11] = fake; small[12] = 64
+    assert lib.dsel_project_cand(*small) == -4
 
 
 def test_topk_workspace_sizing(lib):

@@ -88,6 +88,8 @@ def _rand_inputs(seed, B, L, V, d, r, e_std=1.0):
     (6, 1, 1000, 512, 192),   # one position per block, three 64-column tiles
     (40, 16, 30000, 128, 256),  # 80 row tiles, gate split along K
     (70, 9, 9000, 640, 224),  # 79 row tiles (not a multiple of the 8 XCDs), 7 column tiles
+    (1, 16, 20000, 2560, 256),  # one block: both GEMMs split along K (10 ways)
+    (2, 8, 5000, 1024, 128),  # candidate GEMM split 4 ways
 ])
 def test_project_matches_oracle(ora, dev, B, L, V, d, r):
     inp, cand = _rand_inputs(B * 1000 + L, B, L, V, d, r)
