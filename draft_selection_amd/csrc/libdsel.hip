@@ -94,7 +94,7 @@ DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t
     if (s != DSEL_OK || ns == 1) return s;
     const void *k2 = dt == DSEL_BF16 ? (const void *)topk16_merge_kernel<true>
                                      : (const void *)topk16_merge_kernel<false>;
-    return launch(k2, dim3((unsigned)rows), dim3(64), &p, 0, stream);
+    return launch(k2, dim3((unsigned)rows), dim3(256), &p, 0, stream);
 }
 
 namespace {

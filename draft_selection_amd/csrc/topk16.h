@@ -279,16 +279,18 @@ __global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
     }
 }
 
-// Merge the nsplit partial lists of a row: one wave per row, 3 lists per step
-// sorted together with the running best 16.
+// Merge the nsplit partial lists of a row: one workgroup (4 waves) per row.
+// Wave w folds lists 3w, 3w+1, 3w+2, then 3w+12, ... into its running best 16
+// (one 64-key sort per 3 lists), and wave 0 sorts the four waves' lists.
 template <bool BF16>
-__global__ __launch_bounds__(64) void topk16_merge_kernel(TopkParams p) {
+__global__ __launch_bounds__(256) void topk16_merge_kernel(TopkParams p) {
     constexpr int ES = BF16 ? 2 : 4;
     const int64_t row = blockIdx.x;
     const uint32_t lane = lane_id();
+    const int wave = (int)(threadIdx.x / kWave);
     const uint64_t *src = p.partial + row * p.nsplit * kK;
     uint64_t best = 0ull;
-    for (int s0 = 0; s0 < p.nsplit; s0 += 3) {
+    for (int s0 = 3 * wave; s0 < p.nsplit; s0 += 12) {
         uint64_t k = best;
         if (lane >= (uint32_t)kK) {
             int s = s0 + (int)(lane - kK) / kK;
@@ -296,6 +298,11 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(TopkParams p) {
         }
         best = wave_sort64_desc(k);
     }
+    __shared__ uint64_t sk[4 * kK];
+    if (lane < (uint32_t)kK) sk[wave * kK + lane] = best;
+    __syncthreads();
+    if (wave != 0) return;
+    best = wave_sort64_desc(sk[lane]);
     if (lane < (uint32_t)kK) {
         const char *rowp = p.logits + row * p.ld * ES;
         uint32_t id = key_id(best);
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(64) void topk16_merge_kernel(TopkParams p) {
 // Workgroups per row: enough rows x splits to fill 256 CUs several times over,
 // but never slices shorter than 4096 elements.
 #ifndef DSEL_TOPK_TARGET_WG
-#define DSEL_TOPK_TARGET_WG 1024
+#define DSEL_TOPK_TARGET_WG 512
 #endif
 inline int topk_nsplit(int64_t rows, int64_t V) {
     if (rows <= 0) return 1;
