@@ -293,7 +293,7 @@ DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, 
     p.S = S;
     p.S_in = S;
     const int64_t positions = batch * block;
-    dsel_status st = launch(pair_kernel_for(r), dim3((unsigned)((positions + 3) / 4)), dim3(256), &p, 0, stream);
+    dsel_status st = launch(pair_kernel_for(r), dim3((unsigned)positions), dim3(256), &p, 0, stream);
     if (st != DSEL_OK || !walk) return st;
     return launch_walk(p, stream);
 }

@@ -6,12 +6,11 @@
 // "Selection beats correction", says the same.)
 //
 // Two kernels:
-//  pair_kernel: one wave per position (b, t), four per workgroup, so the loads
-//     spread over the whole chip.  The 16 x 16 table
-//     P[i][j] = sum_c A_prev[i][c] G[c] B_cur[j][c] is one fp32 MFMA
-//     accumulation (v_mfma_f32_16x16x4_f32, r/4 steps); each lane streams
-//     16-byte slices of its own A and B row, two slices ahead of the MFMAs.
-//     S = U + P (row i >= 1 of position 0 is -inf) is written out.
+//  pair_kernel: one workgroup per position (b, t), its 4 waves sharing the
+//     rank so that enough loads are in flight over the whole chip.  The 16 x 16
+//     table P[i][j] = sum_c A_prev[i][c] G[c] B_cur[j][c] is an fp32 MFMA
+//     accumulation (v_mfma_f32_16x16x4_f32, r/4 steps over the 4 waves, summed
+//     through LDS).  S = U + P (row i >= 1 of position 0 is -inf) is written.
 //  walk_kernel: one workgroup per draft block, wave w loading the score tables
 //     of positions t = w, w + nw, ... (16 KB per block), then:
 //  1. Decisions, in parallel for every predecessor row of every position: the
@@ -134,60 +133,57 @@ __device__ __forceinline__ void decide_position(const float (&s)[4], int t, cons
 }
 
 // Step 1 for one position: the score table in registers (MFMA layout).
+// One position (b, t) per workgroup of 4 waves.  The rank is cut into 16-wide
+// slices, slice s going to wave s % 4; each wave issues every load of its
+// slices up front (so the whole grid keeps enough bytes in flight for HBM) and
+// accumulates its partial 16 x 16 table with v_mfma_f32_16x16x4_f32: lane
+// (fr, fg) supplies row fr and column 4 fg + c of a slice's c-th MFMA (the
+// order of the sum over the rank is a permutation).  The four partial tables
+// are summed through LDS in wave order.
 template <int R>
-__device__ __forceinline__ void score_position(const PairParams &p, int64_t bt, int t, float (&s)[4]) {
+__global__ __launch_bounds__(256) void pair_kernel(PairParams p) {
+    constexpr int NS = R / 16;              // 16-wide slices of the rank (R % 32 == 0)
+    constexpr int SPW = (NS + 3) / 4;       // slices per wave (the last waves may get fewer)
+    const int64_t bt = blockIdx.x;
+    const int t = (int)(bt % p.L);
+    const int wave = (int)(threadIdx.x >> 6);
     const uint32_t lane = lane_id();
     const int fr = lane & 15, fg = lane >> 4;
     const float *Ap = p.A_prev + (bt * kK + fr) * R + 4 * fg;
     const float *Bp = p.B_cur + (bt * kK + fr) * R + 4 * fg;
     const float *Gp = p.G + bt * R + 4 * fg;
+    float4 a[SPW], g[SPW], b[SPW];
+#pragma unroll
+    for (int q = 0; q < SPW; ++q) {
+        const int sl = wave + 4 * q;
+        const int c = (sl < NS ? sl : 0) * 16;  // a wave past the last slice loads slice 0, unused
+        a[q] = *(const float4 *)(Ap + c);
+        g[q] = *(const float4 *)(Gp + c);
+        b[q] = *(const float4 *)(Bp + c);
+    }
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-    constexpr int NS = R / 16;  // 16-wide slices of the rank (even: R % 32 == 0)
-    float4 a[2][2], g[2][2], b[2][2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-        a[0][q] = *(const float4 *)(Ap + 16 * q);
-        g[0][q] = *(const float4 *)(Gp + 16 * q);
-        b[0][q] = *(const float4 *)(Bp + 16 * q);
+    for (int q = 0; q < SPW; ++q) {
+        if (wave + 4 * q >= NS) break;
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q].x * g[q].x, b[q].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q].y * g[q].y, b[q].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q].z * g[q].z, b[q].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q].w * g[q].w, b[q].w, acc, 0, 0, 0);
     }
+    __shared__ floatx4 part[4][kWave];
+    part[wave][lane] = acc;
+    __syncthreads();
+    if (wave != 0) return;
+    floatx4 sum = part[0][lane];
 #pragma unroll
-    for (int s0 = 0; s0 < NS; s0 += 2) {
-        const int cur = (s0 / 2) & 1, nxt = cur ^ 1;
-        if (s0 + 2 < NS) {
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                a[nxt][q] = *(const float4 *)(Ap + 16 * (s0 + 2 + q));
-                g[nxt][q] = *(const float4 *)(Gp + 16 * (s0 + 2 + q));
-                b[nxt][q] = *(const float4 *)(Bp + 16 * (s0 + 2 + q));
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cur][q].x * g[cur][q].x, b[cur][q].x, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cur][q].y * g[cur][q].y, b[cur][q].y, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cur][q].z * g[cur][q].z, b[cur][q].z, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[cur][q].w * g[cur][q].w, b[cur][q].w, acc, 0, 0, 0);
-        }
-    }
+    for (int w = 1; w < 4; ++w) sum += part[w][lane];
+    // acc layout (16x16x4 f32): lane (fr, fg) holds rows i = 4 fg + v, column fr
     const float u = p.cand_u[bt * kK + fr];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
         const int i = 4 * fg + v;
-        s[v] = (t == 0 && i >= 1) ? -__builtin_inff() : u + acc[v];
+        p.S[(bt * kK + i) * kK + fr] = (t == 0 && i >= 1) ? -__builtin_inff() : u + sum[v];
     }
-}
-
-// Scores of one position per wave.
-template <int R>
-__global__ __launch_bounds__(256) void pair_kernel(PairParams p) {
-    const int64_t bt = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (bt >= (int64_t)p.B * p.L) return;
-    const int t = (int)(bt % p.L);
-    const uint32_t lane = lane_id();
-    float s[4];
-    score_position<R>(p, bt, t, s);
-#pragma unroll
-    for (int v = 0; v < 4; ++v) p.S[(bt * kK + 4 * (lane >> 4) + v) * kK + (lane & 15)] = s[v];
 }
 
 // The walk over scores in global memory: one workgroup per block.
