@@ -48,6 +48,8 @@ def _load():
             "ora_step": [P, I32, I32, D, D, P, P, P],
             "ora_walk": [P, P, P, D, I32, I64, I64, P, P, P, P, P],
             "ora_step_table": [P, P, D, I32, I64, I64, P, P],
+            "ora_verify": [P, I32, I64, I64, I64, I64, P, P, P, I32, D, P, P, P, P, P, P],
+            "ora_verify_draw": [P, I32, I64, I64, I64, I64, P, P, I32, D, P, I64, I64, I32, P, P],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -175,3 +177,46 @@ def run(inp: Dict[str, np.ndarray], mode: int = GREEDY, T: float = 1.0, vocab: O
     S = score_pairs(cand_u, A, Bm, G)
     w = walk(S, cand_id, mode, inp.get("uniforms"), T)
     return dict(cand_id=cand_id, cand_u=cand_u, A_prev=A, B_cur=Bm, G=G, S=S, **w)
+
+
+def _tlogits(tlogits, vocab):
+    tl = np.ascontiguousarray(tlogits)
+    dtype = 0 if tl.dtype == np.float32 else 1
+    assert tl.dtype in (np.float32, np.uint16)
+    B, L1, ld = tl.shape
+    return tl, dtype, B, L1 - 1, (ld if vocab is None else int(vocab)), ld
+
+
+def verify(tlogits, cand_id, path_slot, q=None, mode: int = GREEDY, T: float = 1.0, u_acc=None,
+           u_res=None, vocab: Optional[int] = None):
+    """Lossless verification of drafted blocks against target logits
+    ``[B, L+1, ld]`` (see ``ora_verify``).  Returns dict with ``n_acc`` [B],
+    ``out_tok`` [B, L+1] and the margins ``m_acc`` [B, L], ``m_draw`` [B]."""
+    tl, dt, B, L, V, ld = _tlogits(tlogits, vocab)
+    cand_id = np.ascontiguousarray(cand_id, np.int32)
+    path_slot = np.ascontiguousarray(path_slot, np.int32)
+    q = None if q is None else np.ascontiguousarray(q, np.float64)
+    ua = None if u_acc is None else np.ascontiguousarray(u_acc, np.float32)
+    ur = None if u_res is None else np.ascontiguousarray(u_res, np.float32)
+    out = dict(n_acc=np.empty(B, np.int32), out_tok=np.empty((B, L + 1), np.int32),
+               m_acc=np.empty((B, L), np.float64), m_draw=np.empty(B, np.float64))
+    _check(_load().ora_verify(_p(tl), dt, B, L, V, ld, _p(cand_id), _p(path_slot), _p(q), int(mode),
+                              float(T), _p(ua), _p(ur), _p(out["n_acc"]), _p(out["out_tok"]),
+                              _p(out["m_acc"]), _p(out["m_draw"])), "verify")
+    return out
+
+
+def verify_draw(tlogits, b: int, t: int, residual: bool, cand_id=None, q=None, mode: int = SAMPLED,
+                T: float = 1.0, u_res=None, vocab: Optional[int] = None):
+    """The extra token of block ``b`` drawn at position ``t`` (see
+    ``ora_verify_draw``): returns ``(token, margin)``."""
+    tl, dt, B, L, V, ld = _tlogits(tlogits, vocab)
+    cand_id = None if cand_id is None else np.ascontiguousarray(cand_id, np.int32)
+    q = None if q is None else np.ascontiguousarray(q, np.float64)
+    ur = None if u_res is None else np.ascontiguousarray(u_res, np.float32)
+    tok = C.c_int(0)
+    mg = C.c_double(0)
+    _check(_load().ora_verify_draw(_p(tl), dt, B, L, V, ld, _p(cand_id), _p(q), int(mode), float(T),
+                                   _p(ur), int(b), int(t), int(bool(residual)), C.byref(tok), C.byref(mg)),
+           "verify_draw")
+    return tok.value, mg.value

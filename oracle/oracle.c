@@ -10,6 +10,7 @@
 
 #include <math.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 static double bf16_to_f64(uint16_t u) {
@@ -249,4 +250,147 @@ int ora_step_table(const double *S, const float *uniforms, double T, int mode,
         }
     }
     return bad ? -1 : 0;
+}
+
+/* ------------------------------------------------------ verification ---- */
+/* [P1] Method (lossless rejection sampling restores the target's sampling
+ * distribution) and Setup; [P3] "One pass to draft, one pass to verify".
+ * Plain definitions, fp64: softmax over the whole vocabulary, the min(1, p/q)
+ * acceptance as a multiply-compare, and the inverse-CDF draw in token order. */
+
+/* arg max of a row, ties to the lower id, NaN lowest */
+static int64_t row_argmax(const void *tl, int dtype, int64_t base, int64_t V) {
+    int64_t best = 0;
+    double bv = logit_at(tl, dtype, base);
+    for (int64_t v = 1; v < V; ++v) {
+        double x = logit_at(tl, dtype, base + v);
+        if (ranks_above(x, v, bv, best)) {
+            bv = x;
+            best = v;
+        }
+    }
+    return best;
+}
+
+/* max and sum of exp((z - max) / T) of a row */
+static void row_softmax_stats(const void *tl, int dtype, int64_t base, int64_t V, double T, double *m,
+                              double *Z) {
+    double mx = -INFINITY;
+    for (int64_t v = 0; v < V; ++v) {
+        double x = logit_at(tl, dtype, base + v);
+        if (x > mx) mx = x;
+    }
+    double z = 0.0;
+    for (int64_t v = 0; v < V; ++v) z += exp((logit_at(tl, dtype, base + v) - mx) / T);
+    *m = mx;
+    *Z = z;
+}
+
+/* q_t(v) of token v at (b, t): the candidate's weight, 0 off the candidates */
+static double draft_q(const int32_t *cand_id, const double *q, int64_t bt, int64_t v) {
+    for (int j = 0; j < ORA_K; ++j)
+        if (cand_id[bt * ORA_K + j] == v) return q[bt * ORA_K + j];
+    return 0.0;
+}
+
+/* inverse-CDF draw over the vocabulary from w(v) = p(v) (residual = 0) or
+ * max(0, p(v) - q(v)) (residual = 1); p(v) = exp((z_v - m) / T) / Z */
+static void draw_token(const void *tl, int dtype, int64_t base, int64_t V, double T, double m, double Z,
+                       const int32_t *cand_id, const double *q, int64_t bt, int residual, double u,
+                       int32_t *tok, double *margin) {
+    double *w = (double *)malloc((size_t)V * sizeof(double));
+    double tot = 0.0;
+    for (int64_t v = 0; v < V; ++v) {
+        double p = exp((logit_at(tl, dtype, base + v) - m) / T) / Z;
+        if (residual) {
+            double d = p - draft_q(cand_id, q, bt, v);
+            p = d > 0.0 ? d : 0.0;
+        }
+        w[v] = p;
+        tot += p;
+    }
+    const double target = u * tot;
+    double c = 0.0, prev = 0.0;
+    int64_t pick = -1, last_pos = -1;
+    for (int64_t v = 0; v < V; ++v) {
+        prev = c;
+        c += w[v];
+        if (w[v] > 0.0) last_pos = v;
+        if (target < c) {
+            pick = v;
+            break;
+        }
+    }
+    if (pick < 0) {  /* u Z at or past the total (rounding): the last token with weight */
+        pick = last_pos;
+        prev = c - (pick >= 0 ? w[pick] : 0.0);
+    }
+    *tok = (int32_t)pick;
+    if (margin) {
+        double lo = target - prev, hi = c - target;
+        *margin = (tot > 0.0 ? (lo < hi ? lo : hi) / tot : NAN);
+    }
+    free(w);
+}
+
+int ora_verify_draw(const void *tlogits, int dtype, int64_t B, int64_t L, int64_t V, int64_t ld,
+                    const int32_t *cand_id, const double *q, int mode, double T, const float *u_res,
+                    int64_t b, int64_t t, int residual, int32_t *tok, double *margin) {
+    if (!tlogits || !tok || b < 0 || b >= B || t < 0 || t > L || V < 1 || ld < V) return -1;
+    const int64_t base = (b * (L + 1) + t) * ld;
+    if (mode == 0) {
+        *tok = (int32_t)row_argmax(tlogits, dtype, base, V);
+        if (margin) *margin = NAN;
+        return 0;
+    }
+    if (mode != 1 || !(T > 0.0) || !u_res || (residual && (!cand_id || !q || t >= L))) return -1;
+    double m, Z;
+    row_softmax_stats(tlogits, dtype, base, V, T, &m, &Z);
+    draw_token(tlogits, dtype, base, V, T, m, Z, cand_id, q, b * L + t, residual, (double)u_res[b], tok,
+               margin);
+    return 0;
+}
+
+int ora_verify(const void *tlogits, int dtype, int64_t B, int64_t L, int64_t V, int64_t ld,
+               const int32_t *cand_id, const int32_t *path_slot, const double *q, int mode,
+               double T, const float *u_acc, const float *u_res, int32_t *n_acc,
+               int32_t *out_tok, double *m_acc, double *m_draw) {
+    if (!tlogits || !cand_id || !path_slot || !n_acc || !out_tok || B < 0 || L < 1 || V < 1 || ld < V)
+        return -1;
+    if (dtype != 0 && dtype != 1) return -1;
+    if (mode == 1 && (!q || !u_acc || !u_res || !(T > 0.0))) return -1;
+    if (mode != 0 && mode != 1) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t b = 0; b < B; ++b) {
+        int64_t t = 0;
+        for (; t < L; ++t) {
+            const int64_t bt = b * L + t;
+            const int32_t x = cand_id[bt * ORA_K + path_slot[bt]];
+            const int64_t base = (b * (L + 1) + t) * ld;
+            int ok;
+            if (mode == 0) {
+                ok = row_argmax(tlogits, dtype, base, V) == x;
+                if (m_acc) m_acc[bt] = NAN;
+            } else {
+                double m, Z;
+                row_softmax_stats(tlogits, dtype, base, V, T, &m, &Z);
+                const double px = exp((logit_at(tlogits, dtype, base + x) - m) / T) / Z;
+                const double lhs = (double)u_acc[bt] * q[bt * ORA_K + path_slot[bt]];
+                ok = lhs < px;
+                if (m_acc) m_acc[bt] = fabs(lhs - px);
+            }
+            if (!ok) break;
+            out_tok[b * (L + 1) + t] = x;
+        }
+        for (int64_t s = t + 1; s < L; ++s)
+            if (m_acc) m_acc[b * L + s] = NAN;
+        n_acc[b] = (int32_t)t;
+        int32_t tok;
+        double mg = NAN;
+        ora_verify_draw(tlogits, dtype, B, L, V, ld, cand_id, q, mode, T, u_res, b, t, t < L, &tok, &mg);
+        out_tok[b * (L + 1) + t] = tok;
+        for (int64_t s = t + 1; s <= L; ++s) out_tok[b * (L + 1) + s] = -1;
+        if (m_draw) m_draw[b] = mg;
+    }
+    return 0;
 }

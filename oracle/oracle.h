@@ -70,6 +70,45 @@ int ora_walk(const double *S, const int32_t *cand_id, const float *uniforms, dou
 int ora_step_table(const double *S, const float *uniforms, double T, int mode,
                    int64_t B, int64_t L, int32_t *choice, double *aux);
 
+/* ------------------------------------------------------ verification ---- */
+/* Lossless verification of a drafted block against the target model ([P1]
+ * Method, last paragraph, and Setup: sampling stays lossless through rejection
+ * sampling; [P3] "One pass to draft, one pass to verify": the accepted prefix
+ * is kept and the first miss is replaced by the target's own choice).
+ *
+ * target logits: rows (b, t), t = 0..L (row L follows the block), ld elements
+ * apart, fp32 (dtype 0) or bf16 bits (dtype 1).  The drafted token of position
+ * t is cand_id[b,t,path_slot[b,t]], drawn from q[b,t,:] (the walk's 16-way
+ * distribution over the candidates).
+ *
+ * mode 0 (greedy): accept while the drafted token is the target's arg max
+ *   (ties to the lower id, NaN lowest); the first miss, or row L if all
+ *   are accepted, contributes the target's arg max.
+ * mode 1 (sampled, T > 0): p_t = softmax(z_t / T) over the vocabulary.
+ *   Position t accepts its token x iff u_acc[b,t] * q_t(x) < p_t(x) (so with
+ *   probability min(1, p/q)).  At the first rejection the extra token is drawn
+ *   from r(v) = max(0, p_t(v) - q_t(v)) / Z_r, q_t being zero off the
+ *   candidates; if all L are accepted it is drawn from p_L.  The draw is the
+ *   inverse CDF in token-id order: the first v with u_res[b] * Z < C_v.
+ *
+ * Outputs: n_acc[b]; out_tok[b, 0..L]: the n_acc accepted tokens, then the
+ * extra token at index n_acc, -1 after it.  Diagnostics (nullable):
+ *   m_acc[b,t]  sampled: |u q - p| of each tested position (NaN when untested);
+ *               greedy: NaN.
+ *   m_draw[b]   sampled: distance of u Z to the nearest CDF edge of the drawn
+ *               token, divided by Z; greedy: NaN. */
+int ora_verify(const void *tlogits, int dtype, int64_t B, int64_t L, int64_t V, int64_t ld,
+               const int32_t *cand_id, const int32_t *path_slot, const double *q, int mode,
+               double T, const float *u_acc, const float *u_res, int32_t *n_acc,
+               int32_t *out_tok, double *m_acc, double *m_draw);
+
+/* The extra token alone, for a given position t of block b: with residual = 1
+ * the draw from max(0, p_t - q_t), else from p_t (mode 1), or the arg max of
+ * row t (mode 0).  *tok and *margin as above. */
+int ora_verify_draw(const void *tlogits, int dtype, int64_t B, int64_t L, int64_t V, int64_t ld,
+                    const int32_t *cand_id, const double *q, int mode, double T, const float *u_res,
+                    int64_t b, int64_t t, int residual, int32_t *tok, double *margin);
+
 #ifdef __cplusplus
 }
 #endif

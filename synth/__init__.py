@@ -43,6 +43,7 @@ K = 16  # candidates kept per draft position
 
 # tensor tags for SeedSequence spawn keys
 _T_LOGITS, _T_E, _T_WA, _T_WB, _T_WH, _T_H, _T_VER, _T_U, _T_INJ = range(1, 10)
+_T_TGT, _T_UACC, _T_URES = range(10, 13)
 _E_CHUNK = 256  # rows of E per seed child
 
 
@@ -198,6 +199,43 @@ def make_verified(cfg: Config, seed: int = 0) -> np.ndarray:
 def make_uniforms(cfg: Config, seed: int = 0) -> np.ndarray:
     """Caller-side uniforms of the sampled walk, ``U[0,1)`` float32 ``[batch, block]``."""
     return _rng(seed, _T_U).random((cfg.batch, cfg.block), dtype=np.float32)
+
+
+def make_target_logits(cfg: Config, seed: int = 0, blocks: Optional[Iterable[int]] = None,
+                       noise: float = 1.0) -> np.ndarray:
+    """Target-model logits for verifying each block: ``[nb, block + 1, vocab]``
+    in the draft logits' dtype.  Row t < block is the draft's row t plus
+    N(0, noise^2) per token (a target that mostly agrees with the drafter);
+    row ``block`` (the token after the block) is a fresh draw of the same
+    kind."""
+    blocks = list(range(cfg.batch)) if blocks is None else list(blocks)
+    prior = None
+    if cfg.logit_kind == "gumbel_zipf":
+        prior = (-np.log(np.arange(1, cfg.vocab + 1, dtype=np.float64))).astype(np.float32)
+    dt = np.float32 if cfg.logits_dtype == "f32" else np.uint16
+    L, V = cfg.block, cfg.vocab
+    out = np.empty((len(blocks), L + 1, V), dtype=dt)
+
+    def one(i):
+        b = blocks[i]
+        x = np.empty((L + 1, V), np.float32)
+        x[:L] = _logits_block(cfg, seed, b, prior)
+        for t in range(L):
+            x[t] += np.float32(noise) * _rng(seed, _T_TGT, b * (L + 1) + t).standard_normal(V, dtype=np.float32)
+        rng = _rng(seed, _T_TGT, b * (L + 1) + L)
+        x[L] = _gumbel_zipf_row(rng, prior) if prior is not None else rng.standard_normal(V, dtype=np.float32)
+        out[i] = x if cfg.logits_dtype == "f32" else f32_to_bf16_bits(x)
+
+    with ThreadPoolExecutor(_workers()) as ex:
+        list(ex.map(one, range(len(blocks))))
+    return out
+
+
+def make_verify_uniforms(cfg: Config, seed: int = 0):
+    """Caller-side uniforms of the sampled verification: ``u_acc [batch, block]``
+    (one per acceptance test) and ``u_res [batch]`` (the extra token's draw)."""
+    return (_rng(seed, _T_UACC).random((cfg.batch, cfg.block), dtype=np.float32),
+            _rng(seed, _T_URES).random(cfg.batch, dtype=np.float32))
 
 
 def make(cfg: Config, seed: int = 0) -> Dict[str, np.ndarray]:
