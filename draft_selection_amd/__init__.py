@@ -65,6 +65,8 @@ def _load():
             "dsel_project_cand": ([P, I64, I64, P, P, I64, P, I64, I64, P, P, P, SZ, P], I32),
             "dsel_score_pairs": ([P, P, P, P, I64, I64, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_walk": ([P, I64, I64, C.POINTER(WalkArgs), P], I32),
+            "dsel_verify_workspace_bytes": ([I64, I64, I64], SZ),
+            "dsel_verify": ([P, I32, I64, I64, I64, I64, P, P, P, I32, C.c_float, P, P, P, P, P, SZ, P], I32),
             "dsel_device_error": ([C.POINTER(C.c_int32), P], I32),
             "dsel_status_string": ([I32], C.c_char_p),
             "dsel_version": ([], I32),
@@ -302,6 +304,44 @@ def device_error(stream=None) -> int:
     v = C.c_int32(0)
     _check(_load().dsel_device_error(C.byref(v), _stream(stream)), "dsel_device_error")
     return int(v.value)
+
+
+def verify_workspace_bytes(batch: int, block: int, vocab: int) -> int:
+    return int(_load().dsel_verify_workspace_bytes(batch, block, vocab))
+
+
+def verify(target_logits, cand_id, path_slot, q=None, mode: int = GREEDY, temperature: float = 1.0,
+           u_acc=None, u_res=None, vocab: Optional[int] = None, workspace=None, stream=None):
+    """Verify drafted blocks against target logits ``[B, L+1, ld]`` (fp32 or
+    bf16): returns ``(n_accepted [B] int32, out_tok [B, L+1] int32)``."""
+    B, L1, ld = target_logits.shape
+    L = L1 - 1
+    V = ld if vocab is None else int(vocab)
+    dt = F32 if target_logits.dtype == torch.float32 else BF16
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("target_logits must be float32 or bfloat16")
+    if target_logits.stride(2) != 1 or target_logits.stride(1) != target_logits.stride(2) * ld \
+            or target_logits.stride(0) != L1 * ld:
+        raise ValueError("target_logits must be contiguous")
+    _need(cand_id, "cand_id", torch.int32, (B, L, K))
+    _need(path_slot, "path_slot", torch.int32, (B, L))
+    if mode == SAMPLED:
+        _need(q, "q", torch.float32, (B, L, K))
+        _need(u_acc, "u_acc", torch.float32, (B, L))
+        _need(u_res, "u_res", torch.float32, (B,))
+    dev = target_logits.device
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tok = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(verify_workspace_bytes(B, L, V), 1), dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    st = _load().dsel_verify(_ptr(target_logits), dt, B, L, V, ld, _ptr(cand_id), _ptr(path_slot),
+                             _ptr(q) if mode == SAMPLED else None, int(mode), float(temperature),
+                             _ptr(u_acc) if mode == SAMPLED else None,
+                             _ptr(u_res) if mode == SAMPLED else None, _ptr(n_acc), _ptr(out_tok),
+                             _ptr(workspace), wsb, _stream(stream))
+    _check(st, "dsel_verify")
+    return n_acc, out_tok
 
 
 def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,

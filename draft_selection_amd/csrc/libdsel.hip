@@ -11,6 +11,7 @@
 #include "pairwalk.h"
 #include "project.h"
 #include "topk16.h"
+#include "verify.h"
 
 #define DSEL_API extern "C" __attribute__((visibility("default")))
 
@@ -342,3 +343,65 @@ DSEL_API const char *dsel_status_string(dsel_status s) {
 }
 
 DSEL_API int32_t dsel_version(void) { return DSEL_VERSION; }
+
+// ---- verify ----------------------------------------------------------------
+
+DSEL_API size_t dsel_verify_workspace_bytes(int64_t batch, int64_t block, int64_t vocab) {
+    if (batch <= 0 || block < 1 || block > DSEL_MAX_BLOCK || vocab < kK ||
+        vocab > (int64_t)kVChunk * kVMaxChunks)
+        return 0;
+    return verify_workspace_bytes(batch, block, vocab);
+}
+
+DSEL_API dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64_t batch,
+                                 int64_t block, int64_t vocab, int64_t ld, const int32_t *cand_id,
+                                 const int32_t *path_slot, const float *q, dsel_walk_mode mode,
+                                 float temperature, const float *u_acc, const float *u_res,
+                                 int32_t *n_accepted, int32_t *out_tok, void *workspace,
+                                 size_t workspace_bytes, dsel_stream_t stream) {
+    if (dt != DSEL_F32 && dt != DSEL_BF16) return DSEL_E_DTYPE;
+    if (mode != DSEL_GREEDY && mode != DSEL_SAMPLED) return DSEL_E_DTYPE;
+    if (batch < 0 || batch >= (int64_t)INT_MAX / (DSEL_MAX_BLOCK + 1) || block < 1 || block > DSEL_MAX_BLOCK)
+        return DSEL_E_ARG;
+    if (vocab < kK || vocab > (int64_t)kVChunk * kVMaxChunks || ld < vocab) return DSEL_E_ARG;
+    if (mode == DSEL_SAMPLED && !(temperature > 0.0f && temperature < __builtin_inff())) return DSEL_E_ARG;
+    if (batch == 0) return DSEL_OK;
+    if (!target_logits || !cand_id || !path_slot || !n_accepted || !out_tok) return DSEL_E_ARG;
+    if (mode == DSEL_SAMPLED && (!q || !u_acc || !u_res)) return DSEL_E_ARG;
+    const int64_t es = dt == DSEL_BF16 ? 2 : 4;
+    const int64_t rows = batch * (block + 1);
+    if (ld > INT64_MAX / es / rows) return DSEL_E_ARG;
+    if (!aligned(target_logits, 16) || (ld * es) % 16 != 0) return DSEL_E_ALIGN;
+    if (!aligned(cand_id, 4) || !aligned(path_slot, 4) || !aligned(n_accepted, 4) || !aligned(out_tok, 4) ||
+        (q && !aligned(q, 4)) || (u_acc && !aligned(u_acc, 4)) || (u_res && !aligned(u_res, 4)))
+        return DSEL_E_ALIGN;
+    const size_t need = verify_workspace_bytes(batch, block, vocab);
+    if (!workspace || workspace_bytes < need) return DSEL_E_WORKSPACE;
+    if (!aligned(workspace, 16)) return DSEL_E_ALIGN;
+
+    VerifyParams p;
+    p.logits = (const char *)target_logits;
+    p.V = vocab;
+    p.ld = ld;
+    p.B = (int)batch;
+    p.L = (int)block;
+    p.nchunk = (int)((vocab + kVChunk - 1) / kVChunk);
+    p.scale = mode == DSEL_SAMPLED ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
+    p.cand_id = cand_id;
+    p.path_slot = path_slot;
+    p.q = q;
+    p.u_acc = u_acc;
+    p.u_res = u_res;
+    p.n_acc = n_accepted;
+    p.out_tok = out_tok;
+    p.row_stat = (float *)workspace;
+    p.chunk_stat = p.row_stat + rows * 4;
+    const bool bf = dt == DSEL_BF16, sm = mode == DSEL_SAMPLED;
+    const void *k1 = bf ? (sm ? (const void *)verify_stats_kernel<true, true> : (const void *)verify_stats_kernel<true, false>)
+                        : (sm ? (const void *)verify_stats_kernel<false, true> : (const void *)verify_stats_kernel<false, false>);
+    const void *k2 = bf ? (sm ? (const void *)verify_draw_kernel<true, true> : (const void *)verify_draw_kernel<true, false>)
+                        : (sm ? (const void *)verify_draw_kernel<false, true> : (const void *)verify_draw_kernel<false, false>);
+    dsel_status st = launch(k1, dim3((unsigned)rows), dim3(256), &p, 0, stream);
+    if (st != DSEL_OK) return st;
+    return launch(k2, dim3((unsigned)batch), dim3(256), &p, 0, stream);
+}

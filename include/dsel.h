@@ -184,6 +184,42 @@ dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const flo
 dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const dsel_walk_args *walk,
                       dsel_stream_t stream);
 
+/* verify -- lossless verification of the drafted blocks against the target
+ * model, the step after the walk ([P1] Method, last paragraph, and Setup:
+ * sampling stays lossless through rejection sampling; [P3] "One pass to draft,
+ * one pass to verify": the accepted prefix is kept and the first miss is
+ * replaced by the target's own choice).
+ *   target_logits  [batch * (block + 1)][ld] of dtype `dt`: row (b, t) holds
+ *                  the target's logits for position t of block b (row t = block
+ *                  is the position after the block).  Row starts must be 16-byte
+ *                  aligned (pointer and ld * element size); 16 <= vocab <=
+ *                  4,194,304; ld >= vocab.
+ *   cand_id, path_slot, q   the walk's candidates [batch, block, 16], chosen
+ *                  slots [batch, block] and (sampled mode) its 16-way step
+ *                  distributions q [batch, block, 16] (nullable when greedy).
+ *   mode           DSEL_GREEDY: position t is accepted while its drafted token
+ *                  is the arg max of target row t (ties to the lower id, NaN
+ *                  lowest); the extra token is the arg max of the first rejected
+ *                  row, or of row `block` when all are accepted.
+ *                  DSEL_SAMPLED (temperature T > 0): p_t = softmax(z_t / T); t
+ *                  accepts its token x iff u_acc[b,t] * q_t(x) < p_t(x); the
+ *                  extra token is the inverse-CDF draw (token order, uniform
+ *                  u_res[b]) from max(0, p_t - q_t) at the first rejection (q_t
+ *                  is zero off the candidates), or from p_block if none.  Target
+ *                  logits must then be finite or -inf, with a finite row max.
+ *   n_accepted     out [batch] int32: accepted positions n (0..block).
+ *   out_tok        out [batch, block + 1] int32: the n accepted tokens, the
+ *                  extra token at index n, -1 after it.
+ *   workspace      device scratch of dsel_verify_workspace_bytes() bytes;
+ *                  contents need no initialisation.
+ * Requirements: 1 <= block <= DSEL_MAX_BLOCK. */
+size_t dsel_verify_workspace_bytes(int64_t batch, int64_t block, int64_t vocab);
+dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64_t batch, int64_t block,
+                        int64_t vocab, int64_t ld, const int32_t *cand_id, const int32_t *path_slot,
+                        const float *q, dsel_walk_mode mode, float temperature, const float *u_acc,
+                        const float *u_res, int32_t *n_accepted, int32_t *out_tok, void *workspace,
+                        size_t workspace_bytes, dsel_stream_t stream);
+
 /* Synchronise `stream`, then read and clear the device error word of the
  * current device (bits DSEL_DEVERR_*; 0 = no error). */
 dsel_status dsel_device_error(int32_t *out_code, dsel_stream_t stream);

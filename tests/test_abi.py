@@ -31,7 +31,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("dsel_select_topk", "dsel_project", "dsel_project_gate", "dsel_project_cand",
-                 "dsel_score_pairs", "dsel_walk"):
+                 "dsel_score_pairs", "dsel_walk", "dsel_verify"):
         assert want in names
 
 
@@ -105,3 +105,27 @@ def test_validation_rejects_before_launch(lib):
     assert lib.dsel_walk(fake, 1, 8, C.byref(w), None) == -1
     assert lib.dsel_walk(fake, 1, 0, C.byref(w), None) == -1
     assert lib.dsel_device_error(None, None) == -1
+
+
+def test_verify_validation(lib):
+    P = C.c_void_p
+    fake, odd = P(0x100000), P(0x100008)
+    ws = lib.dsel_verify_workspace_bytes(4, 8, 151936)
+    assert ws > 0 and lib.dsel_verify_workspace_bytes(4, 33, 151936) == 0
+    assert lib.dsel_verify_workspace_bytes(4, 8, (1 << 22) + 1) == 0
+
+    def call(**kw):
+        a = dict(tl=fake, dt=1, B=4, L=8, V=151936, ld=151936, cand=fake, slot=fake, q=fake, mode=1,
+                 T=C.c_float(1.0), ua=fake, ur=fake, n=fake, out=fake, ws=fake, wsb=ws)
+        a.update(kw)
+        return lib.dsel_verify(a["tl"], a["dt"], a["B"], a["L"], a["V"], a["ld"], a["cand"], a["slot"],
+                               a["q"], a["mode"], a["T"], a["ua"], a["ur"], a["n"], a["out"], a["ws"],
+                               a["wsb"], None)
+
+    assert call(dt=3) == -2 and call(mode=2) == -2
+    assert call(L=33) == -1 and call(V=(1 << 22) + 1, ld=(1 << 22) + 8) == -1 and call(ld=100) == -1
+    assert call(T=C.c_float(0.0)) == -1 and call(q=None) == -1 and call(ur=None) == -1
+    assert call(mode=0, q=None, ua=None, ur=None, T=C.c_float(0.0), ws=None, wsb=0) == -4
+    assert call(tl=odd) == -3 and call(ld=151937) == -3     # row starts must be 16-byte aligned
+    assert call(ws=None) == -4 and call(wsb=ws - 1) == -4
+    assert call(B=0, tl=None, cand=None) == 0               # no work: pointers may be NULL
