@@ -154,6 +154,59 @@ def cpu_baseline(cfg, inp, budget_s=15.0):
                       f"(top-16, fp64 projections, scores, walk), {t_total:.1f} s"}
 
 
+def time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream):
+    """Verification of the drafted blocks (the step after the walk) against
+    synthetic target logits [batch, block + 1, vocab]: HIP-event time per call
+    and the HBM rate of its one pass over the target logits."""
+    import torch
+
+    import synth
+
+    B, L, V = cfg.batch, cfg.block, cfg.vocab
+    tl = synth.make_target_logits(cfg)
+    ua, ur = synth.make_verify_uniforms(cfg)
+    dev = cand_id.device
+    if tl.dtype == np.uint16:
+        d_tl = torch.from_numpy(tl.view(np.int16)).to(dev).view(torch.bfloat16)
+    else:
+        d_tl = torch.from_numpy(tl).to(dev)
+    del tl
+    d_ua, d_ur = torch.from_numpy(ua).to(dev), torch.from_numpy(ur).to(dev)
+    n_acc = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tok = torch.empty((B, L + 1), dtype=torch.int32, device=dev)
+    wsb = lib.dsel_verify_workspace_bytes(B, L, V)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    q = wres.get("q")
+    import ctypes as C
+    sp = C.c_void_p(stream.cuda_stream)
+
+    def call():
+        st = lib.dsel_verify(P(d_tl), dt, B, L, V, V, P(cand_id), P(wres["path_slot"]),
+                             P(q) if mode == 1 else None, mode, C.c_float(cfg.temperature),
+                             P(d_ua) if mode == 1 else None, P(d_ur) if mode == 1 else None,
+                             P(n_acc), P(out_tok), P(ws), wsb, sp)
+        if st:
+            raise RuntimeError(f"dsel_verify status {st}")
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    k = min(args.steps, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(k):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / k
+    nbytes = B * (L + 1) * V * (2 if cfg.logits_dtype == "bf16" else 4)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"mode": "sampled" if mode == 1 else "greedy", "us_per_call": round(us, 2),
+            "target_logits_bytes": nbytes, "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "mean_accepted": round(float(n_acc.float().mean()), 3),
+            "data": "synthetic target logits: draft logits + N(0,1) noise, fresh row after the block"}
+
+
 def stage_means(evs):
     """Mean microseconds between consecutive stage events over the steps."""
     names = ("project_gate", "select_topk", "project_cand", "score_pairs_walk")
@@ -174,6 +227,8 @@ def main():
                     help="run the gate GEMM before the top-16 or beside it on a second stream")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the pass that evicts the caches before every step")
+    ap.add_argument("--no-verify", action="store_true",
+                    help="skip timing the verification of the drafted blocks (dsel_verify)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
@@ -215,7 +270,8 @@ def main():
     pwsb = ds.project_workspace_bytes(B, L, cfg.d, cfg.r)
     pws = torch.empty(max(pwsb, 1), dtype=torch.uint8, device=dev)
     S = torch.empty((B, L, K, K), dtype=torch.float32, device=dev)
-    wargs, wres = ds._walk_args(cand_id, mode, cfg.temperature, d["uniforms"], False, True)
+    # the sampled walk also returns its step distributions q: verification needs them
+    wargs, wres = ds._walk_args(cand_id, mode, cfg.temperature, d["uniforms"], mode == 1, True)
 
     import ctypes as C
     lib = ds.lib()
@@ -307,6 +363,8 @@ def main():
         del flush
         cold = stage_means(cevs)
 
+    verify = None if args.no_verify else time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream)
+
     ms_step = wall * 1e3 / args.steps
     warm = stage_means(evs)
     st_topk, st_proj, st_pair = warm["select_topk"], warm["project_cand"], warm["score_pairs_walk"]
@@ -349,6 +407,7 @@ def main():
         "project_cand_mfma": {"TFLOP/s": round(proj_tfs, 2), "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4)},
         "project_gate": args.gate,
         "roofline": roof,
+        "verify": verify,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

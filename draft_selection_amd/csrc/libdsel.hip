@@ -348,7 +348,7 @@ DSEL_API int32_t dsel_version(void) { return DSEL_VERSION; }
 
 DSEL_API size_t dsel_verify_workspace_bytes(int64_t batch, int64_t block, int64_t vocab) {
     if (batch <= 0 || block < 1 || block > DSEL_MAX_BLOCK || vocab < kK ||
-        vocab > (int64_t)kVChunk * kVMaxChunks)
+        vocab > kVMaxVocab)
         return 0;
     return verify_workspace_bytes(batch, block, vocab);
 }
@@ -363,7 +363,7 @@ DSEL_API dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64
     if (mode != DSEL_GREEDY && mode != DSEL_SAMPLED) return DSEL_E_DTYPE;
     if (batch < 0 || batch >= (int64_t)INT_MAX / (DSEL_MAX_BLOCK + 1) || block < 1 || block > DSEL_MAX_BLOCK)
         return DSEL_E_ARG;
-    if (vocab < kK || vocab > (int64_t)kVChunk * kVMaxChunks || ld < vocab) return DSEL_E_ARG;
+    if (vocab < kK || vocab > kVMaxVocab || ld < vocab) return DSEL_E_ARG;
     if (mode == DSEL_SAMPLED && !(temperature > 0.0f && temperature < __builtin_inff())) return DSEL_E_ARG;
     if (batch == 0) return DSEL_OK;
     if (!target_logits || !cand_id || !path_slot || !n_accepted || !out_tok) return DSEL_E_ARG;
@@ -385,7 +385,6 @@ DSEL_API dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64
     p.ld = ld;
     p.B = (int)batch;
     p.L = (int)block;
-    p.nchunk = (int)((vocab + kVChunk - 1) / kVChunk);
     p.scale = mode == DSEL_SAMPLED ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
     p.cand_id = cand_id;
     p.path_slot = path_slot;
@@ -394,14 +393,24 @@ DSEL_API dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64
     p.u_res = u_res;
     p.n_acc = n_accepted;
     p.out_tok = out_tok;
-    p.row_stat = (float *)workspace;
-    p.chunk_stat = p.row_stat + rows * 4;
     const bool bf = dt == DSEL_BF16, sm = mode == DSEL_SAMPLED;
+    // chunks of 256 16-byte vectors; enough workgroups per row for about 2048
+    // in all (8 per CU), at most kVMaxSplit, none of them empty
+    const int64_t chunk_tokens = (int64_t)kVChunkVecs * (bf ? 8 : 4);
+    p.nchunk = (int)((vocab + chunk_tokens - 1) / chunk_tokens);
+    int64_t ns = (2048 + rows - 1) / rows;
+    ns = ns < 1 ? 1 : ns > kVMaxSplit ? kVMaxSplit : ns;
+    ns = ns < p.nchunk ? ns : p.nchunk;
+    p.cps = (int)((p.nchunk + ns - 1) / ns);
+    p.nsplit = (p.nchunk + p.cps - 1) / p.cps;
+    if (rows * p.nsplit > (int64_t)INT_MAX) return DSEL_E_ARG;
+    p.part = (VerifyPart *)workspace;
+    p.chunk = (float2 *)((char *)workspace + verify_part_bytes(batch, block));
     const void *k1 = bf ? (sm ? (const void *)verify_stats_kernel<true, true> : (const void *)verify_stats_kernel<true, false>)
                         : (sm ? (const void *)verify_stats_kernel<false, true> : (const void *)verify_stats_kernel<false, false>);
     const void *k2 = bf ? (sm ? (const void *)verify_draw_kernel<true, true> : (const void *)verify_draw_kernel<true, false>)
                         : (sm ? (const void *)verify_draw_kernel<false, true> : (const void *)verify_draw_kernel<false, false>);
-    dsel_status st = launch(k1, dim3((unsigned)rows), dim3(256), &p, 0, stream);
+    dsel_status st = launch(k1, dim3((unsigned)(rows * p.nsplit)), dim3(256), &p, 0, stream);
     if (st != DSEL_OK) return st;
     return launch(k2, dim3((unsigned)batch), dim3(256), &p, 0, stream);
 }

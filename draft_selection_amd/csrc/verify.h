@@ -16,34 +16,50 @@
 //            candidates), or from p_L when every position is accepted.
 //
 // Two kernels:
-//   verify_stats_kernel  one workgroup (4 waves) per target row, HBM-bound: one
-//       pass over the row gives its arg max and, for the sampled rule, its max
-//       m and Z = sum exp2((z - m) s) (s = log2(e) / T), plus the same two
-//       numbers for every chunk of 2048 tokens (the draw needs them).
+//   verify_stats_kernel  HBM-bound, nsplit workgroups (4 waves) per target row.
+//       A row is cut into chunks of 256 16-byte vectors (2048 bf16 or 1024
+//       fp32 tokens); each wave streams whole chunks with non-temporal loads,
+//       the next chunk in flight while the current one is reduced.  Greedy: a
+//       per-vector max screens the exact (value, id) key compare of the arg
+//       max.  Sampled: per chunk its max mc and sum of exp2((z - mc) s),
+//       s = log2(e) / T, kept for the draw; the wave folds the chunks into
+//       one (max, sum) by rescaling.  Each workgroup writes one partial.
 //   verify_draw_kernel   one workgroup per block: the L acceptance tests run in
-//       parallel (one lane each) and the first miss is a ballot; the extra
-//       token's inverse CDF walks the chunk masses (prefix scan over chunks),
-//       then scans the one chunk where u_res * Z falls.
+//       parallel (one lane each, partials combined in a fixed order) and the
+//       first miss is a ballot.  The sampled extra token's inverse CDF prefix-
+//       scans the chunk masses (candidate corrections added per chunk), then
+//       loads the one chunk that holds u_res * Z, one vector per thread, and
+//       prefix-scans its tokens.
 #pragma once
 
 #include "common.h"
 
 namespace dsel {
 
-constexpr int kVChunk = 2048;        // tokens per chunk of the row statistics
-constexpr int kVMaxChunks = 2048;    // vocab <= 2048 chunks = 4,194,304 tokens
+constexpr int64_t kVMaxVocab = 1 << 22;  // 4,194,304 tokens
+constexpr int kVU = 4;                   // 16-byte vectors per lane per chunk
+constexpr int kVChunkVecs = kWave * kVU; // 256 vectors per chunk
+constexpr int kVMaxSplit = 16;           // workgroups per row, at most
+
+// One workgroup's partial result for its slice of a row.
+struct alignas(16) VerifyPart {
+    float m, z;         // sampled: max and sum of exp2((z - m) s) over the slice
+    uint32_t klo, khi;  // greedy: the slice's best (value, id) key
+};
 
 struct VerifyParams {
     const char *logits;  // target row (b, t), t = 0..L, starts at logits + (b (L+1) + t) ld es
     int64_t V, ld;
     int B, L;
-    int nchunk;          // ceil(V / kVChunk)
+    int nsplit;          // workgroups per row
+    int nchunk;          // chunks per row: ceil(V / (256 EPV))
+    int cps;             // chunks per workgroup (the last one may have fewer)
     float scale;         // log2(e) / T (sampled)
     const int32_t *cand_id, *path_slot;
     const float *q, *u_acc, *u_res;
     int32_t *n_acc, *out_tok;
-    float *row_stat;     // [rows][4]: max, Z, arg max (int bits), unused
-    float *chunk_stat;   // [rows][nchunk][2]: chunk max, chunk sum of exp2((z - chunk max) s)
+    VerifyPart *part;    // [rows][nsplit]
+    float2 *chunk;       // [rows][nchunk]: chunk max, sum of exp2((z - max) s) (sampled)
 };
 
 __device__ __forceinline__ float wave_max_f(float x) {
@@ -89,109 +105,182 @@ __device__ __forceinline__ float logit_elem(const char *rowp, int64_t i) {
     else return *(const float *)(rowp + i * 4);
 }
 
-// One pass over a target row: arg max (64-bit candidate keys), and for the
-// sampled rule the row's and every chunk's max / sum of exp2.  Wave w takes
-// chunks w, w + 4, ...; lane l holds elements of vectors c * (2048 / EPV) +
-// u * 64 + l of its chunk (16-byte loads; row starts are 16-byte aligned).
-template <bool BF16, bool SAMPLED>
-__global__ __launch_bounds__(256) void verify_stats_kernel(VerifyParams p) {
-    constexpr int EPV = BF16 ? 8 : 4;
-    constexpr int U = kVChunk / (kWave * EPV);  // vectors per lane per chunk
-    const int64_t row = blockIdx.x;
-    const int wave = (int)(threadIdx.x >> 6);
-    const uint32_t lane = lane_id();
-    const char *rowp = p.logits + row * p.ld * (BF16 ? 2 : 4);
-    const u32x4 *vb = (const u32x4 *)rowp;
-    const float s = p.scale;
-
-    float wm = -__builtin_inff(), ws = 0.0f;  // this wave's running max and sum
-    uint64_t wkey = 0;
-    for (int c = wave; c < p.nchunk; c += 4) {
-        float x[U][EPV];
+// 8 (bf16) or 4 (fp32) logits of a 16-byte vector, widened to float
+template <bool BF16>
+__device__ __forceinline__ void widen_vec(const u32x4 &w, float (&x)[BF16 ? 8 : 4]) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t e0 = ((int64_t)c * (kVChunk / EPV) + u * kWave + lane) * EPV;
-            if (e0 + EPV <= p.V) {
-                const u32x4 w = __builtin_nontemporal_load(vb + e0 / EPV);
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const uint32_t word = w[BF16 ? e >> 1 : e];
-                    x[u][e] = BF16 ? __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16))
-                                   : __uint_as_float(word);
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    x[u][e] = e0 + e < p.V ? logit_elem<BF16>(rowp, e0 + e) : __builtin_nanf("");
-            }
-        }
-        uint64_t key = 0;
-        float lm = -__builtin_inff();
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int e = 0; e < EPV; ++e) {
-                const int64_t id = ((int64_t)c * (kVChunk / EPV) + u * kWave + lane) * EPV + e;
-                if (id < p.V) {
-                    const uint64_t k = cand_key(x[u][e], (uint32_t)id);
-                    key = k > key ? k : key;
-                    lm = __builtin_fmaxf(lm, x[u][e]);
-                }
-            }
-        key = wave_max_u64(key);
-        wkey = key > wkey ? key : wkey;
-        if constexpr (SAMPLED) {
-            const float mc = wave_max_f(lm);
-            float ls = 0.0f;
-#pragma unroll
-            for (int u = 0; u < U; ++u)
-#pragma unroll
-                for (int e = 0; e < EPV; ++e) {
-                    const int64_t id = ((int64_t)c * (kVChunk / EPV) + u * kWave + lane) * EPV + e;
-                    if (id < p.V) ls += exp2_rel(x[u][e], mc, s);
-                }
-            const float sc = wave_sum_f(ls);
-            if (lane == 0) {
-                float *cs = p.chunk_stat + (row * p.nchunk + c) * 2;
-                cs[0] = mc;
-                cs[1] = sc;
-            }
-            const float nm = __builtin_fmaxf(wm, mc);
-            ws = ws * exp2_rel(wm, nm, s) + sc * exp2_rel(mc, nm, s);
-            wm = nm;
-        }
-    }
-    __shared__ float sm[4], ss[4];
-    __shared__ uint64_t sk[4];
-    if (lane == 0) {
-        sm[wave] = wm;
-        ss[wave] = ws;
-        sk[wave] = wkey;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint64_t k = sk[0];
-        float m = sm[0];
-        for (int w = 1; w < 4; ++w) {
-            k = sk[w] > k ? sk[w] : k;
-            m = __builtin_fmaxf(m, sm[w]);
-        }
-        float z = 0.0f;
-        for (int w = 0; w < 4; ++w) z += ss[w] * exp2_rel(sm[w], m, s);
-        float *rs = p.row_stat + row * 4;
-        rs[0] = m;
-        rs[1] = z;
-        rs[2] = __uint_as_float(key_id(k));
-        rs[3] = 0.0f;
+    for (int e = 0; e < (BF16 ? 8 : 4); ++e) {
+        const uint32_t word = w[BF16 ? e >> 1 : e];
+        x[e] = BF16 ? __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16)) : __uint_as_float(word);
     }
 }
 
-// Block-wide exclusive prefix of one float per thread (256 threads), and the
-// total.  Fixed order, so the result is deterministic.
-__device__ __forceinline__ float block_exclusive_scan(float x, float *total, float *lds4) {
+// Load chunk c of a row: lane l takes vectors c 256 + u 64 + l (u < kVU); an
+// index past the row's whole vectors is clamped to the last one (its values
+// are not used).  The loads are issued unconditionally, so the next chunk can
+// be in flight while the current one is reduced.
+__device__ __forceinline__ void verify_load_chunk(u32x4 (&w)[kVU], const u32x4 *vb, int64_t c, int64_t nfull) {
+    const uint32_t lane = lane_id();
+#pragma unroll
+    for (int u = 0; u < kVU; ++u) {
+        int64_t vi = c * kVChunkVecs + u * kWave + lane;
+        vi = vi < nfull ? vi : nfull - 1;
+        w[u] = __builtin_nontemporal_load(vb + vi);
+    }
+}
+
+// Workgroup (row, sp) takes chunks [sp cps, min(nchunk, (sp + 1) cps)); wave w
+// takes every fourth of them starting at the w-th.
+template <bool BF16, bool SAMPLED>
+__global__ __launch_bounds__(256) void verify_stats_kernel(VerifyParams p) {
+    constexpr int EPV = BF16 ? 8 : 4;
+    const int64_t row = blockIdx.x / p.nsplit;
+    const int sp = (int)(blockIdx.x - row * p.nsplit);
+    const int tid = (int)threadIdx.x, wave = tid >> 6;
+    const uint32_t lane = lane_id();
+    const char *rowp = p.logits + row * p.ld * (BF16 ? 2 : 4);
+    const u32x4 *vb = (const u32x4 *)rowp;
+    const int64_t nfull = p.V / EPV;              // whole vectors
+    const int tail = (int)(p.V - nfull * EPV);    // tokens of the partial last vector
+    const int c0 = sp * p.cps;
+    const int c1 = c0 + p.cps < p.nchunk ? c0 + p.cps : p.nchunk;
+    const float s = p.scale;
+
+    float bv = -__builtin_inff();  // greedy: the lane's best value and key
+    uint64_t bkey = 0;
+    float wm = -__builtin_inff(), wz = 0.0f;  // sampled: the wave's running max and sum
+
+    u32x4 cur[kVU], nxt[kVU];
+    int c = c0 + wave;
+    if (c < c1) verify_load_chunk(cur, vb, c, nfull);
+    for (; c < c1; c += 4) {
+        verify_load_chunk(nxt, vb, c + 4 < c1 ? c + 4 : c, nfull);
+        float x[kVU][EPV];
+        int cnt[kVU];
+#pragma unroll
+        for (int u = 0; u < kVU; ++u) {
+            const int64_t vi = (int64_t)c * kVChunkVecs + u * kWave + lane;
+            widen_vec<BF16>(cur[u], x[u]);
+            cnt[u] = vi < nfull ? EPV : (vi == nfull ? tail : 0);
+            if (vi == nfull && tail) {  // the partial last vector, element by element
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    x[u][e] = e < tail ? logit_elem<BF16>(rowp, nfull * EPV + e) : -__builtin_inff();
+            }
+        }
+        if constexpr (!SAMPLED) {
+#pragma unroll
+            for (int u = 0; u < kVU; ++u) {
+                float vm = -__builtin_inff();
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) vm = __builtin_fmaxf(vm, x[u][e]);
+                // NaN (v_max drops it only when the other operand is a number),
+                // ties and the first vector go to the exact compare
+                if (cnt[u] && (!(vm < bv) || bkey == 0 || vm != vm)) {
+                    const int64_t id0 = ((int64_t)c * kVChunkVecs + u * kWave + lane) * EPV;
+#pragma unroll
+                    for (int e = 0; e < EPV; ++e) {
+                        if (e < cnt[u]) {
+                            const uint64_t k = cand_key(x[u][e], (uint32_t)(id0 + e));
+                            if (k > bkey) {
+                                bkey = k;
+                                bv = x[u][e] == x[u][e] ? x[u][e] : bv;
+                            }
+                        }
+                    }
+                }
+            }
+        } else {
+            float lm = -__builtin_inff();
+#pragma unroll
+            for (int u = 0; u < kVU; ++u)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    if (e < cnt[u]) lm = __builtin_fmaxf(lm, x[u][e]);
+            const float mc = wave_max_f(lm);
+            float ls = 0.0f;
+#pragma unroll
+            for (int u = 0; u < kVU; ++u)
+#pragma unroll
+                for (int e = 0; e < EPV; ++e)
+                    if (e < cnt[u]) ls += exp2_rel(x[u][e], mc, s);
+            const float zc = wave_sum_f(ls);
+            if (lane == 0) p.chunk[row * p.nchunk + c] = make_float2(mc, zc);
+            const float nm = __builtin_fmaxf(wm, mc);
+            wz = wz * exp2_rel(wm, nm, s) + zc * exp2_rel(mc, nm, s);
+            wm = nm;
+        }
+#pragma unroll
+        for (int u = 0; u < kVU; ++u) cur[u] = nxt[u];
+    }
+    // the workgroup's partial: waves combined in a fixed order
+    __shared__ float sm[4], sz[4];
+    __shared__ uint64_t sk[4];
+    if constexpr (!SAMPLED) {
+        bkey = wave_max_u64(bkey);
+        if (lane == 0) sk[wave] = bkey;
+    } else if (lane == 0) {
+        sm[wave] = wm;
+        sz[wave] = wz;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        VerifyPart out;
+        if constexpr (!SAMPLED) {
+            uint64_t k = sk[0];
+            for (int w = 1; w < 4; ++w) k = sk[w] > k ? sk[w] : k;
+            out.m = 0.0f;
+            out.z = 0.0f;
+            out.klo = (uint32_t)k;
+            out.khi = (uint32_t)(k >> 32);
+        } else {
+            float m = sm[0];
+            for (int w = 1; w < 4; ++w) m = __builtin_fmaxf(m, sm[w]);
+            float z = 0.0f;
+            for (int w = 0; w < 4; ++w) z += sz[w] * exp2_rel(sm[w], m, s);
+            out.m = m;
+            out.z = z;
+            out.klo = out.khi = 0u;
+        }
+        p.part[row * p.nsplit + sp] = out;
+    }
+}
+
+// A row's arg max (greedy) from its partials.
+__device__ __forceinline__ uint32_t verify_row_argmax(const VerifyParams &p, int64_t row) {
+    uint64_t k = 0;
+    for (int i = 0; i < p.nsplit; ++i) {
+        const VerifyPart &q = p.part[row * p.nsplit + i];
+        const uint64_t ki = ((uint64_t)q.khi << 32) | q.klo;
+        k = ki > k ? ki : k;
+    }
+    return key_id(k);
+}
+
+// A row's max m and Z = sum exp2((z - m) s) (sampled) from its partials, in a
+// fixed order, so every reader of a row gets the same two numbers.
+__device__ __forceinline__ void verify_row_mz(const VerifyParams &p, int64_t row, float *m, float *Z) {
+    float mm = -__builtin_inff();
+    for (int i = 0; i < p.nsplit; ++i) mm = __builtin_fmaxf(mm, p.part[row * p.nsplit + i].m);
+    float z = 0.0f;
+    for (int i = 0; i < p.nsplit; ++i) {
+        const VerifyPart &q = p.part[row * p.nsplit + i];
+        z += q.z * exp2_rel(q.m, mm, p.scale);
+    }
+    *m = mm;
+    *Z = z;
+}
+
+// Block-wide prefix of one non-negative float per thread (256 threads): the
+// thread's interval [lo, hi) of the running sum, and the total.  Each thread's
+// lo is bit-identical to the previous thread's hi (both come from the same
+// additions in the same order), so the intervals tile [0, total) with no gap or
+// overlap and exactly one thread holds any tau in that range.
+__device__ __forceinline__ void block_scan_edges(float x, float *lo, float *hi, float *total, float *lds4) {
     const int wave = (int)(threadIdx.x >> 6);
     const uint32_t lane = lane_id();
     const float inc = wave_scan_f(x);
+    const float prev = shfl_idxf(inc, lane ? lane - 1 : 0);
     if (lane == kWave - 1) lds4[wave] = inc;
     __syncthreads();
     float off = 0.0f, tot = 0.0f;
@@ -201,20 +290,24 @@ __device__ __forceinline__ float block_exclusive_scan(float x, float *total, flo
     }
     __syncthreads();
     *total = tot;
-    return off + inc - x;
+    *hi = off + inc;
+    *lo = lane ? off + prev : off;
 }
 
 template <bool BF16, bool SAMPLED>
 __global__ __launch_bounds__(256) void verify_draw_kernel(VerifyParams p) {
+    constexpr int EPV = BF16 ? 8 : 4;
+    constexpr int CT = kVChunkVecs * EPV;  // tokens per chunk
     const int b = blockIdx.x;
     const int L = p.L;
     const int tid = (int)threadIdx.x;
     const uint32_t lane = lane_id();
     const int64_t es = BF16 ? 2 : 4;
-    __shared__ float w[kVMaxChunks];
     __shared__ float lds4[4];
-    __shared__ int s_n, s_k, s_tok, s_last;
-    __shared__ float s_cbefore;
+    __shared__ int s_n, s_tok, s_last, s_chunk, s_clast;
+    __shared__ float s_off;
+    __shared__ int32_t s_cid[kK];
+    __shared__ float s_cq[kK], s_cadj[kK];
 
     // 1. acceptance tests, one lane per position
     if (tid < kWave) {
@@ -227,143 +320,174 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(VerifyParams p) {
             const int64_t row = (int64_t)b * (L + 1) + lane;
             if (x >= 0 && (int64_t)x < p.V) {
                 if constexpr (SAMPLED) {
-                    const float *rs = p.row_stat + row * 4;
+                    float m, Z;
+                    verify_row_mz(p, row, &m, &Z);
                     const float zx = logit_elem<BF16>(p.logits + row * p.ld * es, x);
-                    const float px = exp2_rel(zx, rs[0], p.scale) / rs[1];
+                    const float px = exp2_rel(zx, m, p.scale) / Z;
                     acc = p.u_acc[bt] * p.q[bt * kK + slot] < px;
                 } else {
-                    acc = (uint32_t)x == __float_as_uint(p.row_stat[row * 4 + 2]);
+                    acc = (uint32_t)x == verify_row_argmax(p, row);
                 }
             }
         }
         const uint64_t miss = ballot((int)lane < L && !acc);
         const int n = miss ? (int)__builtin_ctzll(miss) : L;
         if ((int)lane < n) p.out_tok[(int64_t)b * (L + 1) + lane] = x;
-        if (lane == 0) s_n = n;
+        if (lane == 0) {
+            s_n = n;
+            s_tok = 0x7FFFFFFF;
+            s_last = -1;
+            s_chunk = -1;
+            s_clast = -1;
+        }
     }
     __syncthreads();
     const int n = s_n;
     const int64_t row = (int64_t)b * (L + 1) + n;
     int32_t tok;
     if constexpr (!SAMPLED) {
-        tok = (int32_t)__float_as_uint(p.row_stat[row * 4 + 2]);
+        tok = (int32_t)verify_row_argmax(p, row);
     } else {
-        // 2. mass of every chunk of the draw's distribution
+        // 2. the draw's weights: w(v) = p(v), less q(v) (clamped at 0) at the
+        // candidates when position n was rejected.
         const bool residual = n < L;
-        const float m = p.row_stat[row * 4], Z = p.row_stat[row * 4 + 1], s = p.scale;
+        const float s = p.scale;
+        float m, Z;
+        verify_row_mz(p, row, &m, &Z);
         const char *rowp = p.logits + row * p.ld * es;
-        for (int c = tid; c < p.nchunk; c += 256) {
-            const float *cs = p.chunk_stat + (row * p.nchunk + c) * 2;
-            w[c] = cs[1] * exp2_rel(cs[0], m, s) / Z;
-        }
-        __syncthreads();
-        // residual: subtract min(p, q) of each candidate from its chunk, in
-        // candidate order (one thread, values gathered by 16 lanes)
-        int32_t cj = -1;
-        float qj = 0.0f, pj = 0.0f;
-        if (residual && tid < kK) {
-            const int64_t bt = (int64_t)b * L + n;
-            cj = p.cand_id[bt * kK + tid];
-            qj = p.q[bt * kK + tid];
-            if (cj >= 0 && (int64_t)cj < p.V) pj = exp2_rel(logit_elem<BF16>(rowp, cj), m, s) / Z;
-        }
-        if (residual && tid < kWave) {
-            for (int j = 0; j < kK; ++j) {
-                const int32_t c = __builtin_amdgcn_readlane(cj, j);
-                const float pq = __builtin_fminf(__uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(pj), j)),
-                                                 __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(qj), j)));
-                if (tid == 0 && c >= 0 && (int64_t)c < p.V) w[c / kVChunk] -= pq;
-            }
-        }
-        __syncthreads();
-        // 3. the chunk where u Z_r falls: thread i owns chunks [i per, (i+1) per)
-        const int per = (p.nchunk + 255) / 256;
-        const int c0 = tid * per, c1 = c0 + per < p.nchunk ? c0 + per : p.nchunk;
-        float mine = 0.0f;
-        int lastpos = -1;
-        for (int c = c0; c < c1; ++c) {
-            const float v = w[c] > 0.0f ? w[c] : 0.0f;
-            mine += v;
-            if (v > 0.0f) lastpos = c;
-        }
-        float Zr;
-        const float before = block_exclusive_scan(mine, &Zr, lds4);
-        const float tau = p.u_res[b] * Zr;
-        if (tid == 0) {
-            s_k = 0x7FFFFFFF;
-            s_last = -1;
-        }
-        __syncthreads();
-        float cum = before;
-        for (int c = c0; c < c1; ++c) {
-            const float v = w[c] > 0.0f ? w[c] : 0.0f;
-            if (tau < cum + v) {
-                atomicMin(&s_k, c);
-                break;
-            }
-            cum += v;
-        }
-        atomicMax(&s_last, lastpos);
-        __syncthreads();
-        int k = s_k != 0x7FFFFFFF ? s_k : s_last;  // past the total (rounding): the last chunk with mass
-        if (k < 0) k = 0;
-        __syncthreads();  // everyone has read s_k / s_last before they are reused
-        // cumulative mass before chunk k (the owner of k recomputes it)
-        if (k >= c0 && k < c1) {
-            float cb = before;
-            for (int c = c0; c < k; ++c) cb += w[c] > 0.0f ? w[c] : 0.0f;
-            s_cbefore = cb;
-        }
-        if (tid == 0) {
-            s_tok = 0x7FFFFFFF;
-            s_last = -1;
-        }
-        __syncthreads();
-        // 4. scan chunk k: thread i takes tokens k 2048 + 8 i .. + 7
-        float wv[8];
-        float tsum = 0.0f;
-        int tlast = -1;
-        const int64_t v0 = (int64_t)k * kVChunk + 8 * tid;
-        int32_t cand[kK];
-        float candq[kK];
-        if (residual) {
-            const int64_t bt = (int64_t)b * L + n;
-#pragma unroll
-            for (int j = 0; j < kK; ++j) {
-                cand[j] = p.cand_id[bt * kK + j];
-                candq[j] = p.q[bt * kK + j];
-            }
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int64_t v = v0 + e;
-            float x = 0.0f;
-            if (v < p.V) {
-                x = exp2_rel(logit_elem<BF16>(rowp, v), m, s) / Z;
-                if (residual) {
-#pragma unroll
-                    for (int j = 0; j < kK; ++j)
-                        if (cand[j] == v) x -= candq[j];
-                    x = x > 0.0f ? x : 0.0f;
+        if (tid < kK) {
+            int32_t c = -1;
+            float qc = 0.0f, adj = 0.0f;
+            if (residual) {
+                const int64_t bt = (int64_t)b * L + n;
+                c = p.cand_id[bt * kK + tid];
+                qc = p.q[bt * kK + tid];
+                for (int j = 0; j < tid; ++j)  // a repeated id takes the first slot's q
+                    if (p.cand_id[bt * kK + j] == c) c = -1;
+                if (c >= 0 && (int64_t)c < p.V) {
+                    const float pc = exp2_rel(logit_elem<BF16>(rowp, c), m, s) / Z;
+                    adj = __builtin_fmaxf(pc - qc, 0.0f) - pc;
+                } else {
+                    c = -1;
                 }
             }
-            wv[e] = x;
-            tsum += x;
-            if (x > 0.0f) tlast = (int)e;
+            s_cid[tid] = c;
+            s_cq[tid] = qc;
+            s_cadj[tid] = adj;
         }
-        float dummy;
-        float cum2 = s_cbefore + block_exclusive_scan(tsum, &dummy, lds4);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if (tau < cum2 + wv[e]) {
-                atomicMin(&s_tok, (int)(v0 + e));
-                break;
-            }
-            cum2 += wv[e];
-        }
-        if (tlast >= 0) atomicMax(&s_last, (int)(v0 + tlast));
         __syncthreads();
-        tok = s_tok != 0x7FFFFFFF ? s_tok : s_last;  // past the chunk's mass (rounding): its last token with mass
+        // chunk masses from the chunk statistics; thread i owns the contiguous
+        // chunks [i cpt, (i + 1) cpt)
+        const int cpt = (p.nchunk + 255) >> 8;
+        const int ca = tid * cpt, cb = ca + cpt < p.nchunk ? ca + cpt : p.nchunk;
+        uint32_t cmask = 0;
+#pragma unroll
+        for (int j = 0; j < kK; ++j)
+            if (s_cid[j] >= 0 && s_cid[j] / CT >= ca && s_cid[j] / CT < cb) cmask |= 1u << j;
+        const float2 *cs = p.chunk + row * p.nchunk;
+        auto cmass = [&](int c) {
+            const float2 st = cs[c];
+            float w = st.y * exp2_rel(st.x, m, s) / Z;
+            for (uint32_t mk = cmask; mk; mk &= mk - 1) {
+                const int j = __builtin_ctz(mk);
+                if (s_cid[j] / CT == c) w += s_cadj[j];
+            }
+            return w > 0.0f ? w : 0.0f;
+        };
+        float mine = 0.0f;
+        int lastc = -1;
+        for (int c = ca; c < cb; ++c) {
+            const float w = cmass(c);
+            mine += w;
+            if (w > 0.0f) lastc = c;
+        }
+        float lo, hi, Zr;
+        block_scan_edges(mine, &lo, &hi, &Zr, lds4);
+        const float tau = p.u_res[b] * Zr;
+        if (lastc >= 0) atomicMax(&s_clast, lastc);
+        if (tau >= lo && tau < hi) {  // exactly one thread
+            float cum = lo;
+            int pick = -1;
+            float off = __builtin_inff();
+            for (int c = ca; c < cb; ++c) {
+                const float w = cmass(c);
+                if (w > 0.0f && tau < cum + w) {
+                    pick = c;
+                    off = tau - cum;
+                    break;
+                }
+                cum += w;
+            }
+            s_chunk = pick >= 0 ? pick : lastc;  // the rescan rounds differently: last chunk with mass
+            s_off = off;
+        }
+        __syncthreads();
+        int ch = s_chunk;
+        float target = s_off;
+        if (ch < 0) {  // u Z rounded up to the total: the last chunk with mass
+            ch = s_clast;
+            target = __builtin_inff();
+        }
+        if (ch < 0) {
+            tok = -1;  // no token has mass
+        } else {
+            // 3. the chunk's tokens, one vector per thread
+            const int64_t nfull = p.V / EPV;
+            const int tail = (int)(p.V - nfull * EPV);
+            const int64_t vi = (int64_t)ch * kVChunkVecs + tid;
+            const int64_t t0 = vi * EPV;
+            float x[EPV];
+            int cnt = 0;
+            if (vi < nfull) {
+                widen_vec<BF16>(*((const u32x4 *)rowp + vi), x);
+                cnt = EPV;
+            } else if (vi == nfull && tail) {
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) x[e] = e < tail ? logit_elem<BF16>(rowp, t0 + e) : -__builtin_inff();
+                cnt = tail;
+            }
+            uint32_t tmask = 0;
+#pragma unroll
+            for (int j = 0; j < kK; ++j)
+                if (cnt && s_cid[j] >= t0 && s_cid[j] < t0 + cnt) tmask |= 1u << j;
+            float w[EPV];
+            float ms = 0.0f;
+            int lastpos = -1;
+#pragma unroll
+            for (int e = 0; e < EPV; ++e) {
+                float we = 0.0f;
+                if (e < cnt) {
+                    we = exp2_rel(x[e], m, s) / Z;
+                    for (uint32_t mk = tmask; mk; mk &= mk - 1) {
+                        const int j = __builtin_ctz(mk);
+                        if (s_cid[j] == t0 + e) {
+                            const float d = we - s_cq[j];
+                            we = d > 0.0f ? d : 0.0f;
+                        }
+                    }
+                }
+                w[e] = we;
+                ms += we;
+                if (we > 0.0f) lastpos = (int)(t0 + e);
+            }
+            float lo2, hi2, tot2;
+            block_scan_edges(ms, &lo2, &hi2, &tot2, lds4);
+            if (lastpos >= 0) atomicMax(&s_last, lastpos);
+            if (target >= lo2 && target < hi2) {  // exactly one thread
+                float cum = lo2;
+                int pick = -1;
+#pragma unroll
+                for (int e = 0; e < EPV; ++e) {
+                    if (pick < 0 && w[e] > 0.0f && target < cum + w[e]) pick = (int)(t0 + e);
+                    cum += w[e];
+                }
+                s_tok = pick >= 0 ? pick : lastpos;  // the rescan rounds differently
+            }
+            __syncthreads();
+            // target past the chunk's total (rounding): its last token with mass
+            tok = s_tok != 0x7FFFFFFF ? s_tok : s_last;
+            if (tok < 0) tok = (int32_t)(ch * (int64_t)CT);  // the chunk's tokens all round to 0
+        }
     }
     if (tid == 0) {
         p.out_tok[(int64_t)b * (L + 1) + n] = tok;
@@ -372,10 +496,14 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(VerifyParams p) {
     for (int t = n + 1 + tid; t <= L; t += 256) p.out_tok[(int64_t)b * (L + 1) + t] = -1;
 }
 
+// Partials [rows][kVMaxSplit] and chunk statistics [rows][ceil(V / 1024)]
+// (the fp32 chunk, the smaller of the two chunk sizes).
+inline size_t verify_part_bytes(int64_t batch, int64_t block) {
+    return (size_t)(batch * (block + 1)) * kVMaxSplit * sizeof(VerifyPart);
+}
 inline size_t verify_workspace_bytes(int64_t batch, int64_t block, int64_t vocab) {
-    const int64_t rows = batch * (block + 1);
-    const int64_t nchunk = (vocab + kVChunk - 1) / kVChunk;
-    return (size_t)rows * 4 * sizeof(float) + (size_t)rows * nchunk * 2 * sizeof(float);
+    const int64_t nchunk = (vocab + kVChunkVecs * 4 - 1) / (kVChunkVecs * 4);
+    return verify_part_bytes(batch, block) + (size_t)(batch * (block + 1) * nchunk) * sizeof(float2);
 }
 
 }  // namespace dsel

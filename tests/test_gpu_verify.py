@@ -10,7 +10,7 @@ p_t(x) and the draw's CDF in fp32, the oracle in fp64.  A decision may differ
 only where the oracle's own margin is within the fp32 error:
   * acceptance  |u q - p| <= 1e-5 u q  (p in fp32: a few ulp of exp2 and of Z),
   * draw        distance of u Z to the nearest CDF edge <= 1e-5 Z (fp32 sums of
-                2048-token chunks and of the chunk prefix).
+                a few hundred tokens per thread and a 256-wide prefix).
 Such steps are counted; the test then continues from the GPU's decision
 (teacher forcing) and checks that a flagged draw is still a valid one: the
 GPU's token's fp64 CDF interval must contain u Z within that tolerance."""
