@@ -78,6 +78,25 @@ __device__ __forceinline__ float key_threshold(uint64_t k) {
     return __uint_as_float(b);
 }
 
+// Lane-wise signed 16-bit max of two words (v_pk_max_i16).  Read as int16, the
+// bits of non-negative bf16 values order like the values, and every negative
+// value (sign bit set) lies below them; so for a threshold t > 0, "some bf16 of
+// these words is >= t" becomes "some int16 half of their pk_max is >= bits(t)",
+// with no unpacking.  (Positive NaNs also pass; callers re-check exactly.)
+typedef short short2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_max_i16(uint32_t a, uint32_t b) {
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(short2v, a),
+                                                                  __builtin_bit_cast(short2v, b)));
+}
+__device__ __forceinline__ uint32_t bf16x8_pk_max(const u32x4 &w) {
+    return pk_max_i16(pk_max_i16(w.x, w.y), pk_max_i16(w.z, w.w));
+}
+// Both halves hold bits(t) - 1 for a bf16 value t > 0: pk_max_i16(m, floor) !=
+// floor exactly when a half of m is >= bits(t).
+__device__ __forceinline__ uint32_t bf16_pk_floor(float t) {
+    return ((__float_as_uint(t) >> 16) - 1u) * 0x10001u;
+}
+
 // Bitonic sort of one 64-bit key per lane across the wave, descending
 // (lane 0 receives the largest key).
 __device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t key) {

@@ -28,6 +28,10 @@ inline dsel_status launch(const void *kernel, dim3 grid, dim3 block, void *arg, 
     return e == hipSuccess ? DSEL_OK : DSEL_E_HIP;
 }
 
+#ifndef DSEL_VERIFY_WGS
+#define DSEL_VERIFY_WGS 2048
+#endif
+
 #ifndef DSEL_TOPK_UNROLL
 #define DSEL_TOPK_UNROLL 4
 #endif
@@ -398,7 +402,7 @@ DSEL_API dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64
     // in all (8 per CU), at most kVMaxSplit, none of them empty
     const int64_t chunk_tokens = (int64_t)kVChunkVecs * (bf ? 8 : 4);
     p.nchunk = (int)((vocab + chunk_tokens - 1) / chunk_tokens);
-    int64_t ns = (2048 + rows - 1) / rows;
+    int64_t ns = (DSEL_VERIFY_WGS + rows - 1) / rows;
     ns = ns < 1 ? 1 : ns > kVMaxSplit ? kVMaxSplit : ns;
     ns = ns < p.nchunk ? ns : p.nchunk;
     p.cps = (int)((p.nchunk + ns - 1) / ns);

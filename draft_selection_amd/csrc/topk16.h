@@ -153,9 +153,23 @@ __device__ __forceinline__ void chunk_offer(WaveTop &st, const u32x4 (&w)[U], in
 
 // Filter one chunk: a single compare of the lane's chunk maximum screens out
 // (almost) every chunk once the list has filled.
+// For bf16 rows with a positive threshold the screen works on the packed bits
+// (pk_max_i16); a clamped duplicate vector past the range can only cause an
+// extra exact pass, which checks each element's range itself.
 template <bool BF16, int U>
 __device__ __forceinline__ void chunk_filter(WaveTop &st, const u32x4 (&w)[U], int64_t v0, int64_t ve,
                                              int64_t h0) {
+    if constexpr (BF16) {
+        if (st.thr_f > 0.0f) {  // wave-uniform; thr_f is itself a bf16 value
+            const uint32_t floor = bf16_pk_floor(st.thr_f);
+            uint32_t m = floor;
+#pragma unroll
+            for (int u = 0; u < U; ++u) m = pk_max_i16(m, bf16x8_pk_max(w[u]));
+            if (ballot(m != floor) == 0) return;
+            chunk_offer<BF16, U>(st, w, v0, ve, h0, -1);
+            return;
+        }
+    }
     const float m = chunk_max<BF16, U>(w, v0, ve);
     if (ballot(!(m < st.thr_f)) == 0) return;
     chunk_offer<BF16, U>(st, w, v0, ve, h0, -1);

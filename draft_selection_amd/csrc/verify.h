@@ -37,8 +37,11 @@
 namespace dsel {
 
 constexpr int64_t kVMaxVocab = 1 << 22;  // 4,194,304 tokens
-constexpr int kVU = 4;                   // 16-byte vectors per lane per chunk
-constexpr int kVChunkVecs = kWave * kVU; // 256 vectors per chunk
+#ifndef DSEL_VERIFY_U
+#define DSEL_VERIFY_U 4
+#endif
+constexpr int kVU = DSEL_VERIFY_U;       // 16-byte vectors per lane per chunk
+constexpr int kVChunkVecs = kWave * kVU; // vectors per chunk
 constexpr int kVMaxSplit = 16;           // workgroups per row, at most
 
 // One workgroup's partial result for its slice of a row.
@@ -148,6 +151,7 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(VerifyParams p) {
 
     float bv = -__builtin_inff();  // greedy: the lane's best value and key
     uint64_t bkey = 0;
+    float wbv = -__builtin_inff();  // greedy: the wave's best value (max of bv)
     float wm = -__builtin_inff(), wz = 0.0f;  // sampled: the wave's running max and sum
 
     u32x4 cur[kVU], nxt[kVU];
@@ -155,55 +159,91 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(VerifyParams p) {
     if (c < c1) verify_load_chunk(cur, vb, c, nfull);
     for (; c < c1; c += 4) {
         verify_load_chunk(nxt, vb, c + 4 < c1 ? c + 4 : c, nfull);
-        float x[kVU][EPV];
-        int cnt[kVU];
-#pragma unroll
-        for (int u = 0; u < kVU; ++u) {
-            const int64_t vi = (int64_t)c * kVChunkVecs + u * kWave + lane;
-            widen_vec<BF16>(cur[u], x[u]);
-            cnt[u] = vi < nfull ? EPV : (vi == nfull ? tail : 0);
-            if (vi == nfull && tail) {  // the partial last vector, element by element
-#pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    x[u][e] = e < tail ? logit_elem<BF16>(rowp, nfull * EPV + e) : -__builtin_inff();
-            }
-        }
         if constexpr (!SAMPLED) {
+            // screen: can any element of the lane's chunk reach the wave's best
+            // so far (wbv, wave-uniform)?  Nothing below it can be the row's
+            // arg max, so lanes skip it even when it beats their own best.
+            bool pass;
+            if (BF16 && wbv > 0.0f) {  // on the packed bits (wbv is a bf16 value)
+                const uint32_t floor = bf16_pk_floor(wbv);
+                uint32_t m = floor;
 #pragma unroll
-            for (int u = 0; u < kVU; ++u) {
-                float vm = -__builtin_inff();
+                for (int u = 0; u < kVU; ++u) m = pk_max_i16(m, bf16x8_pk_max(cur[u]));
+                pass = m != floor;
+            } else {
+                float cm = -__builtin_inff();
 #pragma unroll
-                for (int e = 0; e < EPV; ++e) vm = __builtin_fmaxf(vm, x[u][e]);
-                // NaN (v_max drops it only when the other operand is a number),
-                // ties and the first vector go to the exact compare
-                if (cnt[u] && (!(vm < bv) || bkey == 0 || vm != vm)) {
-                    const int64_t id0 = ((int64_t)c * kVChunkVecs + u * kWave + lane) * EPV;
+                for (int u = 0; u < kVU; ++u) {
+                    float x[EPV];
+                    widen_vec<BF16>(cur[u], x);
 #pragma unroll
-                    for (int e = 0; e < EPV; ++e) {
-                        if (e < cnt[u]) {
-                            const uint64_t k = cand_key(x[u][e], (uint32_t)(id0 + e));
-                            if (k > bkey) {
-                                bkey = k;
-                                bv = x[u][e] == x[u][e] ? x[u][e] : bv;
-                            }
+                    for (int e = 0; e < EPV; ++e) cm = __builtin_fmaxf(cm, x[e]);
+                }
+                // ties, the first chunk (wbv = -inf) and NaN-only chunks pass;
+                // v_max drops a NaN beside a number, and a NaN never beats a
+                // real key
+                pass = !(cm < wbv) || cm != cm;
+            }
+            // the row's partial last vector always takes the exact compare
+            const int64_t vt = nfull - (int64_t)c * kVChunkVecs;  // its place in this chunk
+            if (tail && vt >= 0 && vt < kVChunkVecs && (int64_t)(vt % kWave) == (int64_t)lane) pass = true;
+            if (ballot(pass)) {
+                if (pass) {
+#pragma unroll
+                    for (int u = 0; u < kVU; ++u) {
+                        const int64_t vi = (int64_t)c * kVChunkVecs + u * kWave + lane;
+                        const int cnt = vi < nfull ? EPV : (vi == nfull ? tail : 0);
+                        float x[EPV];
+                        if (vi < nfull) {
+                            widen_vec<BF16>(cur[u], x);
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < EPV; ++e)
+                                x[e] = e < cnt ? logit_elem<BF16>(rowp, nfull * EPV + e) : -__builtin_inff();
+                        }
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e) {
+                            const uint64_t k = cand_key(x[e], (uint32_t)(vi * EPV + e));
+                            const bool better = e < cnt && k > bkey;
+                            bkey = better ? k : bkey;
+                            bv = better && x[e] == x[e] ? x[e] : bv;
                         }
                     }
                 }
+                wbv = wave_max_f(bv);
             }
         } else {
+            // x = -inf stands for "no element": it leaves the max alone and
+            // adds exp2(-inf) = 0 to the sum, so only the row's last chunk
+            // (clamped vectors, the partial vector) needs per-vector care.
+            float x[kVU][EPV];
+#pragma unroll
+            for (int u = 0; u < kVU; ++u) widen_vec<BF16>(cur[u], x[u]);
+            if (c == p.nchunk - 1) {  // wave-uniform
+#pragma unroll
+                for (int u = 0; u < kVU; ++u) {
+                    const int64_t vi = (int64_t)c * kVChunkVecs + u * kWave + lane;
+                    const int cnt = vi < nfull ? EPV : (vi == nfull ? tail : 0);
+                    if (cnt < EPV) {
+#pragma unroll
+                        for (int e = 0; e < EPV; ++e)
+                            x[u][e] = e < cnt ? logit_elem<BF16>(rowp, nfull * EPV + e) : -__builtin_inff();
+                    }
+                }
+            }
             float lm = -__builtin_inff();
 #pragma unroll
             for (int u = 0; u < kVU; ++u)
 #pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    if (e < cnt[u]) lm = __builtin_fmaxf(lm, x[u][e]);
+                for (int e = 0; e < EPV; ++e) lm = __builtin_fmaxf(lm, x[u][e]);
             const float mc = wave_max_f(lm);
             float ls = 0.0f;
+            if (mc != -__builtin_inff()) {  // wave-uniform; then x = -inf gives exp2(-inf) = 0
 #pragma unroll
-            for (int u = 0; u < kVU; ++u)
+                for (int u = 0; u < kVU; ++u)
 #pragma unroll
-                for (int e = 0; e < EPV; ++e)
-                    if (e < cnt[u]) ls += exp2_rel(x[u][e], mc, s);
+                    for (int e = 0; e < EPV; ++e) ls += __builtin_amdgcn_exp2f((x[u][e] - mc) * s);
+            }
             const float zc = wave_sum_f(ls);
             if (lane == 0) p.chunk[row * p.nchunk + c] = make_float2(mc, zc);
             const float nm = __builtin_fmaxf(wm, mc);
