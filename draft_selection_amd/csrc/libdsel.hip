@@ -158,7 +158,7 @@ DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t
     p.A_prev = A_prev;
     p.G = G;
     p.part = (float *)workspace;
-    const int BN = r % 256 == 0 ? 256 : r % 128 == 0 ? 128 : r % 64 == 0 ? 64 : 32;
+    const int BN = gate_bn(r);
     p.nside = (int)(r / BN);
     p.mt_gate = (int)((batch * block + 127) / 128);
     p.mt_ver = (int)((batch + 127) / 128);

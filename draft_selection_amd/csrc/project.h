@@ -31,11 +31,21 @@
 // blocks.
 #pragma once
 
+#include <type_traits>
+
 #include "common.h"
 
 namespace dsel {
 
 constexpr int kBK = 64;  // K elements per step (128 bytes per row)
+
+// Fragment reads of the next step issued after each MFMA of the current one:
+// 2 front-loads them into the first half of the step, so they have landed
+// well before the wait at the next barrier.
+#ifndef DSEL_MMA_RPM
+#define DSEL_MMA_RPM 2
+#endif
+constexpr int RPM = DSEL_MMA_RPM;
 
 
 // BM x BN tile computed by GM x GN waves, each owning WM x WN as 32 x 32 MFMA
@@ -73,10 +83,12 @@ __device__ __forceinline__ void wg_barrier() { asm volatile("s_barrier" ::: "mem
 // read; the main loop has no other vector-memory loads and does its own waits.
 __device__ __forceinline__ void lds_dma16(const void *src, uint16_t *lds_base) {
     const uint32_t m0v = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void *)lds_base;
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+    // m0 (the LDS destination base) is an input operand, so the compiler
+    // loads it and knows its value
+    asm volatile("global_load_lds_dwordx4 %1, off"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(m0v)), "v"(src)
-                 : "memory", "m0");
+                 : "{m0}"(__builtin_amdgcn_readfirstlane(m0v)), "v"(src)
+                 : "memory");
 }
 
 // s_waitcnt vmcnt(N) lgkmcnt(0): own LDS reads done and all but the last N
@@ -89,13 +101,14 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 
 // acc += X * W^T over K steps [k0, k1) (64-deep steps), k1 > k0.
 //
-// Schedule of one step (four 16-deep slices): while slice s multiplies, the
-// fragments of slice s+1 are read from LDS into the other register buffer.  At
-// the last slice the wave first waits for its own reads and for its DMA of the
-// next step, then meets the others at the barrier (after which every wave is
-// done with this stage and the next stage is complete), refills this stage
-// three steps ahead and reads the first fragments of the next step, all ahead
-// of the last slice's MFMAs, so no LDS latency is exposed at a step boundary.
+// Schedule of one step kt: the wave waits for its own LDS reads of step kt
+// (issued one step earlier) and its own DMA of step kt+1, then meets the
+// others at the barrier: after it nobody reads step kt's stage any more and
+// step kt+1 is complete in LDS.  It refills kt's stage with step kt+3, issues
+// all fragment reads of step kt+1 (KS x (TM + TN) ds_read_b128, into the other
+// register set) and runs the MFMAs of step kt from registers while they fly.
+// Keeping a whole step of reads in flight is what lets LDS reach its streaming
+// rate; one slice at a time leaves it latency-bound.
 template <class T>
 __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DXI], const uint16_t *wbase,
                                              int64_t wstride, int k0, int k1, uint16_t *Xs,
@@ -137,49 +150,87 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
         _Pragma("unroll") for (int u = 0; u < WI; ++u)                                         \
             lds_dma16(wsrc[u] + kk_, Ws + (stage) * BN * kBK + (8 * (wave + NW * u)) * kBK);   \
     } while (0)
-#define DSEL_FRAG(buf, xb_, wb_, s_)                                                           \
+#define DSEL_READ_STEP(set, stage)                                                             \
     do {                                                                                       \
-        const int ch_ = (((s_) * 2 + fk) ^ rsw) << 3;                                          \
-        _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                      \
-            a[buf][i] = *(const bf16x8 *)((xb_) + aoff[i] + ch_);                              \
-        _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                      \
-            b[buf][j] = *(const bf16x8 *)((wb_) + boff[j] + ch_);                              \
+        const uint16_t *xb_ = Xs + (stage) * BM * kBK, *wb_ = Ws + (stage) * BN * kBK;         \
+        _Pragma("unroll") for (int s_ = 0; s_ < KS; ++s_) {                                    \
+            const int ch_ = ((s_ * 2 + fk) ^ rsw) << 3;                                        \
+            _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                  \
+                fa[set][s_][i] = *(const bf16x8 *)(xb_ + aoff[i] + ch_);                       \
+            _Pragma("unroll") for (int j = 0; j < T::TN; ++j)                                  \
+                fb[set][s_][j] = *(const bf16x8 *)(wb_ + boff[j] + ch_);                       \
+        }                                                                                      \
     } while (0)
-
-    bf16x8 a[2][T::TM], b[2][T::TN];
+    bf16x8 fa[2][KS][T::TM], fb[2][KS][T::TN];
+    // DMA load q of a step (q < XI: X rows, then W rows) into stage `stage`
+    auto dma = [&](int q, int kk, int stage) {
+        if (q < XI) lds_dma16(xsrc[q] + kk, Xs + stage * BM * kBK + (8 * (wave + NW * q)) * kBK);
+        else lds_dma16(wsrc[q - XI] + kk, Ws + stage * BN * kBK + (8 * (wave + NW * (q - XI))) * kBK);
+    };
+    // One step kt whose fragments are in register set SET: the MFMAs of kt
+    // with the fragment reads of kt+1 (from the next stage) interleaved one or
+    // two per MFMA, so the matrix pipe starts at once and LDS serves a steady
+    // stream rather than a burst from every wave right after the barrier; the
+    // DMA of kt+3 into kt's stage goes out one load per MFMA from the first.
+    // (Past the last step the reads fetch a stale stage into the unused set:
+    // in bounds and harmless.)
+    // fragment read rr of a step: slice rr / (TM + TN), then its A fragments
+    // and its B fragments
+    constexpr int NR = KS * (T::TM + T::TN);
+    auto frag_read = [&](int rr, const uint16_t *xb, const uint16_t *wb, auto setc) {
+        constexpr int S2 = decltype(setc)::value;
+        const int s_ = rr / (T::TM + T::TN), f = rr % (T::TM + T::TN);
+        const int ch = ((s_ * 2 + fk) ^ rsw) << 3;
+        if (f < T::TM) fa[S2][s_][f] = *(const bf16x8 *)(xb + aoff[f] + ch);
+        else fb[S2][s_][f - T::TM] = *(const bf16x8 *)(wb + boff[f - T::TM] + ch);
+    };
+    int cur = 0;
+    auto step = [&](int kt, auto setc) {
+        constexpr int SET = decltype(setc)::value;
+        wait_vmcnt_lgkm0<PER>();  // own reads of kt done, own DMA of kt+1 landed
+        wg_barrier();             // everyone's: kt's stage is free, kt+1 is complete
+        __builtin_amdgcn_sched_barrier(0);
+        const int nxt = cur == NS - 1 ? 0 : cur + 1;
+        const uint16_t *xb = Xs + nxt * BM * kBK, *wb = Ws + nxt * BN * kBK;
+        const int kk = (kt + 3 < k1 ? kt + 3 : k1 - 1) * kBK;
+        constexpr int NMF = KS * T::TM * T::TN;
+#pragma unroll
+        for (int s_ = 0; s_ < KS; ++s_) {
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j) {
+                    const int q = (s_ * T::TM + i) * T::TN + j;
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[SET][s_][i], fb[SET][s_][j],
+                                                                        acc[i][j], 0, 0, 0);
+#pragma unroll
+                    for (int rr = q * RPM; rr < (q + 1) * RPM; ++rr)
+                        if (rr < NR) frag_read(rr, xb, wb, std::integral_constant<int, SET ^ 1>());
+                    if (q < PER) dma(q, kk, cur);
+                    __builtin_amdgcn_sched_barrier(0);  // keep this order
+                }
+        }
+#pragma unroll
+        for (int rr = NMF * RPM; rr < NR; ++rr) frag_read(rr, xb, wb, std::integral_constant<int, SET ^ 1>());
+#pragma unroll
+        for (int q = NMF; q < PER; ++q) dma(q, kk, cur);
+        cur = nxt;
+    };
     DSEL_ISSUE(k0, 0);
     DSEL_ISSUE(k0 + 1, 1);
     DSEL_ISSUE(k0 + 2, 2);
     wait_vmcnt<2 * PER>();
     wg_barrier();
-    DSEL_FRAG(0, Xs, Ws, 0);
-    int cur = 0;
-    for (int kt = k0; kt < k1; ++kt) {
-        const int nxt = cur == NS - 1 ? 0 : cur + 1;
-        const uint16_t *xb = Xs + cur * BM * kBK;
-        const uint16_t *wb = Ws + cur * BN * kBK;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-            const int c = s & 1, n = c ^ 1;
-            if (s + 1 < KS) {
-                DSEL_FRAG(n, xb, wb, s + 1);
-            } else {
-                wait_vmcnt_lgkm0<PER>();  // own reads of this stage done, own DMA of kt+1 landed
-                wg_barrier();             // everyone's: the stage is free, step kt+1 is complete
-                DSEL_ISSUE(kt + 3, cur);
-                DSEL_FRAG(n, Xs + nxt * BM * kBK, Ws + nxt * BN * kBK, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
-        }
-        cur = nxt;
+    DSEL_READ_STEP(0, 0);
+    for (int kt = k0; kt < k1; kt += 2) {
+        step(kt, std::integral_constant<int, 0>());
+        if (kt + 1 >= k1) break;
+        step(kt + 1, std::integral_constant<int, 1>());
     }
     wait_vmcnt<0>();  // drain the redundant tail loads before LDS is released
 #undef DSEL_ISSUE
-#undef DSEL_FRAG
+#undef DSEL_READ_STEP
+#undef DSEL_STEP
 }
 
 // Valid-row mask of a BM-row tile, shared through LDS.  Rows are loaded by
@@ -222,11 +273,18 @@ struct CandParams {
 // Column tile BN of one side: BN = 256 on 8 waves (2 x 4, wave tile 64 x 64:
 // two waves per SIMD hide each other's LDS latency), BN = 128 and 64 on 4 waves
 // (2 x 2), BN = 32 on 4 waves (4 x 1).
+#ifndef DSEL_CAND_XCD_SIDE
+#define DSEL_CAND_XCD_SIDE 0
+#endif
+#ifndef DSEL_CAND_GM256
+#define DSEL_CAND_GM256 2
+#endif
 #ifndef DSEL_CAND_GN256
 #define DSEL_CAND_GN256 4
 #endif
 template <int BN>
-using CandTile = TileShape<128, BN, (BN == 32 ? 4 : 2), (BN == 32 ? 1 : BN == 256 ? DSEL_CAND_GN256 : 2)>;
+using CandTile = TileShape<128, BN, (BN == 32 ? 4 : BN == 256 ? DSEL_CAND_GM256 : 2),
+                           (BN == 32 ? 1 : BN == 256 ? DSEL_CAND_GN256 : 2)>;
 inline int tile_threads(int BN) {
     return BN == 256 ? CandTile<256>::NT : BN == 128 ? CandTile<128>::NT : BN == 64 ? CandTile<64>::NT
                                                                                  : CandTile<32>::NT;
@@ -249,11 +307,19 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
     const int ks = (int)(blockIdx.x / per_split);
     const int w = (int)(blockIdx.x % per_split);
     const int xcd = w & 7, slot = w >> 3;
+#if DSEL_CAND_XCD_SIDE
+    // XCDs 0-3 take side 0, 4-7 side 1: each L2 holds one W
+    const int side = xcd >> 2;
+    const int mt = (slot / p.nside) * 4 + (xcd & 3);
+    const int n0 = (slot % p.nside) * BN;
+    const int ct = side * p.nside + slot % p.nside;
+#else
     const int ct = slot % ncol;
     const int mt = (slot / ncol) * 8 + xcd;
-    if (mt >= p.mt) return;
     const int side = ct / p.nside;  // 0: W_A, 1: W_B
     const int n0 = (ct % p.nside) * BN;
+#endif
+    if (mt >= p.mt) return;
     const int64_t m0 = (int64_t)mt * BM;
     const int tid = threadIdx.x;
     const int d = p.d, r = p.r;
@@ -522,15 +588,31 @@ __global__ __launch_bounds__(256) void project_gate_reduce_kernel(GateParams p) 
     }
 }
 
-// K splits of the gate job and the workspace they need.
+// Column tile of the gate job: the largest of 256, 128, 64, 32 that divides r
+// and is at most DSEL_GATE_BN (narrow tiles give this short GEMM more
+// workgroups).
+#ifndef DSEL_GATE_BN
+#define DSEL_GATE_BN 256
+#endif
+inline int gate_bn(int64_t r) {
+    for (int bn = 256; bn > 32; bn >>= 1)
+        if (bn <= DSEL_GATE_BN && r % bn == 0) return bn;
+    return 32;
+}
+
+// K splits of the gate job: enough workgroups to fill DSEL_GATE_TARGET_WG
+// slots, keeping at least DSEL_GATE_MIN_STEPS K steps per split.
 #ifndef DSEL_GATE_MIN_STEPS
 #define DSEL_GATE_MIN_STEPS 4
 #endif
+#ifndef DSEL_GATE_TARGET_WG
+#define DSEL_GATE_TARGET_WG 256
+#endif
 inline int gate_nsplit(int64_t batch, int64_t block, int64_t d, int64_t r) {
-    const int64_t BN = r % 256 == 0 ? 256 : r % 128 == 0 ? 128 : r % 64 == 0 ? 64 : 32;
+    const int64_t BN = gate_bn(r);
     const int64_t tiles = ((batch * block + 127) / 128 + (batch + 127) / 128) * (r / BN);
     const int64_t nk = d / kBK;
-    int64_t s = 256 / (tiles > 0 ? tiles : 1);
+    int64_t s = DSEL_GATE_TARGET_WG / (tiles > 0 ? tiles : 1);
     if (s > nk / DSEL_GATE_MIN_STEPS) s = nk / DSEL_GATE_MIN_STEPS;
     if (s < 1) s = 1;
     return (int)s;
