@@ -292,9 +292,12 @@ def main():
         if args.gate == "overlap":
             fork[0].record(strm)
             side.wait_event(fork[0])
-        s0 = lib.dsel_project_gate(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
-                                   P(d["verified"]), B, L, P(A_prev), P(G), P(pws), pwsb,
-                                   ss if args.gate == "overlap" else sp)
+        if args.gate == "overlap":
+            s0 = lib.dsel_project_gate_overlap(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
+                                               P(d["verified"]), B, L, P(A_prev), P(G), ss)
+        else:
+            s0 = lib.dsel_project_gate(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
+                                       P(d["verified"]), B, L, P(A_prev), P(G), P(pws), pwsb, sp)
         if args.gate == "overlap":
             fork[1].record(side)
         if ev is not None:

@@ -62,6 +62,7 @@ def _load():
             "dsel_project": ([P, I64, I64, P, P, P, I64, P, P, P, I64, I64, P, P, P, P, SZ, P], I32),
             "dsel_project_workspace_bytes": ([I64, I64, I64, I64], SZ),
             "dsel_project_gate": ([P, I64, I64, P, P, I64, P, P, I64, I64, P, P, P, SZ, P], I32),
+            "dsel_project_gate_overlap": ([P, I64, I64, P, P, I64, P, P, I64, I64, P, P, P], I32),
             "dsel_project_cand": ([P, I64, I64, P, P, I64, P, I64, I64, P, P, P, SZ, P], I32),
             "dsel_score_pairs": ([P, P, P, P, I64, I64, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_walk": ([P, I64, I64, C.POINTER(WalkArgs), P], I32),
@@ -212,6 +213,22 @@ def project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=None, stream=Non
     _check(st, "dsel_project_gate")
 
 
+def project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=None):
+    """project_gate with one workgroup per output tile and no workspace, for
+    running beside select_topk on another stream."""
+    V, d = E.shape
+    r = W_A.shape[0]
+    B, L = h.shape[:2]
+    for t, n, shp in ((E, "E", (V, d)), (W_A, "W_A", (r, d)), (W_H, "W_H", (r, d)), (h, "h", (B, L, d))):
+        _need(t, n, torch.bfloat16, shp)
+    _need(verified, "verified", torch.int32, (B,))
+    _need(A_prev, "A_prev", torch.float32, (B, L, K, r))
+    _need(G, "G", torch.float32, (B, L, r))
+    st = _load().dsel_project_gate_overlap(_ptr(E), V, d, _ptr(W_A), _ptr(W_H), r, _ptr(h), _ptr(verified),
+                                           B, L, _ptr(A_prev), _ptr(G), _stream(stream))
+    _check(st, "dsel_project_gate_overlap")
+
+
 def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=None, stream=None):
     """B_cur and the predecessor rows of A_prev for positions >= 1."""
     V, d = E.shape
@@ -350,8 +367,9 @@ def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
     """The whole selector: top-16, projections, pair scores and the fused walk.
 
     With ``overlap`` the gate GEMM (which needs no candidates) runs on a side
-    stream while the top-16 runs on the caller's stream; by default it runs
-    first, which measures faster on MI355X (the two contend for the CUs)."""
+    stream, one workgroup per output tile (dsel_project_gate_overlap), while
+    the top-16 runs on the caller's stream; otherwise it runs first, split
+    along d over the whole chip."""
     main = torch.cuda.current_stream() if stream is None else stream
     B, L = h.shape[:2]
     r = W_A.shape[0]
@@ -363,7 +381,7 @@ def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
     if overlap:
         side = side_stream(dev)
         side.wait_stream(main)
-        project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=ws, stream=side)
+        project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=side)
         cand_id, cand_u = select_topk(logits, vocab, stream=main)
         main.wait_stream(side)
     else:

@@ -130,18 +130,21 @@ DSEL_API size_t dsel_project_workspace_bytes(int64_t batch, int64_t block, int64
     return c ? cand_workspace_offset(batch, block, d, r) + c : gate_workspace_bytes(batch, block, d, r);
 }
 
-DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d,
-                                       const uint16_t *W_A, const uint16_t *W_H, int64_t r,
-                                       const uint16_t *h, const int32_t *verified, int64_t batch,
-                                       int64_t block, float *A_prev, float *G, void *workspace,
-                                       size_t workspace_bytes, dsel_stream_t stream) {
+namespace {
+
+// The gate job; `split` = false runs one workgroup per output tile with no
+// K split and no workspace.
+dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                              const uint16_t *W_H, int64_t r, const uint16_t *h, const int32_t *verified,
+                              int64_t batch, int64_t block, float *A_prev, float *G, void *workspace,
+                              size_t workspace_bytes, bool split, dsel_stream_t stream) {
     dsel_status st = check_project_common(E, vocab, d, r, batch, block);
     if (st != DSEL_OK || batch == 0) return st;
     if (!W_A || !W_H || !h || !verified || !A_prev || !G) return DSEL_E_ARG;
     if (!aligned(W_A, 16) || !aligned(W_H, 16) || !aligned(h, 16) || !aligned(verified, 4) ||
-        !aligned(A_prev, 4) || !aligned(G, 4))
+        !aligned(A_prev, 16) || !aligned(G, 16))
         return DSEL_E_ALIGN;
-    const size_t need = gate_workspace_bytes(batch, block, d, r);
+    const size_t need = split ? gate_workspace_bytes(batch, block, d, r) : 0;
     if (need && (!workspace || workspace_bytes < need)) return DSEL_E_WORKSPACE;
     if (need && !aligned(workspace, 16)) return DSEL_E_ALIGN;
     GateParams p;
@@ -158,11 +161,11 @@ DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t
     p.A_prev = A_prev;
     p.G = G;
     p.part = (float *)workspace;
-    const int BN = gate_bn(r);
+    const int BN = gate_bn(batch, block, r);
     p.nside = (int)(r / BN);
     p.mt_gate = (int)((batch * block + 127) / 128);
     p.mt_ver = (int)((batch + 127) / 128);
-    p.nsplit = gate_nsplit(batch, block, d, r);
+    p.nsplit = split ? gate_nsplit(batch, block, d, r) : 1;
     const int64_t grid = (int64_t)(p.mt_gate + p.mt_ver) * p.nside * p.nsplit;
     if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
     const void *k = BN == 256 ? (const void *)project_gate_kernel<256>
@@ -177,6 +180,25 @@ DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t
                   &p, 0, stream);
 }
 
+}  // namespace
+
+DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d,
+                                       const uint16_t *W_A, const uint16_t *W_H, int64_t r,
+                                       const uint16_t *h, const int32_t *verified, int64_t batch,
+                                       int64_t block, float *A_prev, float *G, void *workspace,
+                                       size_t workspace_bytes, dsel_stream_t stream) {
+    return project_gate_impl(E, vocab, d, W_A, W_H, r, h, verified, batch, block, A_prev, G, workspace,
+                             workspace_bytes, true, stream);
+}
+
+DSEL_API dsel_status dsel_project_gate_overlap(const uint16_t *E, int64_t vocab, int64_t d,
+                                               const uint16_t *W_A, const uint16_t *W_H, int64_t r,
+                                               const uint16_t *h, const int32_t *verified, int64_t batch,
+                                               int64_t block, float *A_prev, float *G, dsel_stream_t stream) {
+    return project_gate_impl(E, vocab, d, W_A, W_H, r, h, verified, batch, block, A_prev, G, nullptr, 0, false,
+                             stream);
+}
+
 DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d,
                                        const uint16_t *W_A, const uint16_t *W_B, int64_t r,
                                        const int32_t *cand_id, int64_t batch, int64_t block,
@@ -185,8 +207,8 @@ DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t
     dsel_status st = check_project_common(E, vocab, d, r, batch, block);
     if (st != DSEL_OK || batch == 0) return st;
     if (!W_A || !W_B || !cand_id || !A_prev || !B_cur) return DSEL_E_ARG;
-    if (!aligned(W_A, 16) || !aligned(W_B, 16) || !aligned(cand_id, 4) || !aligned(A_prev, 4) ||
-        !aligned(B_cur, 4))
+    if (!aligned(W_A, 16) || !aligned(W_B, 16) || !aligned(cand_id, 4) || !aligned(A_prev, 16) ||
+        !aligned(B_cur, 16))
         return DSEL_E_ALIGN;
     const size_t cneed = cand_workspace_bytes(batch, block, d, r);
     const size_t coff = cand_workspace_offset(batch, block, d, r);

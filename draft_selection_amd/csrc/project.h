@@ -255,6 +255,58 @@ __device__ __forceinline__ void tile_row_mask(uint32_t xok, uint16_t *lds) {
     __syncthreads();
 }
 
+// The accumulator layout of v_mfma_f32_32x32x16 gives lane l the column l % 32
+// of a 32 x 32 block, rows 8 g + 4 (l / 32) + e (element 4 g + e, e < 4): four
+// rows of one column per group g.  A 4 x 4 transpose inside each quad of lanes
+// (DPP quad permutes, two exchange stages) turns that into one row of four
+// consecutive columns per lane, so the epilogue stores 16 bytes per lane and
+// a quarter of the store instructions.  Lane 4 q + k then holds row
+// 8 g + 4 (l / 32) + k, columns 4 q .. 4 q + 3 of the block.
+__device__ __forceinline__ float dpp_quad_xor1(float x) {  // quad_perm [1, 0, 3, 2]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_quad_xor2(float x) {  // quad_perm [2, 3, 0, 1]
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ floatx4 quad_transpose4(float x0, float x1, float x2, float x3) {
+    const uint32_t k = lane_id() & 3u;
+    float x[4] = {x0, x1, x2, x3};
+#pragma unroll
+    for (int pr = 0; pr < 4; pr += 2) {  // exchange with lane k ^ 1: rows r and r ^ 1
+        const float recv = dpp_quad_xor1((k & 1u) ? x[pr] : x[pr + 1]);
+        if (k & 1u) x[pr] = recv;
+        else x[pr + 1] = recv;
+    }
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {  // exchange with lane k ^ 2: rows r and r ^ 2
+        const float recv = dpp_quad_xor2((k & 2u) ? x[pr] : x[pr + 2]);
+        if (k & 2u) x[pr] = recv;
+        else x[pr + 2] = recv;
+    }
+    return floatx4{x[0], x[1], x[2], x[3]};
+}
+
+// Hand every accumulator of the wave to `put(rl, cl, v)` as rows of four:
+// tile row rl, tile columns cl .. cl + 3 (cl a multiple of 4), values v.
+template <class T, class Put>
+__device__ __forceinline__ void for_tile_rows4(const floatx16 (&acc)[T::TM][T::TN], Put put) {
+    const uint32_t lane = lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / T::GNv, wn = wave % T::GNv;
+    const int rq = 4 * (int)(lane >> 5) + (int)(lane & 3);  // row within a group of 8
+    const int cq = (int)(lane & 31) & ~3;                   // first column of the quad
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const floatx4 v = quad_transpose4(acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                                                  acc[i][j][4 * g + 3]);
+                put(wm * T::WM + i * 32 + 8 * g + rq, wn * T::WN + j * 32 + cq, v);
+            }
+}
+
 struct CandParams {
     const uint16_t *E;
     int64_t V;
@@ -361,27 +413,14 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
 
     if (p.nsplit > 1) {
         // partial tile, row-major; validity and placement are the reduce's
-        const int wm = wave / T::GNv, wn = wave % T::GNv;
         float *tp = p.part + ((int64_t)ks * p.mt * ncol + (int64_t)mt * ncol + ct) * (BM * BN);
-#pragma unroll
-        for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int rl = wm * T::WM + i * 32 + 8 * (v >> 2) + 4 * (int)(lane >> 5) + (v & 3);
-#pragma unroll
-                for (int j = 0; j < T::TN; ++j)
-                    tp[rl * BN + wn * T::WN + j * 32 + (int)(lane & 31)] = acc[i][j][v];
-            }
+        for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) { *(floatx4 *)(tp + rl * BN + cl) = v; });
         return;
     }
 
     // Epilogue.  Row validity comes from the tile's mask; "position t is the
     // last of its block" from an 8-bit mask of the tile's 8 positions.
     tile_row_mask<NW, XI>(xok, Xs);
-    const int wm = wave / T::GNv, wn = wave % T::GNv;
-    uint32_t okw[T::TM];
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i) okw[i] = ((const uint32_t *)Xs)[wm * T::TM + i];
     uint32_t lastq = 0;
     {
         const int64_t bt0 = m0 / kK;
@@ -392,25 +431,16 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
             pos = pos + 1 == p.L ? 0 : pos + 1;
         }
     }
-    // acc[i][j][e] = C[row, col]: row = wm*WM + 32 i + 8 (e / 4) + 4 (lane / 32)
-    // + e % 4, col = wn*WN + 32 j + lane % 32.  Candidate row m = (b t) * 16 + j
-    // of side 0 becomes predecessor row j of position t + 1: output row m + 16.
+    // Candidate row m = (b t) * 16 + j of side 0 becomes predecessor row j of
+    // position t + 1: output row m + 16.
     float *const out = side == 0 ? p.A_prev + (int64_t)kK * r : p.B_cur;
-    const int col = n0 + wn * T::WN + (int)(lane & 31);
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rw = 8 * (v >> 2) + 4 * (int)(lane >> 5) + (v & 3);  // row within the 32-row block
-            const int rl = wm * T::WM + i * 32 + rw;
-            const int64_t m = m0 + rl;
-            if (m >= p.M) continue;
-            if (side == 0 && ((lastq >> (rl >> 4)) & 1u)) continue;  // no successor position
-            const bool ok = (okw[i] >> rw) & 1u;
-            float *dst = out + m * r + col;
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) dst[j * 32] = ok ? acc[i][j][v] : 0.0f;
-        }
+    for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) {
+        const int64_t m = m0 + rl;
+        if (m >= p.M) return;
+        if (side == 0 && ((lastq >> (rl >> 4)) & 1u)) return;  // no successor position
+        const bool ok = (((const uint32_t *)Xs)[rl >> 5] >> (rl & 31)) & 1u;
+        *(floatx4 *)(out + m * r + n0 + cl) = ok ? v : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    });
 }
 
 // Sum the K splits of the candidate job in split order, then the epilogue of
@@ -536,37 +566,28 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
     if (k1 > k0) mma_tile_dma<T>(xsrc, W, d, k0, k1, Xs, Ws, acc);
 
     tile_row_mask<NW, XI>(xok, Xs);
-    const int wm = wave / T::GNv, wn = wave % T::GNv;
-    uint32_t okw[T::TM];
-#pragma unroll
-    for (int i = 0; i < T::TM; ++i) okw[i] = ((const uint32_t *)Xs)[wm * T::TM + i];
     const int64_t rows_all = (int64_t)p.B * p.L + p.B;
+    for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) {
+        const int64_t m = m0 + rl;
+        if (m >= M) return;
+        const bool ok = (((const uint32_t *)Xs)[rl >> 5] >> (rl & 31)) & 1u;
+        if (!ok) v = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        const int n = n0 + cl;
+        if (p.nsplit > 1) {
+            const int64_t row = gate ? m : (int64_t)p.B * p.L + m;
+            *(floatx4 *)(p.part + ((int64_t)ks * rows_all + row) * r + n) = v;
+        } else if (gate) {
+            floatx4 gv;
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i)
+            for (int e = 0; e < 4; ++e) gv[e] = 1.0f / (1.0f + expf(-v[e]));
+            *(floatx4 *)(p.G + m * r + n) = gv;
+        } else {
+            float *base = p.A_prev + (m * p.L * kK) * r + n;
+            *(floatx4 *)base = v;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int rw = 8 * (v >> 2) + 4 * (int)(lane >> 5) + (v & 3);
-            const int rl = wm * T::WM + i * 32 + rw;
-            const int64_t m = m0 + rl;
-            if (m >= M) continue;
-            const bool ok = (okw[i] >> rw) & 1u;
-#pragma unroll
-            for (int j = 0; j < T::TN; ++j) {
-                const int n = n0 + wn * T::WN + j * 32 + (int)(lane & 31);
-                const float val = ok ? acc[i][j][v] : 0.0f;
-                if (p.nsplit > 1) {
-                    const int64_t row = gate ? m : (int64_t)p.B * p.L + m;
-                    p.part[((int64_t)ks * rows_all + row) * r + n] = val;
-                } else if (gate) {
-                    p.G[m * r + n] = 1.0f / (1.0f + expf(-val));
-                } else {
-                    float *base = p.A_prev + (m * p.L * kK) * r + n;
-                    base[0] = val;
-#pragma unroll
-                    for (int z = 1; z < kK; ++z) base[(int64_t)z * r] = 0.0f;
-                }
-            }
+            for (int z = 1; z < kK; ++z) *(floatx4 *)(base + (int64_t)z * r) = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         }
+    });
 }
 
 // Sum the K splits of the gate job in split order, then the epilogue.
@@ -588,32 +609,29 @@ __global__ __launch_bounds__(256) void project_gate_reduce_kernel(GateParams p) 
     }
 }
 
-// Column tile of the gate job: the largest of 256, 128, 64, 32 that divides r
-// and is at most DSEL_GATE_BN (narrow tiles give this short GEMM more
-// workgroups).
-#ifndef DSEL_GATE_BN
-#define DSEL_GATE_BN 256
-#endif
-inline int gate_bn(int64_t r) {
+// Column tile and K splits of the gate job (M = batch*block + batch rows, a
+// short GEMM).  Few row tiles (up to 16, e.g. 64 x 16 positions): 64-wide
+// column tiles and splits of at least 10 K steps; more: 128-wide tiles and
+// splits of at least 8 steps; in both cases about 256 workgroups.  Measured
+// on MI355X: 64 x 16 positions, d 2560: 14 us (against 20 us for 256-wide
+// tiles split 10 ways); 256 x 16, d 6144: 35 us.  The column tile is the
+// largest of 256, 128, 64, 32 that divides r and is at most that width.
+inline int gate_row_tiles(int64_t batch, int64_t block) {
+    return (int)((batch * block + 127) / 128 + (batch + 127) / 128);
+}
+inline int gate_bn(int64_t batch, int64_t block, int64_t r) {
+    const int cap = gate_row_tiles(batch, block) <= 16 ? 64 : 128;
     for (int bn = 256; bn > 32; bn >>= 1)
-        if (bn <= DSEL_GATE_BN && r % bn == 0) return bn;
+        if (bn <= cap && r % bn == 0) return bn;
     return 32;
 }
-
-// K splits of the gate job: enough workgroups to fill DSEL_GATE_TARGET_WG
-// slots, keeping at least DSEL_GATE_MIN_STEPS K steps per split.
-#ifndef DSEL_GATE_MIN_STEPS
-#define DSEL_GATE_MIN_STEPS 4
-#endif
-#ifndef DSEL_GATE_TARGET_WG
-#define DSEL_GATE_TARGET_WG 256
-#endif
 inline int gate_nsplit(int64_t batch, int64_t block, int64_t d, int64_t r) {
-    const int64_t BN = gate_bn(r);
-    const int64_t tiles = ((batch * block + 127) / 128 + (batch + 127) / 128) * (r / BN);
+    const int64_t BN = gate_bn(batch, block, r);
+    const int64_t tiles = (int64_t)gate_row_tiles(batch, block) * (r / BN);
     const int64_t nk = d / kBK;
-    int64_t s = DSEL_GATE_TARGET_WG / (tiles > 0 ? tiles : 1);
-    if (s > nk / DSEL_GATE_MIN_STEPS) s = nk / DSEL_GATE_MIN_STEPS;
+    const int64_t min_steps = BN <= 64 ? 10 : 8;
+    int64_t s = 256 / (tiles > 0 ? tiles : 1);
+    if (s > nk / min_steps) s = nk / min_steps;
     if (s < 1) s = 1;
     return (int)s;
 }

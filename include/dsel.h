@@ -131,6 +131,16 @@ dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d, const
                               const int32_t *verified, int64_t batch, int64_t block, float *A_prev,
                               float *G, void *workspace, size_t workspace_bytes,
                               dsel_stream_t stream);
+/* project_gate for running beside another kernel, e.g. dsel_select_topk on a
+ * second stream: the same outputs as dsel_project_gate, bit for bit except
+ * for the order of the fp32 sums over d, computed with one workgroup per
+ * 128-row output tile, no split along d and no workspace, so it occupies few
+ * CUs (9 at 64 x 16 positions) for longer instead of the whole chip briefly.
+ * Arguments, layouts and requirements as for dsel_project_gate. */
+dsel_status dsel_project_gate_overlap(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                                      const uint16_t *W_H, int64_t r, const uint16_t *h,
+                                      const int32_t *verified, int64_t batch, int64_t block,
+                                      float *A_prev, float *G, dsel_stream_t stream);
 dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
                               const uint16_t *W_B, int64_t r, const int32_t *cand_id,
                               int64_t batch, int64_t block, float *A_prev, float *B_cur,

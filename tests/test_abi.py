@@ -30,7 +30,8 @@ def lib():
 
 def test_header_declares_the_boundary():
     names = _declared()
-    for want in ("dsel_select_topk", "dsel_project", "dsel_project_gate", "dsel_project_cand",
+    for want in ("dsel_select_topk", "dsel_project", "dsel_project_gate", "dsel_project_gate_overlap",
+                 "dsel_project_cand",
                  "dsel_score_pairs", "dsel_walk", "dsel_verify"):
         assert want in names
 

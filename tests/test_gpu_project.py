@@ -96,6 +96,33 @@ def test_project_matches_oracle(ora, dev, B, L, V, d, r):
     _check(ora, dev, inp, cand)
 
 
+@pytest.mark.parametrize("B,L,V,d,r", [
+    (3, 5, 500, 128, 32),
+    (40, 16, 30000, 128, 256),  # 6 row tiles, one per workgroup
+    (1, 16, 20000, 2560, 256),  # one block: 40 K steps in one workgroup
+    (9, 7, 20000, 320, 256),
+    (2, 3, 700, 448, 96),
+])
+def test_project_gate_overlap_matches_oracle(ora, dev, B, L, V, d, r):
+    """The unsplit gate (dsel_project_gate_overlap) writes G and position 0's
+    predecessor rows within the same fp32 bound, and nothing else of A_prev."""
+    inp, cand = _rand_inputs(B * 1000 + L + 7, B, L, V, d, r)
+    t = to_dev(inp, dev)
+    A = torch.full((B, L, K, r), float("nan"), dtype=torch.float32, device=dev)
+    G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
+    ds.project_gate_overlap(t["E"], t["W_A"], t["W_H"], t["h"], t["verified"], A, G)
+    torch.cuda.synchronize()
+    A, G = A.cpu().numpy().astype(np.float64), G.cpu().numpy().astype(np.float64)
+    rA, _, rG = ora.project(inp["E"], inp["W_A"], inp["W_B"], inp["W_H"], inp["h"], cand, inp["verified"])
+    bA, _, bG = _abs_bounds(inp, cand)
+    g = _gamma(inp["E"].shape[1])
+    assert np.all(np.abs(A[:, 0, 0] - rA[:, 0, 0]) <= g * bA[:, 0, 0] + 1e-30)
+    assert np.all(A[:, 0, 1:] == 0.0)
+    assert np.all(np.isnan(A[:, 1:])), "the gate wrote rows of positions >= 1"
+    assert np.all(np.abs(G - rG) <= 0.25 * g * bG + 8 * 2.0 ** -24)
+    assert ds.device_error() == 0
+
+
 def test_project_exact_cases(ora, dev):
     """One-hot E rows with small-integer weights: every sum is exact, so the
     GPU must match bit for bit; a zero gate weight gives G = 1/2 exactly."""
