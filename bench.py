@@ -35,6 +35,7 @@ WRITE_FACTOR = 1.0
 TRAFFIC_KERNELS = {
     "topk16": ("topk16_kernel", ["common.h", "topk16.h"]),
     "project_cand": ("project_cand_kernel", ["common.h", "project.h"]),
+    "verify_stats": ("verify_stats_kernel", ["common.h", "verify.h"]),
 }
 
 

@@ -155,10 +155,8 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(VerifyParams p) {
     float wm = -__builtin_inff(), wz = 0.0f;  // sampled: the wave's running max and sum
 
     u32x4 cur[kVU], nxt[kVU];
-    int c = c0 + wave;
-    if (c < c1) verify_load_chunk(cur, vb, c, nfull);
-    for (; c < c1; c += 4) {
-        verify_load_chunk(nxt, vb, c + 4 < c1 ? c + 4 : c, nfull);
+    // reduce the chunk c held in cur
+    auto process = [&](int c) {
         if constexpr (!SAMPLED) {
             // screen: can any element of the lane's chunk reach the wave's best
             // so far (wbv, wave-uniform)?  Nothing below it can be the row's
@@ -250,8 +248,19 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(VerifyParams p) {
             wz = wz * exp2_rel(wm, nm, s) + zc * exp2_rel(mc, nm, s);
             wm = nm;
         }
+    };
+    // the next chunk's loads go out before the current one is reduced; the
+    // last chunk is peeled off so that no load is issued past the range
+    int c = c0 + wave;
+    if (c < c1) {
+        verify_load_chunk(cur, vb, c, nfull);
+        for (; c + 4 < c1; c += 4) {
+            verify_load_chunk(nxt, vb, c + 4, nfull);
+            process(c);
 #pragma unroll
-        for (int u = 0; u < kVU; ++u) cur[u] = nxt[u];
+            for (int u = 0; u < kVU; ++u) cur[u] = nxt[u];
+        }
+        process(c);
     }
     // the workgroup's partial: waves combined in a fixed order
     __shared__ float sm[4], sz[4];
