@@ -50,6 +50,7 @@ def _load():
             "ora_step_table": [P, P, D, I32, I64, I64, P, P],
             "ora_verify": [P, I32, I64, I64, I64, I64, P, P, P, I32, D, P, P, P, P, P, P],
             "ora_verify_draw": [P, I32, I64, I64, I64, I64, P, P, I32, D, P, I64, I64, I32, P, P],
+            "ora_dyn_conv": [P, P, P, P, I64, I64, I64, P, P],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -220,3 +221,19 @@ def verify_draw(tlogits, b: int, t: int, residual: bool, cand_id=None, q=None, m
                                    _p(ur), int(b), int(t), int(bool(residual)), C.byref(tok), C.byref(mg)),
            "verify_draw")
     return tok.value, mg.value
+
+
+def dyn_conv(x, x_prev, base, W_c):
+    """Dynamic two-tap short convolution (see ``ora_dyn_conv``): bf16 bits in
+    (``x [B,L,d]``, ``x_prev [B,d]``, ``base [2,d]``, ``W_c [2d/16, d]``);
+    returns fp64 ``y [B,L,d]`` and the corrections ``corr [B,L,2d/16]``."""
+    x = np.ascontiguousarray(x, np.uint16)
+    x_prev = np.ascontiguousarray(x_prev, np.uint16)
+    base = np.ascontiguousarray(base, np.uint16)
+    W_c = np.ascontiguousarray(W_c, np.uint16)
+    B, L, d = x.shape
+    assert x_prev.shape == (B, d) and base.shape == (2, d) and W_c.shape == (2 * (d // 16), d)
+    y = np.empty((B, L, d), np.float64)
+    corr = np.empty((B, L, 2 * (d // 16)), np.float64)
+    _check(_load().ora_dyn_conv(_p(x), _p(x_prev), _p(base), _p(W_c), B, L, d, _p(y), _p(corr)), "dyn_conv")
+    return y, corr

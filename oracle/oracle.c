@@ -394,3 +394,35 @@ int ora_verify(const void *tlogits, int dtype, int64_t B, int64_t L, int64_t V, 
     }
     return 0;
 }
+
+/* ------------------------------------------------- dynamic short conv --- */
+/* [P1 Method > Lightweight Local Convolution, eq. Conv_k; P3 "Suffix decay is
+ * local"]: y_t = k_{t,0} x_t + k_{t,1} x_{t-1}, each coefficient the base
+ * kernel plus the correction of its 16-channel group, computed from x_t; the
+ * block's first position reads the last verified token. */
+int ora_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base, const uint16_t *W_c,
+                 int64_t B, int64_t L, int64_t d, double *y, double *corr) {
+    if (!x || !x_prev || !base || !W_c || !y || B < 0 || L < 1 || d < 16 || d % 16 != 0) return -1;
+    const int64_t G = d / 16;  /* correction groups per tap */
+#pragma omp parallel for schedule(static)
+    for (int64_t bt = 0; bt < B * L; ++bt) {
+        const int64_t b = bt / L, t = bt % L;
+        const uint16_t *xt = x + bt * d;
+        const uint16_t *xp = t == 0 ? x_prev + b * d : x + (bt - 1) * d;
+        double *c = (double *)malloc((size_t)(2 * G) * sizeof(double));
+        for (int64_t n = 0; n < 2 * G; ++n) {  /* corr_t = W_c x_t */
+            double acc = 0.0;
+            for (int64_t k = 0; k < d; ++k) acc += bf16_to_f64(W_c[n * d + k]) * bf16_to_f64(xt[k]);
+            c[n] = acc;
+        }
+        for (int64_t ch = 0; ch < d; ++ch) {
+            const double k0 = bf16_to_f64(base[ch]) + c[ch / 16];
+            const double k1 = bf16_to_f64(base[d + ch]) + c[G + ch / 16];
+            y[bt * d + ch] = k0 * bf16_to_f64(xt[ch]) + k1 * bf16_to_f64(xp[ch]);
+        }
+        if (corr)
+            for (int64_t n = 0; n < 2 * G; ++n) corr[bt * 2 * G + n] = c[n];
+        free(c);
+    }
+    return 0;
+}

@@ -109,6 +109,25 @@ int ora_verify_draw(const void *tlogits, int dtype, int64_t B, int64_t L, int64_
                     const int32_t *cand_id, const double *q, int mode, double T, const float *u_res,
                     int64_t b, int64_t t, int residual, int32_t *tok, double *margin);
 
+/* Dynamic two-tap short convolution ([P1] Method > Lightweight Local
+ * Convolution, eq. Conv_k; [P3] "Suffix decay is local"): a depthwise
+ * convolution over the positions of each drafted block that reaches one
+ * position back,
+ *     y_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1},
+ * with every coefficient a learned base kernel plus a correction computed from
+ * the current hidden state, one correction per 16 channels and tap:
+ *     corr_t = W_c x_t                       (2 d/16 values, no bias),
+ *     k_{t,j}[c] = base[j][c] + corr_t[j d/16 + c/16].
+ * The first position of a block reads the last verified token's
+ * representation: x_{-1} = x_prev[b].
+ *   x       [B, L, d] bf16 bits      x_prev  [B, d] bf16 bits
+ *   base    [2, d] bf16 bits (tap 0 = current position, tap 1 = previous)
+ *   W_c     [2 d / 16, d] bf16 bits  (row j d/16 + g: tap j, channel group g)
+ *   y       out [B, L, d] fp64;  corr  out [B, L, 2 d / 16] fp64 (nullable)
+ * d must be a multiple of 16.  fp64 throughout. */
+int ora_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base, const uint16_t *W_c,
+                 int64_t B, int64_t L, int64_t d, double *y, double *corr);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,7 @@ K = 16  # candidates kept per draft position
 # tensor tags for SeedSequence spawn keys
 _T_LOGITS, _T_E, _T_WA, _T_WB, _T_WH, _T_H, _T_VER, _T_U, _T_INJ = range(1, 10)
 _T_TGT, _T_UACC, _T_URES = range(10, 13)
+_T_CX, _T_CXP, _T_CB, _T_CW = range(13, 17)  # dynamic convolution inputs
 _E_CHUNK = 256  # rows of E per seed child
 
 
@@ -236,6 +237,27 @@ def make_verify_uniforms(cfg: Config, seed: int = 0):
     (one per acceptance test) and ``u_res [batch]`` (the extra token's draw)."""
     return (_rng(seed, _T_UACC).random((cfg.batch, cfg.block), dtype=np.float32),
             _rng(seed, _T_URES).random(cfg.batch, dtype=np.float32))
+
+
+def make_conv(cfg: Config, seed: int = 0, blocks: Optional[Iterable[int]] = None) -> Dict[str, np.ndarray]:
+    """Inputs of one dynamic two-tap convolution unit at the drafter's width d,
+    as bf16 bits: ``x [nb, block, d]`` ~ N(0, 1) (the hidden state entering
+    the unit), ``x_prev [nb, d]`` ~ N(0, 1) (the last verified token's),
+    ``base [2, d]`` with tap 0 ~ 1 + N(0, 0.1^2) and tap 1 ~ N(0, 0.1^2) (a
+    near-identity learned kernel), ``W_c [2 d / 16, d]`` ~ N(0, (0.1/sqrt d)^2)
+    (a small correction)."""
+    blocks = list(range(cfg.batch)) if blocks is None else list(blocks)
+    d = cfg.d
+    x = np.stack([_normal_bf16(_rng(seed, _T_CX, b), (cfg.block, d), 1.0) for b in blocks]) \
+        if blocks else np.empty((0, cfg.block, d), np.uint16)
+    xp = np.stack([_normal_bf16(_rng(seed, _T_CXP, b), (d,), 1.0) for b in blocks]) \
+        if blocks else np.empty((0, d), np.uint16)
+    rb = _rng(seed, _T_CB)
+    base = np.empty((2, d), np.float32)
+    base[0] = 1.0 + 0.1 * rb.standard_normal(d, dtype=np.float32)
+    base[1] = 0.1 * rb.standard_normal(d, dtype=np.float32)
+    W_c = _normal_bf16(_rng(seed, _T_CW), (2 * (d // 16), d), 0.1 / np.sqrt(d))
+    return dict(x=x, x_prev=xp, base=f32_to_bf16_bits(base), W_c=W_c)
 
 
 def make(cfg: Config, seed: int = 0) -> Dict[str, np.ndarray]:
