@@ -208,6 +208,60 @@ def time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream):
             "data": "synthetic target logits: draft logits + N(0,1) noise, fresh row after the block"}
 
 
+def time_conv(args, cfg, stream):
+    """The dynamic two-tap convolution unit at the workload's drafter shape
+    (x [batch, block, d]): HIP-event time per call, its HBM rate over the
+    algorithmic bytes and the MFMA rate of its correction GEMM."""
+    import ctypes as C
+
+    import torch
+
+    import draft_selection_amd as ds
+    import synth
+
+    c = synth.make_conv(cfg)
+    dev = torch.device("cuda", torch.cuda.current_device())
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    x, xp, base, W = bf(c["x"]), bf(c["x_prev"]), bf(c["base"]), bf(c["W_c"])
+    B, L, d = cfg.batch, cfg.block, cfg.d
+    y = torch.empty_like(x)
+    lib = ds.lib()
+    wsb = lib.dsel_dyn_conv_workspace_bytes(B, L, d)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    P = ds._ptr
+    sp = C.c_void_p(stream.cuda_stream)
+
+    def call():
+        st = lib.dsel_dyn_conv(P(x), P(xp), P(base), P(W), B, L, d, P(y), P(ws), wsb, sp)
+        if st:
+            raise RuntimeError(f"dsel_dyn_conv status {st}")
+
+    for _ in range(3):
+        call()
+    torch.cuda.synchronize()
+    k = min(args.steps, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(k):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / k
+    M, N = B * L, 2 * (d // 16)
+    nbytes = 2 * M * d * 2 + N * d * 2 + B * d * 2 + 2 * d * 2  # x, y, W_c, x_prev, base
+    flop = 2 * M * N * d
+    gbs = nbytes / (us * 1e-6) / 1e9
+    tfs = flop / (us * 1e-6) / 1e12
+    return {"us_per_call": round(us, 2), "bytes": nbytes, "GB/s": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "flop": flop, "TFLOP/s": round(tfs, 2),
+            "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4),
+            "shape": f"x [{B}, {L}, {d}], W_c [{N}, {d}]",
+            "data": "synthetic: x, x_prev ~ N(0,1); base tap 0 ~ 1 + N(0,0.01), tap 1 ~ N(0,0.01); W_c ~ N(0,(0.1/sqrt d)^2)"}
+
+
 def stage_means(evs):
     """Mean microseconds between consecutive stage events over the steps."""
     names = ("project_gate", "select_topk", "project_cand", "score_pairs_walk")
@@ -230,6 +284,8 @@ def main():
                     help="skip the pass that evicts the caches before every step")
     ap.add_argument("--no-verify", action="store_true",
                     help="skip timing the verification of the drafted blocks (dsel_verify)")
+    ap.add_argument("--no-conv", action="store_true",
+                    help="skip timing the dynamic two-tap convolution unit (dsel_dyn_conv)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
@@ -368,6 +424,7 @@ def main():
         cold = stage_means(cevs)
 
     verify = None if args.no_verify else time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream)
+    conv = None if args.no_conv or cfg.d % 512 else time_conv(args, cfg, stream)
 
     ms_step = wall * 1e3 / args.steps
     warm = stage_means(evs)
@@ -412,6 +469,7 @@ def main():
         "project_gate": args.gate,
         "roofline": roof,
         "verify": verify,
+        "dyn_conv": conv,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

@@ -67,6 +67,8 @@ def _load():
             "dsel_score_pairs": ([P, P, P, P, I64, I64, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_walk": ([P, I64, I64, C.POINTER(WalkArgs), P], I32),
             "dsel_verify_workspace_bytes": ([I64, I64, I64], SZ),
+            "dsel_dyn_conv_workspace_bytes": ([I64, I64, I64], SZ),
+            "dsel_dyn_conv": ([P, P, P, P, I64, I64, I64, P, P, SZ, P], I32),
             "dsel_verify": ([P, I32, I64, I64, I64, I64, P, P, P, I32, C.c_float, P, P, P, P, P, SZ, P], I32),
             "dsel_device_error": ([C.POINTER(C.c_int32), P], I32),
             "dsel_status_string": ([I32], C.c_char_p),
@@ -321,6 +323,32 @@ def device_error(stream=None) -> int:
     v = C.c_int32(0)
     _check(_load().dsel_device_error(C.byref(v), _stream(stream)), "dsel_device_error")
     return int(v.value)
+
+
+def dyn_conv_workspace_bytes(batch: int, block: int, d: int) -> int:
+    return int(_load().dsel_dyn_conv_workspace_bytes(batch, block, d))
+
+
+def dyn_conv(x, x_prev, base, W_c, y=None, workspace=None, stream=None):
+    """Dynamic two-tap short convolution of the drafter over each block's
+    positions: ``x [B, L, d]``, ``x_prev [B, d]``, ``base [2, d]``,
+    ``W_c [2 d / 16, d]``, all bf16; returns ``y [B, L, d]`` bf16."""
+    B, L, d = x.shape
+    _need(x, "x", torch.bfloat16, (B, L, d))
+    _need(x_prev, "x_prev", torch.bfloat16, (B, d))
+    _need(base, "base", torch.bfloat16, (2, d))
+    _need(W_c, "W_c", torch.bfloat16, (2 * (d // 16), d))
+    if y is None:
+        y = torch.empty_like(x)
+    _need(y, "y", torch.bfloat16, (B, L, d))
+    if workspace is None:
+        wsb = dyn_conv_workspace_bytes(B, L, d)
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    wsb = workspace.numel() * workspace.element_size()
+    st = _load().dsel_dyn_conv(_ptr(x), _ptr(x_prev), _ptr(base), _ptr(W_c), B, L, d, _ptr(y), _ptr(workspace),
+                               wsb, _stream(stream))
+    _check(st, "dsel_dyn_conv")
+    return y
 
 
 def verify_workspace_bytes(batch: int, block: int, vocab: int) -> int:

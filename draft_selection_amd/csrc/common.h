@@ -116,6 +116,16 @@ __device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t key) {
     return key;
 }
 
+// The 8 bf16 or 4 fp32 values of a 16-byte vector, widened to float
+template <bool BF16>
+__device__ __forceinline__ void widen_vec(const u32x4 &w, float (&x)[BF16 ? 8 : 4]) {
+#pragma unroll
+    for (int e = 0; e < (BF16 ? 8 : 4); ++e) {
+        const uint32_t word = w[BF16 ? e >> 1 : e];
+        x[e] = BF16 ? __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16)) : __uint_as_float(word);
+    }
+}
+
 // Sticky device error word (bits DSEL_DEVERR_*), one per device.  The library
 // is a single translation unit, so this is its only definition.
 __device__ int g_device_error = 0;

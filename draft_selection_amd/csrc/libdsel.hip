@@ -8,6 +8,7 @@
 
 #include "dsel.h"
 #include "common.h"
+#include "conv.h"
 #include "pairwalk.h"
 #include "project.h"
 #include "topk16.h"
@@ -369,6 +370,50 @@ DSEL_API const char *dsel_status_string(dsel_status s) {
 }
 
 DSEL_API int32_t dsel_version(void) { return DSEL_VERSION; }
+
+// ---- dynamic short convolution ---------------------------------------------
+
+DSEL_API size_t dsel_dyn_conv_workspace_bytes(int64_t batch, int64_t block, int64_t d) {
+    if (batch <= 0 || block < 1 || d < 512 || d % 512 != 0 || d > (1 << 16)) return 0;
+    return conv_workspace_bytes(batch, block, d);
+}
+
+DSEL_API dsel_status dsel_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base,
+                                   const uint16_t *W_c, int64_t batch, int64_t block, int64_t d, uint16_t *y,
+                                   void *workspace, size_t workspace_bytes, dsel_stream_t stream) {
+    if (batch < 0 || block < 1 || d < 512 || d % 512 != 0 || d > (1 << 16)) return DSEL_E_ARG;
+    if (batch > (int64_t)INT_MAX / block) return DSEL_E_ARG;
+    if (batch == 0) return DSEL_OK;
+    if (!x || !x_prev || !base || !W_c || !y) return DSEL_E_ARG;
+    if (!aligned(x, 16) || !aligned(x_prev, 16) || !aligned(base, 16) || !aligned(W_c, 16) || !aligned(y, 16))
+        return DSEL_E_ALIGN;
+    const size_t need = conv_workspace_bytes(batch, block, d);
+    if (!workspace || workspace_bytes < need) return DSEL_E_WORKSPACE;
+    if (!aligned(workspace, 16)) return DSEL_E_ALIGN;
+    ConvParams p;
+    p.x = x;
+    p.x_prev = x_prev;
+    p.base = base;
+    p.W_c = W_c;
+    p.y = y;
+    p.B = (int)batch;
+    p.L = (int)block;
+    p.d = (int)d;
+    p.M = batch * block;
+    p.N = (int)(d / 8);
+    p.mt = (int)((p.M + 127) / 128);
+    const int BN = conv_bn(p.M, p.N);
+    p.nt = p.N / BN;
+    p.nsplit = conv_nsplit(batch, block, d);
+    p.part = (float *)workspace;
+    const int64_t grid = (int64_t)p.mt * p.nt * p.nsplit;
+    if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
+    const void *kc = BN == 256 ? (const void *)conv_corr_kernel<256> : (const void *)conv_corr_kernel<64>;
+    dsel_status st = launch(kc, dim3((unsigned)grid), dim3(tile_threads(BN)), &p, 0, stream);
+    if (st != DSEL_OK) return st;
+    return launch((const void *)conv_apply_kernel, dim3((unsigned)p.M), dim3(256), &p,
+                  (size_t)p.N * sizeof(float), stream);
+}
 
 // ---- verify ----------------------------------------------------------------
 

@@ -108,16 +108,6 @@ __device__ __forceinline__ float logit_elem(const char *rowp, int64_t i) {
     else return *(const float *)(rowp + i * 4);
 }
 
-// 8 (bf16) or 4 (fp32) logits of a 16-byte vector, widened to float
-template <bool BF16>
-__device__ __forceinline__ void widen_vec(const u32x4 &w, float (&x)[BF16 ? 8 : 4]) {
-#pragma unroll
-    for (int e = 0; e < (BF16 ? 8 : 4); ++e) {
-        const uint32_t word = w[BF16 ? e >> 1 : e];
-        x[e] = BF16 ? __uint_as_float((e & 1) ? (word & 0xFFFF0000u) : (word << 16)) : __uint_as_float(word);
-    }
-}
-
 // Load chunk c of a row: lane l takes vectors c 256 + u 64 + l (u < kVU); an
 // index past the row's whole vectors is clamped to the last one (its values
 // are not used).  The loads are issued unconditionally, so the next chunk can

@@ -237,6 +237,31 @@ dsel_status dsel_device_error(int32_t *out_code, dsel_stream_t stream);
 /* Human-readable name of a status code (static storage). */
 const char *dsel_status_string(dsel_status s);
 
+/* dyn_conv -- [P1] Method > Lightweight Local Convolution (eq. Conv_k), [P3]
+ * "Suffix decay is local": the drafter's dynamic two-tap short convolution
+ * over the positions of each drafted block,
+ *     y_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1},
+ *     k_{t,j}[c] = base[j][c] + corr_t[j d/16 + c/16],  corr_t = W_c x_t,
+ * one correction per 16 channels and tap, computed from the current position's
+ * input; position 0 reads the last verified token (x_{-1} = x_prev[b]).
+ *   x        [batch, block, d] bf16: the unit's input at every drafted position.
+ *   x_prev   [batch, d] bf16: the last verified token's representation.
+ *   base     [2, d] bf16: the learned base kernel, tap 0 (current position)
+ *            then tap 1 (previous position).
+ *   W_c      [2 d / 16, d] bf16, linear-layer layout: row j d/16 + g is the
+ *            correction of tap j, channel group g (no bias).
+ *   y        out [batch, block, d] bf16 (round to nearest even); must not
+ *            overlap x.
+ *   workspace  device scratch of at least dsel_dyn_conv_workspace_bytes()
+ *            bytes; contents need no initialisation.
+ * Arithmetic: corr by bf16 MFMA with fp32 accumulation, the taps in fp32.
+ * Requirements: d % 512 == 0, 512 <= d <= 65536, block >= 1, batch >= 0, all
+ * pointers 16-byte aligned. */
+size_t dsel_dyn_conv_workspace_bytes(int64_t batch, int64_t block, int64_t d);
+dsel_status dsel_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base,
+                          const uint16_t *W_c, int64_t batch, int64_t block, int64_t d, uint16_t *y,
+                          void *workspace, size_t workspace_bytes, dsel_stream_t stream);
+
 /* ABI version of this header (major * 100 + minor). */
 int32_t dsel_version(void);
 #define DSEL_VERSION 100
