@@ -51,6 +51,7 @@ def _load():
             "ora_verify": [P, I32, I64, I64, I64, I64, P, P, P, I32, D, P, P, P, P, P, P],
             "ora_verify_draw": [P, I32, I64, I64, I64, I64, P, P, I32, D, P, I64, I64, I32, P, P],
             "ora_dyn_conv": [P, P, P, P, I64, I64, I64, P, P],
+            "ora_lmhead_topk": [P, P, I64, I64, I64, P, P],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -237,3 +238,18 @@ def dyn_conv(x, x_prev, base, W_c):
     corr = np.empty((B, L, 2 * (d // 16)), np.float64)
     _check(_load().ora_dyn_conv(_p(x), _p(x_prev), _p(base), _p(W_c), B, L, d, _p(y), _p(corr)), "dyn_conv")
     return y, corr
+
+
+def lmhead_topk(h, W):
+    """LM head and top-16 (see ``ora_lmhead_topk``): ``h [rows, d]``,
+    ``W [V, d]`` as bf16 bits; returns ``cand_id [rows, 16]`` int32 and the
+    fp64 values of the 17 best, ``cand_z [rows, 17]``."""
+    h = np.ascontiguousarray(h, np.uint16)
+    W = np.ascontiguousarray(W, np.uint16)
+    rows, d = h.shape
+    V = W.shape[0]
+    assert W.shape == (V, d)
+    cid = np.empty((rows, K), np.int32)
+    cz = np.empty((rows, K + 1), np.float64)
+    _check(_load().ora_lmhead_topk(_p(h), _p(W), rows, V, d, _p(cid), _p(cz)), "lmhead_topk")
+    return cid, cz

@@ -426,3 +426,40 @@ int ora_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base
     }
     return 0;
 }
+
+/* ------------------------------------------------- LM head + top-16 --- */
+/* [P1 Method: candidates are the drafter's own top-16 logits, with no extra
+ * LM-head forward]: z = h W^T in fp64, then sorted insertion under the same
+ * total order as ora_select_topk, keeping 17 so the caller can see the margin
+ * of the 16th. */
+int ora_lmhead_topk(const uint16_t *h, const uint16_t *W, int64_t rows, int64_t V, int64_t d,
+                    int32_t *cand_id, double *cand_z) {
+    if (!h || !W || !cand_id || !cand_z || rows < 0 || V < ORA_K || d < 1) return -1;
+    enum { KK = ORA_K + 1 };
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t row = 0; row < rows; ++row) {
+        double val[KK];
+        int64_t id[KK];
+        int n = 0;
+        double *hr = (double *)malloc((size_t)d * sizeof(double));
+        for (int64_t k = 0; k < d; ++k) hr[k] = bf16_to_f64(h[row * d + k]);
+        for (int64_t v = 0; v < V; ++v) {
+            double z = 0.0;
+            for (int64_t k = 0; k < d; ++k) z += hr[k] * bf16_to_f64(W[v * d + k]);
+            if (n == KK && !ranks_above(z, v, val[KK - 1], id[KK - 1])) continue;
+            int pos = (n < KK) ? n : KK - 1;
+            while (pos > 0 && ranks_above(z, v, val[pos - 1], id[pos - 1])) {
+                val[pos] = val[pos - 1];
+                id[pos] = id[pos - 1];
+                --pos;
+            }
+            val[pos] = z;
+            id[pos] = v;
+            if (n < KK) ++n;
+        }
+        for (int j = 0; j < ORA_K; ++j) cand_id[row * ORA_K + j] = (int32_t)id[j];
+        for (int j = 0; j < KK; ++j) cand_z[row * KK + j] = j < n ? val[j] : -INFINITY;
+        free(hr);
+    }
+    return 0;
+}

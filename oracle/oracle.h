@@ -128,6 +128,18 @@ int ora_verify_draw(const void *tlogits, int dtype, int64_t B, int64_t L, int64_
 int ora_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base, const uint16_t *W_c,
                  int64_t B, int64_t L, int64_t d, double *y, double *corr);
 
+/* LM head with the top-16 taken from its output ([P1] Method: the selector
+ * reuses the drafter's logits, no extra LM-head forward; the head's top-16
+ * are the selector's candidates): logits z[r, v] = sum_k h[r, k] W[v, k] in
+ * fp64, then the first 16 of every row under the top-16 order (value
+ * descending, ties to the lower id, NaN lowest).
+ *   h      [rows, d] bf16 bits (the drafter's final hidden states)
+ *   W      [V, d] bf16 bits (the LM-head weight, linear-layer layout)
+ *   cand_id out [rows, 16] int32;  cand_z  out [rows, 17] fp64: the values of
+ *          the 17 best (the 17th bounds what was left out; -inf if V = 16). */
+int ora_lmhead_topk(const uint16_t *h, const uint16_t *W, int64_t rows, int64_t V, int64_t d,
+                    int32_t *cand_id, double *cand_z);
+
 #ifdef __cplusplus
 }
 #endif
