@@ -262,6 +262,63 @@ def time_conv(args, cfg, stream):
             "data": "synthetic: x, x_prev ~ N(0,1); base tap 0 ~ 1 + N(0,0.01), tap 1 ~ N(0,0.01); W_c ~ N(0,(0.1/sqrt d)^2)"}
 
 
+def time_lmhead(args, cfg, E, stream):
+    """The LM head with the fused top-16 at the workload's shape (rows = batch x
+    block hidden states against E, tied embeddings): HIP-event time per call
+    and its MFMA rate; beside it the unfused route (torch's GEMM writing bf16
+    logits, then select_topk), timed the same way."""
+    import ctypes as C
+
+    import torch
+    import torch.nn.functional as F
+
+    import draft_selection_amd as ds
+    import synth
+
+    dev = E.device
+    R, V, dd = cfg.batch * cfg.block, cfg.vocab, cfg.d
+    h = torch.from_numpy(synth.make_h(cfg).reshape(R, dd).view(np.int16)).to(dev).view(torch.bfloat16)
+    lib = ds.lib()
+    P = ds._ptr
+    sp = C.c_void_p(stream.cuda_stream)
+    cid = torch.empty((R, 16), dtype=torch.int32, device=dev)
+    cu = torch.empty((R, 16), dtype=torch.float32, device=dev)
+    wsb = lib.dsel_lmhead_topk_workspace_bytes(R, V)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+
+    def fused():
+        st = lib.dsel_lmhead_topk(P(h), P(E), R, V, dd, P(cid), P(cu), P(ws), wsb, sp)
+        if st:
+            raise RuntimeError(f"dsel_lmhead_topk status {st}")
+
+    def unfused():
+        with torch.cuda.stream(stream):
+            z = F.linear(h, E)  # [R, V] bf16 logits in HBM
+            ds.select_topk(z.view(1, R, V), stream=stream)
+
+    def timed(fn, k):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(k):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k
+
+    k = 10
+    us = timed(fused, k)
+    us_unfused = timed(unfused, k)
+    flop = 2.0 * R * V * dd
+    tfs = flop / (us * 1e-6) / 1e12
+    return {"us_per_call": round(us, 1), "flop": flop, "TFLOP/s": round(tfs, 1),
+            "mfma_frac": round(tfs / BF16_PEAK_TFLOPS, 4), "logit_bytes_not_written": R * V * 2,
+            "unfused_us": round(us_unfused, 1), "unfused": "torch F.linear (bf16 logits to HBM) + dsel_select_topk",
+            "shape": f"h [{R}, {dd}] x E [{V}, {dd}]^T", "data": "synthetic h ~ N(0,1), E ~ N(0,0.02) (tied embeddings)"}
+
+
 def stage_means(evs):
     """Mean microseconds between consecutive stage events over the steps."""
     names = ("project_gate", "select_topk", "project_cand", "score_pairs_walk")
@@ -286,6 +343,8 @@ def main():
                     help="skip timing the verification of the drafted blocks (dsel_verify)")
     ap.add_argument("--no-conv", action="store_true",
                     help="skip timing the dynamic two-tap convolution unit (dsel_dyn_conv)")
+    ap.add_argument("--lmhead", action="store_true",
+                    help="also time the LM head with the fused top-16 (dsel_lmhead_topk) and the unfused route")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
@@ -425,6 +484,7 @@ def main():
 
     verify = None if args.no_verify else time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream)
     conv = None if args.no_conv or cfg.d % 512 else time_conv(args, cfg, stream)
+    lmhead = time_lmhead(args, cfg, d["E"], stream) if args.lmhead else None
 
     ms_step = wall * 1e3 / args.steps
     warm = stage_means(evs)
@@ -470,6 +530,7 @@ def main():
         "roofline": roof,
         "verify": verify,
         "dyn_conv": conv,
+        "lmhead_topk": lmhead,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

@@ -68,6 +68,8 @@ def _load():
             "dsel_walk": ([P, I64, I64, C.POINTER(WalkArgs), P], I32),
             "dsel_verify_workspace_bytes": ([I64, I64, I64], SZ),
             "dsel_dyn_conv_workspace_bytes": ([I64, I64, I64], SZ),
+            "dsel_lmhead_topk_workspace_bytes": ([I64, I64], SZ),
+            "dsel_lmhead_topk": ([P, P, I64, I64, I64, P, P, P, SZ, P], I32),
             "dsel_dyn_conv": ([P, P, P, P, I64, I64, I64, P, P, SZ, P], I32),
             "dsel_verify": ([P, I32, I64, I64, I64, I64, P, P, P, I32, C.c_float, P, P, P, P, P, SZ, P], I32),
             "dsel_device_error": ([C.POINTER(C.c_int32), P], I32),
@@ -323,6 +325,25 @@ def device_error(stream=None) -> int:
     v = C.c_int32(0)
     _check(_load().dsel_device_error(C.byref(v), _stream(stream)), "dsel_device_error")
     return int(v.value)
+
+
+def lmhead_topk(h, W, stream=None):
+    """The LM head and its top-16 in one pass (logits never written):
+    ``h [..., d]`` and ``W [vocab, d]`` bf16; returns ``cand_id [..., 16]``
+    int32 and ``cand_u [..., 16]`` fp32 (the fp32 logits)."""
+    d = h.shape[-1]
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16)
+    _need(W, "W", torch.bfloat16, (V, d))
+    rows = h.numel() // d
+    cid = torch.empty(h.shape[:-1] + (K,), dtype=torch.int32, device=h.device)
+    cu = torch.empty(h.shape[:-1] + (K,), dtype=torch.float32, device=h.device)
+    wsb = int(_load().dsel_lmhead_topk_workspace_bytes(rows, V)) if rows else 0
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=h.device)
+    st = _load().dsel_lmhead_topk(_ptr(h), _ptr(W), rows, V, d, _ptr(cid), _ptr(cu), _ptr(ws), wsb,
+                                  _stream(stream))
+    _check(st, "dsel_lmhead_topk")
+    return cid, cu
 
 
 def dyn_conv_workspace_bytes(batch: int, block: int, d: int) -> int:

@@ -9,6 +9,7 @@
 #include "dsel.h"
 #include "common.h"
 #include "conv.h"
+#include "lmhead.h"
 #include "pairwalk.h"
 #include "project.h"
 #include "topk16.h"
@@ -370,6 +371,52 @@ DSEL_API const char *dsel_status_string(dsel_status s) {
 }
 
 DSEL_API int32_t dsel_version(void) { return DSEL_VERSION; }
+
+// ---- LM head with the top-16 ------------------------------------------------
+
+DSEL_API size_t dsel_lmhead_topk_workspace_bytes(int64_t rows, int64_t vocab) {
+    if (rows <= 0 || vocab < kK || vocab >= (int64_t)INT_MAX) return 0;
+    return lmhead_workspace_bytes(rows, vocab);
+}
+
+DSEL_API dsel_status dsel_lmhead_topk(const uint16_t *h, const uint16_t *W, int64_t rows, int64_t vocab,
+                                      int64_t d, int32_t *cand_id, float *cand_u, void *workspace,
+                                      size_t workspace_bytes, dsel_stream_t stream) {
+    if (rows < 0 || rows > (1 << 24) || vocab < kK || vocab >= (int64_t)INT_MAX || d < 64 || d % 64 != 0 ||
+        d > (1 << 20))
+        return DSEL_E_ARG;
+    if (rows == 0) return DSEL_OK;
+    if (!h || !W || !cand_id || !cand_u) return DSEL_E_ARG;
+    if (!aligned(h, 16) || !aligned(W, 16) || !aligned(cand_id, 4) || !aligned(cand_u, 4)) return DSEL_E_ALIGN;
+    const size_t need = lmhead_workspace_bytes(rows, vocab);
+    if (!workspace || workspace_bytes < need) return DSEL_E_WORKSPACE;
+    if (!aligned(workspace, 16)) return DSEL_E_ALIGN;
+    LmheadParams p;
+    p.h = h;
+    p.W = W;
+    p.R = rows;
+    p.V = vocab;
+    p.d = (int)d;
+    p.mt = (int)((rows + 127) / 128);
+    p.nct = (int)((vocab + kLmBN - 1) / kLmBN);
+    p.nvs = lmhead_nvs(rows, vocab);
+    p.cpw = (p.nct + p.nvs - 1) / p.nvs;
+    p.partial = (uint64_t *)workspace;
+    const int64_t grid = (int64_t)p.mt * p.nvs;
+    if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
+    dsel_status st = launch((const void *)lmhead_topk_kernel, dim3((unsigned)grid), dim3(LmTile::NT), &p, 0, stream);
+    if (st != DSEL_OK) return st;
+    TopkParams tp;
+    tp.logits = nullptr;
+    tp.rows = rows;
+    tp.V = vocab;
+    tp.ld = vocab;
+    tp.nsplit = p.nvs;
+    tp.cand_id = cand_id;
+    tp.cand_u = cand_u;
+    tp.partial = p.partial;
+    return launch((const void *)topk16_merge_kernel<true>, dim3((unsigned)rows), dim3(256), &tp, 0, stream);
+}
 
 // ---- dynamic short convolution ---------------------------------------------
 

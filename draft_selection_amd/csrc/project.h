@@ -99,7 +99,9 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | ((N >> 4) << 14));
 }
 
-// acc += X * W^T over K steps [k0, k1) (64-deep steps), k1 > k0.
+// acc += X * W^T over K steps [k0, k1) (64-deep steps), k1 > k0.  W rows at
+// or past `wrows` (a ragged last tile) load row wrows - 1; their results are
+// the caller's to ignore.
 //
 // Schedule of one step kt: the wave waits for its own LDS reads of step kt
 // (issued one step earlier) and its own DMA of step kt+1, then meets the
@@ -112,7 +114,8 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 template <class T>
 __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DXI], const uint16_t *wbase,
                                              int64_t wstride, int k0, int k1, uint16_t *Xs,
-                                             uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN]) {
+                                             uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN],
+                                             int wrows = T::BNv) {
     constexpr int BM = T::BMv, BN = T::BNv, NW = T::NW;
     constexpr int XI = T::DXI, WI = T::DWI;
     static_assert(XI >= 1 && WI >= 1 && XI * NW * 8 == BM && WI * NW * 8 == BN, "DMA tile shape");
@@ -131,7 +134,8 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
 #pragma unroll
     for (int u = 0; u < WI; ++u) {
         const int row = 8 * (wave + NW * u) + lrow;
-        wsrc[u] = wbase + (int64_t)row * wstride + ((pch ^ ((row >> 1) & 7)) << 3);
+        const int srow = row < wrows ? row : wrows - 1;  // rows past the matrix re-read its last row
+        wsrc[u] = wbase + (int64_t)srow * wstride + ((pch ^ ((row >> 1) & 7)) << 3);
     }
     // LDS element offsets of the rows of this lane's fragments, relative to a
     // stage; every such row is = fr (mod 32), so chunk (2 s + fk) of it sits
@@ -231,6 +235,89 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
 #undef DSEL_ISSUE
 #undef DSEL_READ_STEP
 #undef DSEL_STEP
+}
+
+// The same product with a leaner register footprint: fragments are read one
+// 16-deep slice ahead (two sets of TM + TN fragments instead of two whole K
+// steps), for kernels that keep other state live beside the GEMM.  While
+// slice s multiplies, slice s+1 is read; at a step's last slice the wave waits
+// for its own reads and its DMA of the next step, meets the others at the
+// barrier, refills the stage three steps ahead and reads the next step's
+// first fragments ahead of the last slice's MFMAs.
+template <class T>
+__device__ __forceinline__ void mma_tile_dma_lean(const uint16_t *const (&xsrc)[T::DXI], const uint16_t *wbase,
+                                                  int64_t wstride, int k0, int k1, uint16_t *Xs, uint16_t *Ws,
+                                                  floatx16 (&acc)[T::TM][T::TN], int wrows = T::BNv) {
+    constexpr int BM = T::BMv, BN = T::BNv, NW = T::NW;
+    constexpr int XI = T::DXI, WI = T::DWI;
+    static_assert(XI >= 1 && WI >= 1 && XI * NW * 8 == BM && WI * NW * 8 == BN, "DMA tile shape");
+    constexpr int PER = XI + WI;
+    constexpr int NS = 3;
+    constexpr int KS = kBK / 16;
+    const uint32_t lane = lane_id();
+    const int wave = threadIdx.x >> 6;
+    const int wm = wave / T::GNv, wn = wave % T::GNv;
+    const int fr = lane & 31, fk = lane >> 5;
+    const int lrow = (int)(lane >> 3), pch = (int)(lane & 7);
+    const uint16_t *wsrc[WI];
+#pragma unroll
+    for (int u = 0; u < WI; ++u) {
+        const int row = 8 * (wave + NW * u) + lrow;
+        const int srow = row < wrows ? row : wrows - 1;
+        wsrc[u] = wbase + (int64_t)srow * wstride + ((pch ^ ((row >> 1) & 7)) << 3);
+    }
+    int aoff[T::TM], boff[T::TN];
+#pragma unroll
+    for (int i = 0; i < T::TM; ++i) aoff[i] = (wm * T::WM + i * 32 + fr) * kBK;
+#pragma unroll
+    for (int j = 0; j < T::TN; ++j) boff[j] = (wn * T::WN + j * 32 + fr) * kBK;
+    const int rsw = (fr >> 1) & 7;
+    auto issue = [&](int k, int stage) {
+        const int kk = (k < k1 ? k : k1 - 1) * kBK;
+#pragma unroll
+        for (int u = 0; u < XI; ++u) lds_dma16(xsrc[u] + kk, Xs + stage * BM * kBK + (8 * (wave + NW * u)) * kBK);
+#pragma unroll
+        for (int u = 0; u < WI; ++u) lds_dma16(wsrc[u] + kk, Ws + stage * BN * kBK + (8 * (wave + NW * u)) * kBK);
+    };
+    bf16x8 a[2][T::TM], b[2][T::TN];
+    auto frag = [&](int buf, const uint16_t *xb, const uint16_t *wb, int sl) {
+        const int ch = ((sl * 2 + fk) ^ rsw) << 3;
+#pragma unroll
+        for (int i = 0; i < T::TM; ++i) a[buf][i] = *(const bf16x8 *)(xb + aoff[i] + ch);
+#pragma unroll
+        for (int j = 0; j < T::TN; ++j) b[buf][j] = *(const bf16x8 *)(wb + boff[j] + ch);
+    };
+    issue(k0, 0);
+    issue(k0 + 1, 1);
+    issue(k0 + 2, 2);
+    wait_vmcnt<2 * PER>();
+    wg_barrier();
+    frag(0, Xs, Ws, 0);
+    int cur = 0;
+    for (int kt = k0; kt < k1; ++kt) {
+        const int nxt = cur == NS - 1 ? 0 : cur + 1;
+        const uint16_t *xb = Xs + cur * BM * kBK;
+        const uint16_t *wb = Ws + cur * BN * kBK;
+#pragma unroll
+        for (int sl = 0; sl < KS; ++sl) {
+            const int c = sl & 1, n = c ^ 1;
+            if (sl + 1 < KS) {
+                frag(n, xb, wb, sl + 1);
+            } else {
+                wait_vmcnt_lgkm0<PER>();
+                wg_barrier();
+                issue(kt + 3, cur);
+                frag(n, Xs + nxt * BM * kBK, Ws + nxt * BN * kBK, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < T::TM; ++i)
+#pragma unroll
+                for (int j = 0; j < T::TN; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+        }
+        cur = nxt;
+    }
+    wait_vmcnt<0>();
 }
 
 // Valid-row mask of a BM-row tile, shared through LDS.  Rows are loaded by

@@ -294,6 +294,8 @@ __global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
 }
 
 // Merge the nsplit partial lists of a row: one workgroup (4 waves) per row.
+// With logits == nullptr (lists from the LM-head kernel) a zero value comes out
+// as +0.0.
 // Wave w folds lists 3w, 3w+1, 3w+2, then 3w+12, ... into its running best 16
 // (one 64-key sort per 3 lists), and wave 0 sorts the four waves' lists.
 template <bool BF16>
@@ -318,11 +320,17 @@ __global__ __launch_bounds__(256) void topk16_merge_kernel(TopkParams p) {
     if (wave != 0) return;
     best = wave_sort64_desc(sk[lane]);
     if (lane < (uint32_t)kK) {
-        const char *rowp = p.logits + row * p.ld * ES;
         uint32_t id = key_id(best);
         p.cand_id[row * kK + lane] = (int32_t)id;
         float u;
-        if (!key_value(best, &u)) u = (int64_t)id < p.V ? load_elem<BF16>(rowp, id) : __builtin_nanf("");
+        if (!key_value(best, &u)) {
+            if (p.logits) {  // the two merged codes: read the exact bits back
+                const char *rowp = p.logits + row * p.ld * ES;
+                u = (int64_t)id < p.V ? load_elem<BF16>(rowp, id) : __builtin_nanf("");
+            } else {         // no logits in memory (the LM-head path): NaN, or a zero
+                u = (uint32_t)(best >> 32) == 0u ? __builtin_nanf("") : 0.0f;
+            }
+        }
         p.cand_u[row * kK + lane] = u;
     }
 }

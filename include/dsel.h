@@ -237,6 +237,27 @@ dsel_status dsel_device_error(int32_t *out_code, dsel_stream_t stream);
 /* Human-readable name of a status code (static storage). */
 const char *dsel_status_string(dsel_status s);
 
+/* lmhead_topk -- [P1] Method > Lightweight Path Selector: the candidates are
+ * the drafter's own 16 best logits, with no extra LM-head forward.  The LM
+ * head z = h W^T and the top-16 of every row in one pass: the logits stay on
+ * chip and never reach HBM.
+ *   h        [rows, d] bf16: the drafter's final hidden states (rows =
+ *            batch * block positions).
+ *   W        [vocab, d] bf16: the LM-head weight (linear-layer layout; with
+ *            tied embeddings, the embedding table E).
+ *   cand_id  out [rows, 16] int32, cand_u out [rows, 16] fp32: the 16 best
+ *            logits of each row, value descending, ties to the lower id (as
+ *            dsel_select_topk on the logits); a zero logit comes out as +0.0.
+ *   workspace  at least dsel_lmhead_topk_workspace_bytes() bytes (per-split
+ *            partial lists); contents need no initialisation.
+ * Arithmetic: bf16 MFMA with fp32 accumulation; the order is taken on those
+ * fp32 logits.  Requirements: 16 <= vocab < 2^31, d % 64 == 0, rows >= 0, h
+ * and W 16-byte aligned. */
+size_t dsel_lmhead_topk_workspace_bytes(int64_t rows, int64_t vocab);
+dsel_status dsel_lmhead_topk(const uint16_t *h, const uint16_t *W, int64_t rows, int64_t vocab, int64_t d,
+                             int32_t *cand_id, float *cand_u, void *workspace, size_t workspace_bytes,
+                             dsel_stream_t stream);
+
 /* dyn_conv -- [P1] Method > Lightweight Local Convolution (eq. Conv_k), [P3]
  * "Suffix decay is local": the drafter's dynamic two-tap short convolution
  * over the positions of each drafted block,
