@@ -253,3 +253,89 @@ def lmhead_topk(h, W):
     cz = np.empty((rows, K + 1), np.float64)
     _check(_load().ora_lmhead_topk(_p(h), _p(W), rows, V, d, _p(cid), _p(cz)), "lmhead_topk")
     return cid, cz
+
+
+# ------------------------------------------------------------ ragged batches --
+# Block size is a per-request knob ("DFlash 2: Keep Drafting Parallel",
+# supplementary deployment notes: oMLX runs blocks of 5, the release tables use
+# 8 and 16; "DFlash 2: The Drafter Stopped Guessing Alone", "What to check on
+# your own serving": the block size is a knob).  A ragged batch keeps the
+# padded [batch, block] layout and gives each block its own length
+# block_len[b] in 0..block; block b is then exactly the selector (or
+# verification) run on that block alone at that length.  Padding positions
+# have no result: NaN (floats) and -1 (ids) here.
+
+
+def _lens(block_len, B: int, L: int) -> np.ndarray:
+    lens = np.asarray(block_len, np.int64).reshape(-1)
+    if lens.shape != (B,) or (lens < 0).any() or (lens > L).any():
+        raise ValueError(f"block_len must be [{B}] with entries in 0..{L}")
+    return lens
+
+
+def run_ragged(inp: Dict[str, np.ndarray], block_len, mode: int = GREEDY, T: float = 1.0,
+               vocab: Optional[int] = None):
+    """The whole selector on a ragged batch: block ``b`` is ``run`` on its
+    first ``block_len[b]`` positions alone; padding is NaN / -1."""
+    B, L = inp["logits"].shape[:2]
+    lens = _lens(block_len, B, L)
+    r = inp["W_A"].shape[0]
+    out = dict(cand_id=np.full((B, L, K), -1, np.int32), cand_u=np.full((B, L, K), np.nan, np.float32),
+               A_prev=np.full((B, L, K, r), np.nan), B_cur=np.full((B, L, K, r), np.nan),
+               G=np.full((B, L, r), np.nan), S=np.full((B, L, K, K), np.nan),
+               path_tok=np.full((B, L), -1, np.int32), path_slot=np.full((B, L), -1, np.int32),
+               path_s=np.full((B, L), np.nan), aux=np.full((B, L), np.nan), q=np.full((B, L, K), np.nan))
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        sub = dict(inp)
+        for k in ("logits", "h", "uniforms"):
+            if k in inp and inp[k] is not None:
+                sub[k] = np.ascontiguousarray(inp[k][b:b + 1, :n])
+        sub["verified"] = np.ascontiguousarray(inp["verified"][b:b + 1])
+        o = run(sub, mode, T, vocab)
+        for k in out:
+            out[k][b, :n] = o[k][0]
+    return out
+
+
+def verify_ragged(tlogits, block_len, cand_id, path_slot, q=None, mode: int = GREEDY, T: float = 1.0,
+                  u_acc=None, u_res=None, vocab: Optional[int] = None):
+    """Verification of a ragged batch: target rows ``[B, L+1, ld]``, block
+    ``b`` verified on its rows ``0 .. block_len[b]`` alone (row ``block_len[b]``
+    follows its last drafted token).  ``out_tok [B, L+1]`` holds the accepted
+    tokens, the extra token, then -1."""
+    tl = np.ascontiguousarray(tlogits)
+    B, L1 = tl.shape[:2]
+    L = L1 - 1
+    lens = _lens(block_len, B, L)
+    out = dict(n_acc=np.zeros(B, np.int32), out_tok=np.full((B, L + 1), -1, np.int32),
+               m_acc=np.full((B, L), np.nan), m_draw=np.full(B, np.nan))
+    for b in range(B):
+        n = int(lens[b])
+        sl = lambda a: None if a is None else np.ascontiguousarray(a[b:b + 1, :n])
+        o = verify(tl[b:b + 1, :n + 1], sl(cand_id), sl(path_slot), sl(q), mode, T, sl(u_acc),
+                   None if u_res is None else np.ascontiguousarray(u_res[b:b + 1]), vocab)
+        out["n_acc"][b] = o["n_acc"][0]
+        out["out_tok"][b, :n + 1] = o["out_tok"][0]
+        out["m_acc"][b, :n] = o["m_acc"][0]
+        out["m_draw"][b] = o["m_draw"][0]
+    return out
+
+
+def dyn_conv_ragged(x, x_prev, base, W_c, block_len):
+    """Dynamic convolution of a ragged batch: block ``b`` is ``dyn_conv`` on
+    its first ``block_len[b]`` positions alone; padding is NaN."""
+    B, L, d = x.shape
+    lens = _lens(block_len, B, L)
+    y = np.full((B, L, d), np.nan)
+    corr = np.full((B, L, 2 * (d // 16)), np.nan)
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        yb, cb = dyn_conv(x[b:b + 1, :n], x_prev[b:b + 1], base, W_c)
+        y[b, :n] = yb[0]
+        corr[b, :n] = cb[0]
+    return y, corr

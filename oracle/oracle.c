@@ -355,10 +355,11 @@ int ora_verify(const void *tlogits, int dtype, int64_t B, int64_t L, int64_t V, 
                const int32_t *cand_id, const int32_t *path_slot, const double *q, int mode,
                double T, const float *u_acc, const float *u_res, int32_t *n_acc,
                int32_t *out_tok, double *m_acc, double *m_draw) {
-    if (!tlogits || !cand_id || !path_slot || !n_acc || !out_tok || B < 0 || L < 1 || V < 1 || ld < V)
-        return -1;
+    /* L = 0 is a block that drafted nothing: no test, the extra token from row 0 */
+    if (!tlogits || !n_acc || !out_tok || B < 0 || L < 0 || V < 1 || ld < V) return -1;
+    if (L > 0 && (!cand_id || !path_slot)) return -1;
     if (dtype != 0 && dtype != 1) return -1;
-    if (mode == 1 && (!q || !u_acc || !u_res || !(T > 0.0))) return -1;
+    if (mode == 1 && (!u_res || !(T > 0.0) || (L > 0 && (!q || !u_acc)))) return -1;
     if (mode != 0 && mode != 1) return -1;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t b = 0; b < B; ++b) {

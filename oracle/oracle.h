@@ -79,7 +79,9 @@ int ora_step_table(const double *S, const float *uniforms, double T, int mode,
  * target logits: rows (b, t), t = 0..L (row L follows the block), ld elements
  * apart, fp32 (dtype 0) or bf16 bits (dtype 1).  The drafted token of position
  * t is cand_id[b,t,path_slot[b,t]], drawn from q[b,t,:] (the walk's 16-way
- * distribution over the candidates).
+ * distribution over the candidates).  L = 0 is allowed: a block that drafted
+ * nothing tests nothing and takes its extra token from row 0 (plain decoding);
+ * cand_id, path_slot, q and u_acc may then be NULL.
  *
  * mode 0 (greedy): accept while the drafted token is the target's arg max
  *   (ties to the lower id, NaN lowest); the first miss, or row L if all

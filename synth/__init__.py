@@ -45,6 +45,7 @@ K = 16  # candidates kept per draft position
 _T_LOGITS, _T_E, _T_WA, _T_WB, _T_WH, _T_H, _T_VER, _T_U, _T_INJ = range(1, 10)
 _T_TGT, _T_UACC, _T_URES = range(10, 13)
 _T_CX, _T_CXP, _T_CB, _T_CW = range(13, 17)  # dynamic convolution inputs
+_T_LEN = 17  # per-block lengths of a ragged batch
 _E_CHUNK = 256  # rows of E per seed child
 
 
@@ -258,6 +259,19 @@ def make_conv(cfg: Config, seed: int = 0, blocks: Optional[Iterable[int]] = None
     base[1] = 0.1 * rb.standard_normal(d, dtype=np.float32)
     W_c = _normal_bf16(_rng(seed, _T_CW), (2 * (d // 16), d), 0.1 / np.sqrt(d))
     return dict(x=x, x_prev=xp, base=f32_to_bf16_bits(base), W_c=W_c)
+
+
+def make_block_len(cfg: Config, seed: int = 0, choices: Optional[Iterable[int]] = None) -> np.ndarray:
+    """Per-block lengths of a ragged batch, ``[batch]`` int32 in ``0..block``,
+    each drawn uniformly from ``choices``.  The default mix is the block sizes
+    the pages run (5 on oMLX, 8 and 16 in the release tables) that fit
+    ``cfg.block``, plus ``cfg.block`` itself."""
+    if choices is None:
+        choices = sorted({c for c in (5, 8, 16) if c <= cfg.block} | {cfg.block})
+    choices = np.asarray(list(choices), np.int64)
+    if choices.size == 0 or (choices < 0).any() or (choices > cfg.block).any():
+        raise ValueError("block lengths must lie in 0..block")
+    return choices[_rng(seed, _T_LEN).integers(0, choices.size, size=cfg.batch)].astype(np.int32)
 
 
 def make(cfg: Config, seed: int = 0) -> Dict[str, np.ndarray]:
