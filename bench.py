@@ -182,7 +182,7 @@ def time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream):
     sp = C.c_void_p(stream.cuda_stream)
 
     def call():
-        st = lib.dsel_verify(P(d_tl), dt, B, L, V, V, P(cand_id), P(wres["path_slot"]),
+        st = lib.dsel_verify(P(d_tl), dt, B, L, None, V, V, P(cand_id), P(wres["path_slot"]),
                              P(q) if mode == 1 else None, mode, C.c_float(cfg.temperature),
                              P(d_ua) if mode == 1 else None, P(d_ur) if mode == 1 else None,
                              P(n_acc), P(out_tok), P(ws), wsb, sp)
@@ -235,7 +235,7 @@ def time_conv(args, cfg, stream):
     sp = C.c_void_p(stream.cuda_stream)
 
     def call():
-        st = lib.dsel_dyn_conv(P(x), P(xp), P(base), P(W), B, L, d, P(y), P(ws), wsb, sp)
+        st = lib.dsel_dyn_conv(P(x), P(xp), P(base), P(W), B, L, None, d, P(y), P(ws), wsb, sp)
         if st:
             raise RuntimeError(f"dsel_dyn_conv status {st}")
 
@@ -343,6 +343,8 @@ def main():
                     help="skip timing the verification of the drafted blocks (dsel_verify)")
     ap.add_argument("--no-conv", action="store_true",
                     help="skip timing the dynamic two-tap convolution unit (dsel_dyn_conv)")
+    ap.add_argument("--no-ragged", action="store_true",
+                    help="skip timing the same step on a ragged batch (per-block lengths)")
     ap.add_argument("--lmhead", action="store_true",
                     help="also time the LM head with the fused top-16 (dsel_lmhead_topk) and the unfused route")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -398,11 +400,12 @@ def main():
     ss = C.c_void_p(side.cuda_stream)
     fork = [torch.cuda.Event() for _ in range(2)]
 
-    def step(strm, ev=None):
+    def step(strm, ev=None, lens=None):
         # the gate GEMM needs no candidates: either it runs first, or on a side
         # stream beside the top-16 (the side stream first waits for the
-        # previous step).
+        # previous step).  `lens`: per-block lengths of a ragged batch.
         sp = C.c_void_p(strm.cuda_stream)
+        LN = P(lens) if lens is not None else None
         if ev is not None:
             ev[0].record(strm)
         if args.gate == "overlap":
@@ -410,24 +413,24 @@ def main():
             side.wait_event(fork[0])
         if args.gate == "overlap":
             s0 = lib.dsel_project_gate_overlap(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
-                                               P(d["verified"]), B, L, P(A_prev), P(G), ss)
+                                               P(d["verified"]), B, L, LN, P(A_prev), P(G), ss)
         else:
             s0 = lib.dsel_project_gate(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
-                                       P(d["verified"]), B, L, P(A_prev), P(G), P(pws), pwsb, sp)
+                                       P(d["verified"]), B, L, LN, P(A_prev), P(G), P(pws), pwsb, sp)
         if args.gate == "overlap":
             fork[1].record(side)
         if ev is not None:
             ev[1].record(strm)
-        s1 = lib.dsel_select_topk(P(d["logits"]), dt, B, L, V, V, P(cand_id), P(cand_u), P(ws), wsb, sp)
+        s1 = lib.dsel_select_topk(P(d["logits"]), dt, B, L, LN, V, V, P(cand_id), P(cand_u), P(ws), wsb, sp)
         if ev is not None:
             ev[2].record(strm)
         if args.gate == "overlap":
             strm.wait_event(fork[1])
         s2 = lib.dsel_project_cand(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_B"]), cfg.r, P(cand_id),
-                                   B, L, P(A_prev), P(B_cur), P(pws), pwsb, sp)
+                                   B, L, LN, P(A_prev), P(B_cur), P(pws), pwsb, sp)
         if ev is not None:
             ev[3].record(strm)
-        s3 = lib.dsel_score_pairs(P(cand_u), P(A_prev), P(B_cur), P(G), B, L, cfg.r, P(S),
+        s3 = lib.dsel_score_pairs(P(cand_u), P(A_prev), P(B_cur), P(G), B, L, LN, cfg.r, P(S),
                                   C.byref(wargs), sp)
         if ev is not None:
             ev[4].record(strm)
@@ -482,6 +485,38 @@ def main():
         del flush
         cold = stage_means(cevs)
 
+    # (4) a ragged batch: the same step with each block at its own length
+    # (the 5 / 8 / 16 mix), one HIP graph replayed K times
+    ragged = None
+    if not args.no_ragged and L > 1:
+        lens_np = synth.make_block_len(cfg)
+        lens = torch.from_numpy(lens_np).to(dev)
+        revs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            step(stream, revs[i], lens=lens)
+        torch.cuda.synchronize()
+        rgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(rgraph):
+            step(torch.cuda.current_stream(), lens=lens)
+        for _ in range(args.warmup):
+            rgraph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            rgraph.replay()
+        torch.cuda.synchronize()
+        ms_r = (time.perf_counter() - t0) * 1e3 / args.steps
+        assert ds.device_error() == 0
+        pos = int(lens_np.sum())
+        ragged = {"lengths": "each block %s positions, drawn uniformly"
+                             % " / ".join(map(str, sorted(set(lens_np.tolist())))),
+                  "positions": pos, "padded_positions": B * L,
+                  "ms_per_step": round(ms_r, 5), "blocks/s": round(B / (ms_r * 1e-3), 1),
+                  "positions/s": round(pos / (ms_r * 1e-3), 1),
+                  "uniform_positions/s": round(B * L / (wall / args.steps), 1),
+                  "stages_us": stage_means(revs)}
+        del rgraph
+
     verify = None if args.no_verify else time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream)
     conv = None if args.no_conv or cfg.d % 512 else time_conv(args, cfg, stream)
     lmhead = time_lmhead(args, cfg, d["E"], stream) if args.lmhead else None
@@ -531,6 +566,7 @@ def main():
         "verify": verify,
         "dyn_conv": conv,
         "lmhead_topk": lmhead,
+        "ragged": ragged,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)

@@ -58,20 +58,20 @@ def _load():
         P, I64, I32, SZ = C.c_void_p, C.c_int64, C.c_int32, C.c_size_t
         sig = {
             "dsel_topk_workspace_bytes": ([I64, I64, I32], SZ),
-            "dsel_select_topk": ([P, I32, I64, I64, I64, I64, P, P, P, SZ, P], I32),
-            "dsel_project": ([P, I64, I64, P, P, P, I64, P, P, P, I64, I64, P, P, P, P, SZ, P], I32),
+            "dsel_select_topk": ([P, I32, I64, I64, P, I64, I64, P, P, P, SZ, P], I32),
+            "dsel_project": ([P, I64, I64, P, P, P, I64, P, P, P, I64, I64, P, P, P, P, P, SZ, P], I32),
             "dsel_project_workspace_bytes": ([I64, I64, I64, I64], SZ),
-            "dsel_project_gate": ([P, I64, I64, P, P, I64, P, P, I64, I64, P, P, P, SZ, P], I32),
-            "dsel_project_gate_overlap": ([P, I64, I64, P, P, I64, P, P, I64, I64, P, P, P], I32),
-            "dsel_project_cand": ([P, I64, I64, P, P, I64, P, I64, I64, P, P, P, SZ, P], I32),
-            "dsel_score_pairs": ([P, P, P, P, I64, I64, I64, P, C.POINTER(WalkArgs), P], I32),
-            "dsel_walk": ([P, I64, I64, C.POINTER(WalkArgs), P], I32),
+            "dsel_project_gate": ([P, I64, I64, P, P, I64, P, P, I64, I64, P, P, P, P, SZ, P], I32),
+            "dsel_project_gate_overlap": ([P, I64, I64, P, P, I64, P, P, I64, I64, P, P, P, P], I32),
+            "dsel_project_cand": ([P, I64, I64, P, P, I64, P, I64, I64, P, P, P, P, SZ, P], I32),
+            "dsel_score_pairs": ([P, P, P, P, I64, I64, P, I64, P, C.POINTER(WalkArgs), P], I32),
+            "dsel_walk": ([P, I64, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_verify_workspace_bytes": ([I64, I64, I64], SZ),
             "dsel_dyn_conv_workspace_bytes": ([I64, I64, I64], SZ),
             "dsel_lmhead_topk_workspace_bytes": ([I64, I64], SZ),
             "dsel_lmhead_topk": ([P, P, I64, I64, I64, P, P, P, SZ, P], I32),
-            "dsel_dyn_conv": ([P, P, P, P, I64, I64, I64, P, P, SZ, P], I32),
-            "dsel_verify": ([P, I32, I64, I64, I64, I64, P, P, P, I32, C.c_float, P, P, P, P, P, SZ, P], I32),
+            "dsel_dyn_conv": ([P, P, P, P, I64, I64, P, I64, P, P, SZ, P], I32),
+            "dsel_verify": ([P, I32, I64, I64, P, I64, I64, P, P, P, I32, C.c_float, P, P, P, P, P, SZ, P], I32),
             "dsel_device_error": ([C.POINTER(C.c_int32), P], I32),
             "dsel_status_string": ([I32], C.c_char_p),
             "dsel_version": ([], I32),
@@ -114,16 +114,27 @@ def _need(t: torch.Tensor, name: str, dtype, shape=None):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _lens(block_len, B: int):
+    """Checked pointer of an optional ragged-batch length array ``[B]`` int32."""
+    if block_len is None:
+        return None
+    _need(block_len, "block_len", torch.int32, (B,))
+    return _ptr(block_len)
+
+
 def topk_workspace_bytes(rows: int, vocab: int, dtype: torch.dtype) -> int:
     dt = BF16 if dtype == torch.bfloat16 else F32
     return int(_load().dsel_topk_workspace_bytes(rows, vocab, dt))
 
 
 def select_topk(logits: torch.Tensor, vocab: Optional[int] = None, out=None, workspace=None,
-                stream=None):
+                stream=None, block_len=None):
     """Top-16 of every draft position.  ``logits [batch, block, ld]`` fp32 or bf16
     with unit stride in the last dim; the first ``vocab`` (default ``ld``) entries
-    of each row are used.  Returns ``cand_id [B,L,16] int32``, ``cand_u [B,L,16] fp32``."""
+    of each row are used.  Returns ``cand_id [B,L,16] int32``, ``cand_u [B,L,16] fp32``.
+    ``block_len`` (every call below takes it too): optional int32 ``[batch]`` of
+    valid positions per block (a ragged batch); padding is neither read nor
+    written."""
     if logits.dim() != 3:
         raise ValueError("logits must be [batch, block, ld]")
     if logits.dtype not in (torch.float32, torch.bfloat16):
@@ -157,13 +168,13 @@ def select_topk(logits: torch.Tensor, vocab: Optional[int] = None, out=None, wor
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = _load().dsel_select_topk(_ptr(logits), dt, B, L, V, ld, _ptr(cand_id), _ptr(cand_u),
+    st = _load().dsel_select_topk(_ptr(logits), dt, B, L, _lens(block_len, B), V, ld, _ptr(cand_id), _ptr(cand_u),
                                   _ptr(workspace), wsb, _stream(stream))
     _check(st, "dsel_select_topk")
     return cand_id, cand_u
 
 
-def project(E, W_A, W_B, W_H, h, cand_id, verified, out=None, stream=None):
+def project(E, W_A, W_B, W_H, h, cand_id, verified, out=None, stream=None, block_len=None):
     """``A_prev [B,L,16,r]``, ``B_cur [B,L,16,r]``, ``G [B,L,r]`` (fp32) from bf16
     ``E [V,d]``, ``W_* [r,d]``, ``h [B,L,d]``, int32 ``cand_id``, ``verified [B]``."""
     V, d = E.shape
@@ -184,7 +195,7 @@ def project(E, W_A, W_B, W_H, h, cand_id, verified, out=None, stream=None):
     ws = _project_workspace(B, L, d, r, dev)
     wsb = 0 if ws is None else ws.numel()
     st = _load().dsel_project(_ptr(E), V, d, _ptr(W_A), _ptr(W_B), _ptr(W_H), r, _ptr(h),
-                              _ptr(cand_id), _ptr(verified), B, L, _ptr(A_prev), _ptr(B_cur),
+                              _ptr(cand_id), _ptr(verified), B, L, _lens(block_len, B), _ptr(A_prev), _ptr(B_cur),
                               _ptr(G), _ptr(ws), wsb, _stream(stream))
     _check(st, "dsel_project")
     return A_prev, B_cur, G
@@ -199,7 +210,7 @@ def _project_workspace(B, L, d, r, dev):
     return torch.empty(n, dtype=torch.uint8, device=dev) if n else None
 
 
-def project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=None, stream=None):
+def project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=None, stream=None, block_len=None):
     """G and the position-0 predecessor rows of A_prev (needs no candidates)."""
     V, d = E.shape
     r = W_A.shape[0]
@@ -213,11 +224,12 @@ def project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=None, stream=Non
         workspace = _project_workspace(B, L, d, r, E.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _load().dsel_project_gate(_ptr(E), V, d, _ptr(W_A), _ptr(W_H), r, _ptr(h), _ptr(verified),
-                                   B, L, _ptr(A_prev), _ptr(G), _ptr(workspace), wsb, _stream(stream))
+                                   B, L, _lens(block_len, B), _ptr(A_prev), _ptr(G), _ptr(workspace), wsb,
+                                   _stream(stream))
     _check(st, "dsel_project_gate")
 
 
-def project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=None):
+def project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=None, block_len=None):
     """project_gate with one workgroup per output tile and no workspace, for
     running beside select_topk on another stream."""
     V, d = E.shape
@@ -229,11 +241,11 @@ def project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=None):
     _need(A_prev, "A_prev", torch.float32, (B, L, K, r))
     _need(G, "G", torch.float32, (B, L, r))
     st = _load().dsel_project_gate_overlap(_ptr(E), V, d, _ptr(W_A), _ptr(W_H), r, _ptr(h), _ptr(verified),
-                                           B, L, _ptr(A_prev), _ptr(G), _stream(stream))
+                                           B, L, _lens(block_len, B), _ptr(A_prev), _ptr(G), _stream(stream))
     _check(st, "dsel_project_gate_overlap")
 
 
-def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=None, stream=None):
+def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=None, stream=None, block_len=None):
     """B_cur and the predecessor rows of A_prev for positions >= 1."""
     V, d = E.shape
     r = W_A.shape[0]
@@ -247,7 +259,7 @@ def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=None, stream=Non
         workspace = _project_workspace(B, L, d, r, E.device)
     wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = _load().dsel_project_cand(_ptr(E), V, d, _ptr(W_A), _ptr(W_B), r, _ptr(cand_id), B, L,
-                                   _ptr(A_prev), _ptr(B_cur), _ptr(workspace), wsb, _stream(stream))
+                                   _lens(block_len, B), _ptr(A_prev), _ptr(B_cur), _ptr(workspace), wsb, _stream(stream))
     _check(st, "dsel_project_cand")
 
 
@@ -285,7 +297,7 @@ def _walk_args(cand_id, mode, temperature, uniforms, want_q, want_s):
 
 def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Optional[int] = None,
                 cand_id=None, temperature: float = 1.0, uniforms=None, want_q: bool = False,
-                stream=None):
+                stream=None, block_len=None):
     """Pair scores ``S [B,L,16,16]`` (returned if ``want_S``) and, when
     ``walk_mode`` is given, the walk over them.  Returns a dict."""
     B, L, _, r = A_prev.shape
@@ -301,7 +313,7 @@ def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Option
             raise ValueError("the walk needs cand_id")
         _need(cand_id, "cand_id", torch.int32, (B, L, K))
         wa, res = _walk_args(cand_id, walk_mode, temperature, uniforms, want_q, True)
-    st = _load().dsel_score_pairs(_ptr(cand_u), _ptr(A_prev), _ptr(B_cur), _ptr(G), B, L, r,
+    st = _load().dsel_score_pairs(_ptr(cand_u), _ptr(A_prev), _ptr(B_cur), _ptr(G), B, L, _lens(block_len, B), r,
                                   _ptr(S), C.byref(wa) if wa is not None else None, _stream(stream))
     _check(st, "dsel_score_pairs")
     if want_S:
@@ -310,13 +322,13 @@ def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Option
 
 
 def walk(S, cand_id, mode: int = GREEDY, temperature: float = 1.0, uniforms=None,
-         want_q: bool = False, stream=None):
+         want_q: bool = False, stream=None, block_len=None):
     """The walk alone over ``S [B,L,16,16]`` fp32."""
     B, L = S.shape[:2]
     _need(S, "S", torch.float32, (B, L, K, K))
     _need(cand_id, "cand_id", torch.int32, (B, L, K))
     wa, res = _walk_args(cand_id, mode, temperature, uniforms, want_q, True)
-    _check(_load().dsel_walk(_ptr(S), B, L, C.byref(wa), _stream(stream)), "dsel_walk")
+    _check(_load().dsel_walk(_ptr(S), B, L, _lens(block_len, B), C.byref(wa), _stream(stream)), "dsel_walk")
     return res
 
 
@@ -350,7 +362,7 @@ def dyn_conv_workspace_bytes(batch: int, block: int, d: int) -> int:
     return int(_load().dsel_dyn_conv_workspace_bytes(batch, block, d))
 
 
-def dyn_conv(x, x_prev, base, W_c, y=None, workspace=None, stream=None):
+def dyn_conv(x, x_prev, base, W_c, y=None, workspace=None, stream=None, block_len=None):
     """Dynamic two-tap short convolution of the drafter over each block's
     positions: ``x [B, L, d]``, ``x_prev [B, d]``, ``base [2, d]``,
     ``W_c [2 d / 16, d]``, all bf16; returns ``y [B, L, d]`` bf16."""
@@ -366,7 +378,8 @@ def dyn_conv(x, x_prev, base, W_c, y=None, workspace=None, stream=None):
         wsb = dyn_conv_workspace_bytes(B, L, d)
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
     wsb = workspace.numel() * workspace.element_size()
-    st = _load().dsel_dyn_conv(_ptr(x), _ptr(x_prev), _ptr(base), _ptr(W_c), B, L, d, _ptr(y), _ptr(workspace),
+    st = _load().dsel_dyn_conv(_ptr(x), _ptr(x_prev), _ptr(base), _ptr(W_c), B, L, _lens(block_len, B), d,
+                               _ptr(y), _ptr(workspace),
                                wsb, _stream(stream))
     _check(st, "dsel_dyn_conv")
     return y
@@ -377,7 +390,8 @@ def verify_workspace_bytes(batch: int, block: int, vocab: int) -> int:
 
 
 def verify(target_logits, cand_id, path_slot, q=None, mode: int = GREEDY, temperature: float = 1.0,
-           u_acc=None, u_res=None, vocab: Optional[int] = None, workspace=None, stream=None):
+           u_acc=None, u_res=None, vocab: Optional[int] = None, workspace=None, stream=None,
+           block_len=None):
     """Verify drafted blocks against target logits ``[B, L+1, ld]`` (fp32 or
     bf16): returns ``(n_accepted [B] int32, out_tok [B, L+1] int32)``."""
     B, L1, ld = target_logits.shape
@@ -401,7 +415,8 @@ def verify(target_logits, cand_id, path_slot, q=None, mode: int = GREEDY, temper
     if workspace is None:
         workspace = torch.empty(max(verify_workspace_bytes(B, L, V), 1), dtype=torch.uint8, device=dev)
     wsb = workspace.numel() * workspace.element_size()
-    st = _load().dsel_verify(_ptr(target_logits), dt, B, L, V, ld, _ptr(cand_id), _ptr(path_slot),
+    st = _load().dsel_verify(_ptr(target_logits), dt, B, L, _lens(block_len, B), V, ld, _ptr(cand_id),
+                             _ptr(path_slot),
                              _ptr(q) if mode == SAMPLED else None, int(mode), float(temperature),
                              _ptr(u_acc) if mode == SAMPLED else None,
                              _ptr(u_res) if mode == SAMPLED else None, _ptr(n_acc), _ptr(out_tok),
@@ -412,7 +427,8 @@ def verify(target_logits, cand_id, path_slot, q=None, mode: int = GREEDY, temper
 
 def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
                 temperature: float = 1.0, uniforms=None, vocab: Optional[int] = None,
-                want_S: bool = False, want_q: bool = False, overlap: bool = False, stream=None):
+                want_S: bool = False, want_q: bool = False, overlap: bool = False, stream=None,
+                block_len=None):
     """The whole selector: top-16, projections, pair scores and the fused walk.
 
     With ``overlap`` the gate GEMM (which needs no candidates) runs on a side
@@ -430,14 +446,15 @@ def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
     if overlap:
         side = side_stream(dev)
         side.wait_stream(main)
-        project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=side)
-        cand_id, cand_u = select_topk(logits, vocab, stream=main)
+        project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=side, block_len=block_len)
+        cand_id, cand_u = select_topk(logits, vocab, stream=main, block_len=block_len)
         main.wait_stream(side)
     else:
-        project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=ws, stream=main)
-        cand_id, cand_u = select_topk(logits, vocab, stream=main)
-    project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=ws, stream=main)
+        project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=ws, stream=main, block_len=block_len)
+        cand_id, cand_u = select_topk(logits, vocab, stream=main, block_len=block_len)
+    project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=ws, stream=main, block_len=block_len)
     res = score_pairs(cand_u, A_prev, B_cur, G, want_S=want_S, walk_mode=mode, cand_id=cand_id,
-                      temperature=temperature, uniforms=uniforms, want_q=want_q, stream=main)
+                      temperature=temperature, uniforms=uniforms, want_q=want_q, stream=main,
+                      block_len=block_len)
     res.update(cand_id=cand_id, cand_u=cand_u, A_prev=A_prev, B_cur=B_cur, G=G)
     return res

@@ -130,4 +130,24 @@ __device__ __forceinline__ void widen_vec(const u32x4 &w, float (&x)[BF16 ? 8 : 
 // is a single translation unit, so this is its only definition.
 __device__ int g_device_error = 0;
 
+// Ragged batches keep the padded [batch, L] layout with a valid length per
+// block.  The valid positions of block b: len[b], or L for a uniform batch
+// (len == nullptr).  A length outside [0, L] counts as 0 (the block is empty)
+// and sets bit 2 (DSEL_DEVERR_BLOCK_LEN) of the device error word.
+__device__ __forceinline__ int block_len_of(const int32_t *len, int64_t b, int L) {
+    if (len == nullptr) return L;
+    const int n = len[b];
+    if (n >= 0 && n <= L) return n;
+    atomicOr(&g_device_error, 2);
+    return 0;
+}
+
+// Is flat position i = b L + t (i < 2^31) of a padded batch a real one
+// (t < the length of block b)?  Always, for a uniform batch.
+__device__ __forceinline__ bool position_live(const int32_t *len, uint32_t i, int L) {
+    if (len == nullptr) return true;
+    const uint32_t b = i / (uint32_t)L;
+    return (int)(i - b * (uint32_t)L) < block_len_of(len, b, L);
+}
+
 }  // namespace dsel

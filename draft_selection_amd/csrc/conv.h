@@ -28,6 +28,7 @@ struct ConvParams {
     const uint16_t *x, *x_prev, *base, *W_c;
     uint16_t *y;
     int B, L, d;
+    const int32_t *len;  // ragged batch: valid positions per block (nullptr: all L)
     int64_t M;     // B L positions
     int N;         // 2 G correction columns
     int mt, nt;    // 128-row tiles, column tiles
@@ -61,14 +62,19 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void conv_corr_kernel(ConvParams 
     const uint32_t lane = lane_id();
     const int wave = threadIdx.x >> 6;
 
-    // rows past M load row 0 and are never stored
+    // rows past M and padding positions load row 0 and are never stored
     const uint16_t *xsrc[XI];
+    uint32_t xlive = 0;
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
         const int row = 8 * (wave + NW * u) + (int)(lane >> 3);
         const int64_t m = m0 + row;
-        xsrc[u] = p.x + (m < p.M ? m : 0) * d + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
+        const bool live = m < p.M && position_live(p.len, (uint32_t)m, p.L);
+        if (live) xlive |= 1u << u;
+        xsrc[u] = p.x + (live ? m : 0) * d + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
     }
+    // a tile of padding only has nothing to store (ragged batches)
+    if (p.len && !__syncthreads_or(xlive != 0)) return;
     floatx16 acc[T::TM][T::TN];
 #pragma unroll
     for (int i = 0; i < T::TM; ++i)
@@ -79,9 +85,10 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void conv_corr_kernel(ConvParams 
     if (k1 > k0) mma_tile_dma<T>(xsrc, p.W_c + (int64_t)n0 * d, d, k0, k1, Xs, Ws, acc);
 
     float *out = p.part + (int64_t)ks * p.M * p.N;
+    if (p.len) tile_row_mask<NW, XI>(xlive, Xs, xlive);  // workgroup-uniform branch
     for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) {
         const int64_t m = m0 + rl;
-        if (m < p.M) *(floatx4 *)(out + m * p.N + n0 + cl) = v;
+        if (p.len ? tile_row_live(Xs, rl) : m < p.M) *(floatx4 *)(out + m * p.N + n0 + cl) = v;
     });
 }
 
@@ -98,6 +105,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 __global__ __launch_bounds__(256) void conv_apply_kernel(ConvParams p) {
     extern __shared__ float corr[];  // [N]
     const int64_t m = blockIdx.x;
+    if (!position_live(p.len, (uint32_t)m, p.L)) return;  // padding position (ragged batches)
     const int tid = (int)threadIdx.x;
     const int N = p.N, G = p.d / 16;
     for (int n = tid; n < N; n += 256) {

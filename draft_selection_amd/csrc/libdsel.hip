@@ -68,7 +68,8 @@ DSEL_API size_t dsel_topk_workspace_bytes(int64_t rows, int64_t vocab, dsel_dtyp
 }
 
 DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t batch,
-                                      int64_t block, int64_t vocab, int64_t ld, int32_t *cand_id,
+                                      int64_t block, const int32_t *block_len, int64_t vocab, int64_t ld,
+                                      int32_t *cand_id,
                                       float *cand_u, void *workspace, size_t workspace_bytes,
                                       dsel_stream_t stream) {
     if (dt != DSEL_F32 && dt != DSEL_BF16) return DSEL_E_DTYPE;
@@ -78,7 +79,8 @@ DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t
     if (rows == 0) return DSEL_OK;  // nothing to read or write; pointers may be NULL
     if (!logits || !cand_id || !cand_u) return DSEL_E_ARG;
     const size_t es = dt == DSEL_BF16 ? 2 : 4;
-    if (!aligned(logits, es) || !aligned(cand_id, 4) || !aligned(cand_u, 4)) return DSEL_E_ALIGN;
+    if (!aligned(logits, es) || !aligned(cand_id, 4) || !aligned(cand_u, 4) || !aligned(block_len, 4))
+        return DSEL_E_ALIGN;
     if (ld > INT64_MAX / (int64_t)es / rows) return DSEL_E_ARG;
     const int ns = topk_nsplit(rows, vocab);
     if ((int64_t)ns * rows >= (int64_t)INT_MAX) return DSEL_E_ARG;
@@ -92,6 +94,8 @@ DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t
     p.V = vocab;
     p.ld = ld;
     p.nsplit = ns;
+    p.L = (int)block;
+    p.len = block_len;
     p.cand_id = cand_id;
     p.cand_u = cand_u;
     p.partial = (uint64_t *)workspace;
@@ -138,13 +142,13 @@ namespace {
 // K split and no workspace.
 dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
                               const uint16_t *W_H, int64_t r, const uint16_t *h, const int32_t *verified,
-                              int64_t batch, int64_t block, float *A_prev, float *G, void *workspace,
-                              size_t workspace_bytes, bool split, dsel_stream_t stream) {
+                              int64_t batch, int64_t block, const int32_t *block_len, float *A_prev, float *G,
+                              void *workspace, size_t workspace_bytes, bool split, dsel_stream_t stream) {
     dsel_status st = check_project_common(E, vocab, d, r, batch, block);
     if (st != DSEL_OK || batch == 0) return st;
     if (!W_A || !W_H || !h || !verified || !A_prev || !G) return DSEL_E_ARG;
     if (!aligned(W_A, 16) || !aligned(W_H, 16) || !aligned(h, 16) || !aligned(verified, 4) ||
-        !aligned(A_prev, 16) || !aligned(G, 16))
+        !aligned(A_prev, 16) || !aligned(G, 16) || !aligned(block_len, 4))
         return DSEL_E_ALIGN;
     const size_t need = split ? gate_workspace_bytes(batch, block, d, r) : 0;
     if (need && (!workspace || workspace_bytes < need)) return DSEL_E_WORKSPACE;
@@ -160,6 +164,7 @@ dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const
     p.ver = verified;
     p.B = (int)batch;
     p.L = (int)block;
+    p.len = block_len;
     p.A_prev = A_prev;
     p.G = G;
     p.part = (float *)workspace;
@@ -187,30 +192,31 @@ dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const
 DSEL_API dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d,
                                        const uint16_t *W_A, const uint16_t *W_H, int64_t r,
                                        const uint16_t *h, const int32_t *verified, int64_t batch,
-                                       int64_t block, float *A_prev, float *G, void *workspace,
-                                       size_t workspace_bytes, dsel_stream_t stream) {
-    return project_gate_impl(E, vocab, d, W_A, W_H, r, h, verified, batch, block, A_prev, G, workspace,
-                             workspace_bytes, true, stream);
+                                       int64_t block, const int32_t *block_len, float *A_prev, float *G,
+                                       void *workspace, size_t workspace_bytes, dsel_stream_t stream) {
+    return project_gate_impl(E, vocab, d, W_A, W_H, r, h, verified, batch, block, block_len, A_prev, G,
+                             workspace, workspace_bytes, true, stream);
 }
 
 DSEL_API dsel_status dsel_project_gate_overlap(const uint16_t *E, int64_t vocab, int64_t d,
                                                const uint16_t *W_A, const uint16_t *W_H, int64_t r,
                                                const uint16_t *h, const int32_t *verified, int64_t batch,
-                                               int64_t block, float *A_prev, float *G, dsel_stream_t stream) {
-    return project_gate_impl(E, vocab, d, W_A, W_H, r, h, verified, batch, block, A_prev, G, nullptr, 0, false,
-                             stream);
+                                               int64_t block, const int32_t *block_len, float *A_prev,
+                                               float *G, dsel_stream_t stream) {
+    return project_gate_impl(E, vocab, d, W_A, W_H, r, h, verified, batch, block, block_len, A_prev, G, nullptr,
+                             0, false, stream);
 }
 
 DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d,
                                        const uint16_t *W_A, const uint16_t *W_B, int64_t r,
                                        const int32_t *cand_id, int64_t batch, int64_t block,
-                                       float *A_prev, float *B_cur, void *workspace,
-                                       size_t workspace_bytes, dsel_stream_t stream) {
+                                       const int32_t *block_len, float *A_prev, float *B_cur,
+                                       void *workspace, size_t workspace_bytes, dsel_stream_t stream) {
     dsel_status st = check_project_common(E, vocab, d, r, batch, block);
     if (st != DSEL_OK || batch == 0) return st;
     if (!W_A || !W_B || !cand_id || !A_prev || !B_cur) return DSEL_E_ARG;
     if (!aligned(W_A, 16) || !aligned(W_B, 16) || !aligned(cand_id, 4) || !aligned(A_prev, 16) ||
-        !aligned(B_cur, 16))
+        !aligned(B_cur, 16) || !aligned(block_len, 4))
         return DSEL_E_ALIGN;
     const size_t cneed = cand_workspace_bytes(batch, block, d, r);
     const size_t coff = cand_workspace_offset(batch, block, d, r);
@@ -225,6 +231,7 @@ DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t
     p.WB = W_B;
     p.cand = cand_id;
     p.L = (int)block;
+    p.len = block_len;
     p.M = batch * block * kK;
     p.A_prev = A_prev;
     p.B_cur = B_cur;
@@ -256,19 +263,19 @@ DSEL_API dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, c
                                   const uint16_t *W_B, const uint16_t *W_H, int64_t r,
                                   const uint16_t *h, const int32_t *cand_id,
                                   const int32_t *verified, int64_t batch, int64_t block,
-                                  float *A_prev, float *B_cur, float *G, void *workspace,
-                                  size_t workspace_bytes, dsel_stream_t stream) {
+                                  const int32_t *block_len, float *A_prev, float *B_cur, float *G,
+                                  void *workspace, size_t workspace_bytes, dsel_stream_t stream) {
     dsel_status st = check_project_common(E, vocab, d, r, batch, block);
     if (st != DSEL_OK || batch == 0) return st;
     if (!W_A || !W_B || !W_H || !h || !cand_id || !verified || !A_prev || !B_cur || !G)
         return DSEL_E_ARG;
     const size_t need = dsel_project_workspace_bytes(batch, block, d, r);
     if (need && (!workspace || workspace_bytes < need)) return DSEL_E_WORKSPACE;
-    st = dsel_project_gate(E, vocab, d, W_A, W_H, r, h, verified, batch, block, A_prev, G, workspace,
-                           workspace_bytes, stream);
+    st = dsel_project_gate(E, vocab, d, W_A, W_H, r, h, verified, batch, block, block_len, A_prev, G,
+                           workspace, workspace_bytes, stream);
     if (st != DSEL_OK) return st;
-    return dsel_project_cand(E, vocab, d, W_A, W_B, r, cand_id, batch, block, A_prev, B_cur, workspace,
-                             workspace_bytes, stream);
+    return dsel_project_cand(E, vocab, d, W_A, W_B, r, cand_id, batch, block, block_len, A_prev, B_cur,
+                             workspace, workspace_bytes, stream);
 }
 
 namespace {
@@ -296,8 +303,9 @@ dsel_status launch_walk(PairParams &p, dsel_stream_t stream) {
 }  // namespace
 
 DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const float *B_cur,
-                                      const float *G, int64_t batch, int64_t block, int64_t r,
-                                      float *S, const dsel_walk_args *walk, dsel_stream_t stream) {
+                                      const float *G, int64_t batch, int64_t block,
+                                      const int32_t *block_len, int64_t r, float *S,
+                                      const dsel_walk_args *walk, dsel_stream_t stream) {
     if (batch < 0 || batch >= (int64_t)INT_MAX / DSEL_MAX_BLOCK || block < 1 || block > DSEL_MAX_BLOCK)
         return DSEL_E_ARG;
     if (r < 32 || r > DSEL_MAX_RANK || r % 32 != 0) return DSEL_E_ARG;
@@ -305,7 +313,7 @@ DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, 
     if (batch == 0) return DSEL_OK;  // nothing to read or write; pointers may be NULL
     if (!cand_u || !A_prev || !B_cur || !G || !S) return DSEL_E_ARG;
     if (!aligned(A_prev, 16) || !aligned(B_cur, 16) || !aligned(G, 16) || !aligned(cand_u, 4) ||
-        !aligned(S, 4))
+        !aligned(S, 4) || !aligned(block_len, 4))
         return DSEL_E_ALIGN;
     PairParams p = {};
     if (walk) {
@@ -318,6 +326,7 @@ DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, 
     p.G = G;
     p.B = (int)batch;
     p.L = (int)block;
+    p.len = block_len;
     p.r = (int)r;
     p.S = S;
     p.S_in = S;
@@ -327,20 +336,21 @@ DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, 
     return launch_walk(p, stream);
 }
 
-DSEL_API dsel_status dsel_walk(const float *S, int64_t batch, int64_t block,
+DSEL_API dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const int32_t *block_len,
                                const dsel_walk_args *walk, dsel_stream_t stream) {
     if (!walk) return DSEL_E_ARG;
     if (batch < 0 || batch >= (int64_t)INT_MAX || block < 1 || block > DSEL_MAX_BLOCK) return DSEL_E_ARG;
     if (walk->mode != DSEL_GREEDY && walk->mode != DSEL_SAMPLED) return DSEL_E_DTYPE;
     if (batch == 0) return DSEL_OK;  // nothing to read or write; pointers may be NULL
     if (!S) return DSEL_E_ARG;
-    if (!aligned(S, 4)) return DSEL_E_ALIGN;
+    if (!aligned(S, 4) || !aligned(block_len, 4)) return DSEL_E_ALIGN;
     PairParams p = {};
     dsel_status s = check_walk(walk, &p.w);
     if (s != DSEL_OK) return s;
     p.S_in = S;
     p.B = (int)batch;
     p.L = (int)block;
+    p.len = block_len;
     return launch_walk(p, stream);
 }
 
@@ -412,6 +422,8 @@ DSEL_API dsel_status dsel_lmhead_topk(const uint16_t *h, const uint16_t *W, int6
     tp.V = vocab;
     tp.ld = vocab;
     tp.nsplit = p.nvs;
+    tp.L = 1;
+    tp.len = nullptr;
     tp.cand_id = cand_id;
     tp.cand_u = cand_u;
     tp.partial = p.partial;
@@ -426,13 +438,15 @@ DSEL_API size_t dsel_dyn_conv_workspace_bytes(int64_t batch, int64_t block, int6
 }
 
 DSEL_API dsel_status dsel_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base,
-                                   const uint16_t *W_c, int64_t batch, int64_t block, int64_t d, uint16_t *y,
-                                   void *workspace, size_t workspace_bytes, dsel_stream_t stream) {
+                                   const uint16_t *W_c, int64_t batch, int64_t block,
+                                   const int32_t *block_len, int64_t d, uint16_t *y, void *workspace,
+                                   size_t workspace_bytes, dsel_stream_t stream) {
     if (batch < 0 || block < 1 || d < 512 || d % 512 != 0 || d > (1 << 16)) return DSEL_E_ARG;
     if (batch > (int64_t)INT_MAX / block) return DSEL_E_ARG;
     if (batch == 0) return DSEL_OK;
     if (!x || !x_prev || !base || !W_c || !y) return DSEL_E_ARG;
-    if (!aligned(x, 16) || !aligned(x_prev, 16) || !aligned(base, 16) || !aligned(W_c, 16) || !aligned(y, 16))
+    if (!aligned(x, 16) || !aligned(x_prev, 16) || !aligned(base, 16) || !aligned(W_c, 16) || !aligned(y, 16) ||
+        !aligned(block_len, 4))
         return DSEL_E_ALIGN;
     const size_t need = conv_workspace_bytes(batch, block, d);
     if (!workspace || workspace_bytes < need) return DSEL_E_WORKSPACE;
@@ -445,6 +459,7 @@ DSEL_API dsel_status dsel_dyn_conv(const uint16_t *x, const uint16_t *x_prev, co
     p.y = y;
     p.B = (int)batch;
     p.L = (int)block;
+    p.len = block_len;
     p.d = (int)d;
     p.M = batch * block;
     p.N = (int)(d / 8);
@@ -472,7 +487,8 @@ DSEL_API size_t dsel_verify_workspace_bytes(int64_t batch, int64_t block, int64_
 }
 
 DSEL_API dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64_t batch,
-                                 int64_t block, int64_t vocab, int64_t ld, const int32_t *cand_id,
+                                 int64_t block, const int32_t *block_len, int64_t vocab, int64_t ld,
+                                 const int32_t *cand_id,
                                  const int32_t *path_slot, const float *q, dsel_walk_mode mode,
                                  float temperature, const float *u_acc, const float *u_res,
                                  int32_t *n_accepted, int32_t *out_tok, void *workspace,
@@ -491,7 +507,8 @@ DSEL_API dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64
     if (ld > INT64_MAX / es / rows) return DSEL_E_ARG;
     if (!aligned(target_logits, 16) || (ld * es) % 16 != 0) return DSEL_E_ALIGN;
     if (!aligned(cand_id, 4) || !aligned(path_slot, 4) || !aligned(n_accepted, 4) || !aligned(out_tok, 4) ||
-        (q && !aligned(q, 4)) || (u_acc && !aligned(u_acc, 4)) || (u_res && !aligned(u_res, 4)))
+        (q && !aligned(q, 4)) || (u_acc && !aligned(u_acc, 4)) || (u_res && !aligned(u_res, 4)) ||
+        !aligned(block_len, 4))
         return DSEL_E_ALIGN;
     const size_t need = verify_workspace_bytes(batch, block, vocab);
     if (!workspace || workspace_bytes < need) return DSEL_E_WORKSPACE;
@@ -503,6 +520,7 @@ DSEL_API dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64
     p.ld = ld;
     p.B = (int)batch;
     p.L = (int)block;
+    p.len = block_len;
     p.scale = mode == DSEL_SAMPLED ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
     p.cand_id = cand_id;
     p.path_slot = path_slot;

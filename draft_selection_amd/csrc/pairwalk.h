@@ -39,6 +39,7 @@ struct PairParams {
     const float *cand_u, *A_prev, *B_cur, *G;
     const float *S_in;  // stand-alone walk: scores to walk
     int B, L, r;
+    const int32_t *len;  // ragged batch: valid positions per block (nullptr: all L)
     float *S;  // scores out
     WalkParams w;
 };
@@ -145,7 +146,8 @@ __global__ __launch_bounds__(256) void pair_kernel(PairParams p) {
     constexpr int NS = R / 16;              // 16-wide slices of the rank (R % 32 == 0)
     constexpr int SPW = (NS + 3) / 4;       // slices per wave (the last waves may get fewer)
     const int64_t bt = blockIdx.x;
-    const int t = (int)(bt % p.L);
+    if (!position_live(p.len, blockIdx.x, p.L)) return;  // padding position (ragged batches)
+    const int t = (int)(blockIdx.x % (uint32_t)p.L);
     const int wave = (int)(threadIdx.x >> 6);
     const uint32_t lane = lane_id();
     const int fr = lane & 15, fg = lane >> 4;
@@ -164,11 +166,16 @@ __global__ __launch_bounds__(256) void pair_kernel(PairParams p) {
     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int q = 0; q < SPW; ++q) {
-        if (wave + 4 * q >= NS) break;
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q].x * g[q].x, b[q].x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q].y * g[q].y, b[q].y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q].z * g[q].z, b[q].z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[q].w * g[q].w, b[q].w, acc, 0, 0, 0);
+        // A wave past the last slice multiplies zeros instead of branching, so
+        // every load above stays ahead of the first MFMA.
+        const bool has = wave + 4 * q < NS;
+        const float4 ag = has ? float4{a[q].x * g[q].x, a[q].y * g[q].y, a[q].z * g[q].z, a[q].w * g[q].w}
+                              : float4{0.f, 0.f, 0.f, 0.f};
+        const float4 bb = has ? b[q] : float4{0.f, 0.f, 0.f, 0.f};
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.x, bb.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.y, bb.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.z, bb.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.w, bb.w, acc, 0, 0, 0);
     }
     __shared__ floatx4 part[4][kWave];
     part[wave][lane] = acc;
@@ -198,10 +205,12 @@ __global__ __launch_bounds__(1024) void walk_kernel(PairParams p) {
     sh.ch = (uint8_t *)(sh.row + L);
 
     const int b = blockIdx.x;
+    const int n = block_len_of(p.len, b, L);  // positions to walk (ragged batches: the block's own)
+    if (n == 0) return;
     const int nwave = blockDim.x / kWave;
     const int wave = threadIdx.x / kWave;
     const uint32_t lane = lane_id();
-    for (int t = wave; t < L; t += nwave) {
+    for (int t = wave; t < n; t += nwave) {
         const int64_t bt = (int64_t)b * L + t;
         float s[4];
 #pragma unroll
@@ -212,13 +221,13 @@ __global__ __launch_bounds__(1024) void walk_kernel(PairParams p) {
     __syncthreads();
     if (threadIdx.x == 0) {
         int row = 0;  // the last verified token
-        for (int t = 0; t < L; ++t) {
+        for (int t = 0; t < n; ++t) {
             sh.row[t] = row;
             row = sh.ch[t * kK + row];
         }
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < L * kK; e += blockDim.x) {
+    for (int e = threadIdx.x; e < n * kK; e += blockDim.x) {
         const int t = e / kK, j = e % kK;
         const int64_t bt = (int64_t)b * L + t;
         const int row = sh.row[t];

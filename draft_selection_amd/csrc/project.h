@@ -324,22 +324,39 @@ __device__ __forceinline__ void mma_tile_dma_lean(const uint16_t *const (&xsrc)[
 // lanes with lane % 8 == 0 of wave w as rows 8 (w + NW u) + lane / 8, u < XI;
 // bit u of `xok` says the row's source was valid.  Each (wave, u) pair owns one
 // byte of the mask, so word q of `lds` (read as uint32) afterwards holds rows
-// 32 q .. 32 q + 31.  Call after the main loop: LDS is reused, and the leading
-// barrier also retires every wave's last LDS-DMA.
+// 32 q .. 32 q + 31.  A second mask, `xlive` (the row is a real position of
+// the batch, whatever its token), goes to words 4 .. 7 the same way.  Call after
+// the main loop: LDS is reused, and the leading barrier also retires every
+// wave's last LDS-DMA.
 template <int NW, int XI>
-__device__ __forceinline__ void tile_row_mask(uint32_t xok, uint16_t *lds) {
+__device__ __forceinline__ void tile_row_mask(uint32_t xok, uint16_t *lds, uint32_t xlive = 0u) {
     uint8_t *bytes = (uint8_t *)lds;
     const int wave = threadIdx.x >> 6;
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
         const uint64_t b = ballot(((xok >> u) & 1u) != 0);
-        uint32_t byte = 0;
+        const uint64_t bl = ballot(((xlive >> u) & 1u) != 0);
+        uint32_t byte = 0, bytel = 0;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) byte |= (uint32_t)((b >> (8 * k)) & 1u) << k;
-        if (lane_id() == 0) bytes[wave + NW * u] = (uint8_t)byte;
+        for (int k = 0; k < 8; ++k) {
+            byte |= (uint32_t)((b >> (8 * k)) & 1u) << k;
+            bytel |= (uint32_t)((bl >> (8 * k)) & 1u) << k;
+        }
+        if (lane_id() == 0) {
+            bytes[wave + NW * u] = (uint8_t)byte;
+            bytes[16 + wave + NW * u] = (uint8_t)bytel;
+        }
     }
     __syncthreads();
+}
+
+// Bit rl of the masks tile_row_mask left in LDS.
+__device__ __forceinline__ bool tile_row_ok(const uint16_t *lds, int rl) {
+    return (((const uint32_t *)lds)[rl >> 5] >> (rl & 31)) & 1u;
+}
+__device__ __forceinline__ bool tile_row_live(const uint16_t *lds, int rl) {
+    return (((const uint32_t *)lds)[4 + (rl >> 5)] >> (rl & 31)) & 1u;
 }
 
 // The accumulator layout of v_mfma_f32_32x32x16 gives lane l the column l % 32
@@ -401,6 +418,7 @@ struct CandParams {
     const uint16_t *WA, *WB;
     const int32_t *cand;
     int L;
+    const int32_t *len;  // ragged batch: valid positions per block (nullptr: all L)
     int64_t M;        // batch * block * 16 gathered rows
     int mt, mt_pad;   // row tiles (mt_pad: rounded up to a multiple of 8)
     int nside;        // column tiles per side (r / BN)
@@ -465,8 +483,28 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
     const uint32_t lane = lane_id();
     const int wave = tid >> 6;
 
-    // Gathered source rows of this lane's DMA loads.  Rows past M or with an
-    // out-of-range id load E row 0 and are written as zeros.
+    // The tile's 8 positions (16 candidate rows each): bit q of `validq` says
+    // position q is a real one (t < its block's length), of `succq` that it
+    // has a successor in its block (t + 1 < length).  The same in every wave.
+    uint32_t validq, succq;
+    {
+        const int64_t bt = m0 / kK + (lane & 7);
+        bool v = false, sc = false;
+        if (lane < 8 && bt * kK < p.M) {
+            const uint32_t b = (uint32_t)bt / (uint32_t)p.L;
+            const int n = block_len_of(p.len, b, p.L);
+            const int t = (int)((uint32_t)bt - b * (uint32_t)p.L);
+            v = t < n;
+            sc = t + 1 < n;
+        }
+        validq = (uint32_t)ballot(v);
+        succq = (uint32_t)ballot(sc);
+    }
+    if (validq == 0) return;  // padding only (workgroup-uniform, before any barrier)
+
+    // Gathered source rows of this lane's DMA loads.  Rows past M, of padding
+    // positions or with an out-of-range id load E row 0; the last are written
+    // as zeros, the others not at all.
     const uint16_t *xsrc[XI];
     uint32_t xok = 0;
 #pragma unroll
@@ -474,7 +512,7 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
         const int row = 8 * (wave + NW * u) + (int)(lane >> 3);
         const int64_t m = m0 + row;
         int64_t tok = 0;
-        if (m < p.M) {
+        if (m < p.M && ((validq >> (row >> 4)) & 1u)) {
             const int32_t t = p.cand[m];
             if (t >= 0 && (int64_t)t < p.V) {
                 tok = t;
@@ -505,28 +543,18 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
         return;
     }
 
-    // Epilogue.  Row validity comes from the tile's mask; "position t is the
-    // last of its block" from an 8-bit mask of the tile's 8 positions.
+    // Epilogue.  Token validity comes from the tile's mask; which positions
+    // are written from the position masks: B for every real position, A for
+    // those with a successor.
     tile_row_mask<NW, XI>(xok, Xs);
-    uint32_t lastq = 0;
-    {
-        const int64_t bt0 = m0 / kK;
-        int pos = (int)(bt0 % p.L);
-#pragma unroll
-        for (int q = 0; q < BM / kK; ++q) {
-            if (pos == p.L - 1) lastq |= 1u << q;
-            pos = pos + 1 == p.L ? 0 : pos + 1;
-        }
-    }
+    const uint32_t wq = side == 0 ? succq : validq;
     // Candidate row m = (b t) * 16 + j of side 0 becomes predecessor row j of
     // position t + 1: output row m + 16.
     float *const out = side == 0 ? p.A_prev + (int64_t)kK * r : p.B_cur;
     for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) {
+        if (!((wq >> (rl >> 4)) & 1u)) return;  // padding, or no successor position
         const int64_t m = m0 + rl;
-        if (m >= p.M) return;
-        if (side == 0 && ((lastq >> (rl >> 4)) & 1u)) return;  // no successor position
-        const bool ok = (((const uint32_t *)Xs)[rl >> 5] >> (rl & 31)) & 1u;
-        *(floatx4 *)(out + m * r + n0 + cl) = ok ? v : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        *(floatx4 *)(out + m * r + n0 + cl) = tile_row_ok(Xs, rl) ? v : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     });
 }
 
@@ -544,18 +572,18 @@ __global__ __launch_bounds__(256) void project_cand_reduce_kernel(CandParams p) 
     const int ncol = 2 * p.nside;
     const int mt = (int)(m / BM), rl = (int)(m % BM);
     const int ct = side * p.nside + n / BN;
+    // padding positions, and on side 0 the last position of a block, are not written
+    const uint32_t bt = (uint32_t)(m / kK), b = bt / (uint32_t)p.L;
+    const int pos = (int)(bt - b * (uint32_t)p.L), len = block_len_of(p.len, b, p.L);
+    if (side == 0 ? pos + 1 >= len : pos >= len) return;
     const int64_t stride = (int64_t)p.mt * ncol * BM * BN;
     const float *src = p.part + ((int64_t)mt * ncol + ct) * (BM * BN) + rl * BN + (n % BN);
     float sum = 0.0f;
     for (int ks = 0; ks < p.nsplit; ++ks) sum += src[ks * stride];
     const int32_t t = p.cand[m];
     const bool ok = t >= 0 && (int64_t)t < p.V;
-    if (side == 0) {
-        if ((m / kK) % p.L == p.L - 1) return;  // the last position has no successor
-        p.A_prev[(m + kK) * r + n] = ok ? sum : 0.0f;
-    } else {
-        p.B_cur[m * r + n] = ok ? sum : 0.0f;
-    }
+    if (side == 0) p.A_prev[(m + kK) * r + n] = ok ? sum : 0.0f;
+    else p.B_cur[m * r + n] = ok ? sum : 0.0f;
 }
 
 // K splits of the candidate job: only when its tiles cannot fill the chip,
@@ -586,6 +614,7 @@ struct GateParams {
     const uint16_t *WA, *WH, *h;
     const int32_t *ver;
     int B, L;
+    const int32_t *len;  // ragged batch: valid positions per block (nullptr: all L)
     float *A_prev, *G;
     float *part;        // [nsplit][rows_gate + rows_ver][r] partial sums (nsplit > 1)
     int mt_gate, mt_ver, nside, nsplit;  // 128-row tiles of each job, column tiles, K splits
@@ -620,14 +649,19 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
     const uint32_t lane = lane_id();
     const int wave = threadIdx.x >> 6;
 
+    // Rows past M and rows of padding positions (gate: t >= length; verified
+    // token: an empty block) load h row 0 and are never written.
     const uint16_t *xsrc[XI];
-    uint32_t xok = 0;
+    uint32_t xok = 0, xlive = 0;
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
         const int row = 8 * (wave + NW * u) + (int)(lane >> 3);
         const int64_t m = m0 + row;
-        const uint16_t *base = p.h;  // rows past M load h row 0 and are never written
-        if (m < M) {
+        const uint16_t *base = p.h;
+        bool live = m < M;
+        if (live && p.len) live = gate ? position_live(p.len, (uint32_t)m, p.L) : block_len_of(p.len, m, p.L) > 0;
+        if (live) {
+            xlive |= 1u << u;
             if (gate) {
                 base = p.h + m * d;
                 xok |= 1u << u;
@@ -642,6 +676,8 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
         xsrc[u] = base + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
     }
     const uint16_t *W = (gate ? p.WH : p.WA) + (int64_t)n0 * d;
+    // a tile of padding only has nothing to write (ragged batches)
+    if (p.len && !__syncthreads_or(xlive != 0)) return;
 
     floatx16 acc[T::TM][T::TN];
 #pragma unroll
@@ -652,13 +688,12 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
     if (k1 > k0) mma_tile_dma<T>(xsrc, W, d, k0, k1, Xs, Ws, acc);
 
-    tile_row_mask<NW, XI>(xok, Xs);
+    tile_row_mask<NW, XI>(xok, Xs, xlive);
     const int64_t rows_all = (int64_t)p.B * p.L + p.B;
     for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) {
+        if (!tile_row_live(Xs, rl)) return;
         const int64_t m = m0 + rl;
-        if (m >= M) return;
-        const bool ok = (((const uint32_t *)Xs)[rl >> 5] >> (rl & 31)) & 1u;
-        if (!ok) v = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (!tile_row_ok(Xs, rl)) v = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         const int n = n0 + cl;
         if (p.nsplit > 1) {
             const int64_t row = gate ? m : (int64_t)p.B * p.L + m;
@@ -684,6 +719,11 @@ __global__ __launch_bounds__(256) void project_gate_reduce_kernel(GateParams p) 
     if (e >= rows_all * p.r) return;
     const int64_t row = e / p.r;
     const int n = (int)(e % p.r);
+    if (p.len) {  // padding positions and empty blocks: nothing to write
+        const bool gate = row < (int64_t)p.B * p.L;
+        if (gate ? !position_live(p.len, (uint32_t)row, p.L) : block_len_of(p.len, row - (int64_t)p.B * p.L, p.L) == 0)
+            return;
+    }
     float sum = 0.0f;
     for (int ks = 0; ks < p.nsplit; ++ks) sum += p.part[((int64_t)ks * rows_all + row) * p.r + n];
     if (row < (int64_t)p.B * p.L) {

@@ -27,6 +27,8 @@ struct TopkParams {
     const char *logits;   // row r starts at logits + r * ld * elem_size
     int64_t rows, V, ld;  // ld in elements
     int nsplit;           // workgroups per row
+    int L;                // positions per block (row r is position r % L of block r / L)
+    const int32_t *len;   // ragged batch: valid positions per block (nullptr: all L)
     int32_t *cand_id;
     float *cand_u;
     uint64_t *partial;    // [rows][nsplit][16] keys, used when nsplit > 1
@@ -209,6 +211,7 @@ __global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
     constexpr int EPV = 16 / ES;
     const int64_t row = blockIdx.x / p.nsplit;
     const int split = (int)(blockIdx.x % p.nsplit);
+    if (!position_live(p.len, (uint32_t)row, p.L)) return;  // padding row (ragged batches)
     const int wave = (int)(threadIdx.x / kWave);
     const uint32_t lane = lane_id();
     const char *rowp = p.logits + row * p.ld * ES;
@@ -302,6 +305,7 @@ template <bool BF16>
 __global__ __launch_bounds__(256) void topk16_merge_kernel(TopkParams p) {
     constexpr int ES = BF16 ? 2 : 4;
     const int64_t row = blockIdx.x;
+    if (!position_live(p.len, (uint32_t)row, p.L)) return;  // padding row (ragged batches)
     const uint32_t lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
     const uint64_t *src = p.partial + row * p.nsplit * kK;

@@ -54,6 +54,7 @@ struct VerifyParams {
     const char *logits;  // target row (b, t), t = 0..L, starts at logits + (b (L+1) + t) ld es
     int64_t V, ld;
     int B, L;
+    const int32_t *len;  // ragged batch: drafted positions per block (nullptr: all L)
     int nsplit;          // workgroups per row
     int nchunk;          // chunks per row: ceil(V / (256 EPV))
     int cps;             // chunks per workgroup (the last one may have fewer)
@@ -129,6 +130,11 @@ __global__ __launch_bounds__(256) void verify_stats_kernel(VerifyParams p) {
     constexpr int EPV = BF16 ? 8 : 4;
     const int64_t row = blockIdx.x / p.nsplit;
     const int sp = (int)(blockIdx.x - row * p.nsplit);
+    // ragged batches: block b reads its rows 0 .. len only (row len follows its last token)
+    if (p.len) {
+        const uint32_t b = (uint32_t)row / (uint32_t)(p.L + 1);
+        if ((int)((uint32_t)row - b * (uint32_t)(p.L + 1)) > block_len_of(p.len, b, p.L)) return;
+    }
     const int tid = (int)threadIdx.x, wave = tid >> 6;
     const uint32_t lane = lane_id();
     const char *rowp = p.logits + row * p.ld * (BF16 ? 2 : 4);
@@ -339,6 +345,7 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(VerifyParams p) {
     constexpr int CT = kVChunkVecs * EPV;  // tokens per chunk
     const int b = blockIdx.x;
     const int L = p.L;
+    const int nb = block_len_of(p.len, b, L);  // drafted positions (ragged batches: the block's own)
     const int tid = (int)threadIdx.x;
     const uint32_t lane = lane_id();
     const int64_t es = BF16 ? 2 : 4;
@@ -352,7 +359,7 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(VerifyParams p) {
     if (tid < kWave) {
         bool acc = false;
         int32_t x = -1;
-        if ((int)lane < L) {
+        if ((int)lane < nb) {
             const int64_t bt = (int64_t)b * L + lane;
             const int slot = p.path_slot[bt] & (kK - 1);
             x = p.cand_id[bt * kK + slot];
@@ -369,8 +376,8 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(VerifyParams p) {
                 }
             }
         }
-        const uint64_t miss = ballot((int)lane < L && !acc);
-        const int n = miss ? (int)__builtin_ctzll(miss) : L;
+        const uint64_t miss = ballot((int)lane < nb && !acc);
+        const int n = miss ? (int)__builtin_ctzll(miss) : nb;
         if ((int)lane < n) p.out_tok[(int64_t)b * (L + 1) + lane] = x;
         if (lane == 0) {
             s_n = n;
@@ -389,7 +396,7 @@ __global__ __launch_bounds__(256) void verify_draw_kernel(VerifyParams p) {
     } else {
         // 2. the draw's weights: w(v) = p(v), less q(v) (clamped at 0) at the
         // candidates when position n was rejected.
-        const bool residual = n < L;
+        const bool residual = n < nb;
         const float s = p.scale;
         float m, Z;
         verify_row_mz(p, row, &m, &Z);

@@ -31,6 +31,19 @@
  *     C++ exception crosses the boundary.  Calls on different streams may run
  *     concurrently, except that the device error word (dsel_device_error) is
  *     shared by all calls on one device.
+ *
+ * Ragged batches.  The block size is a per-request knob ([P1] supplementary
+ * deployment notes: oMLX runs blocks of 5, the release tables use 8 and 16;
+ * [P3] "What to check on your own serving").  Every call that takes `batch`
+ * and `block` also takes `block_len`: NULL for a uniform batch, else a DEVICE
+ * array [batch] of int32 (4-byte aligned) giving block b's valid positions,
+ * 0 <= block_len[b] <= block, in the same padded [batch, block] layout.  Block
+ * b is then computed exactly as it would be alone at length block_len[b]
+ * (same bits).  Outputs at padding positions (t >= block_len[b]) are not
+ * written, except where a call says so, and inputs there never affect a result
+ * (they may hold anything, NaN included); a length outside [0, block] makes the
+ * block empty and sets DSEL_DEVERR_BLOCK_LEN.  The launch geometry is that of
+ * the padded batch: workgroups with only padding to do exit at once.
  */
 #ifndef DSEL_H
 #define DSEL_H
@@ -62,6 +75,7 @@ typedef enum { DSEL_GREEDY = 0, DSEL_SAMPLED = 1 } dsel_walk_mode;
 
 /* Device error word bits (see dsel_device_error). */
 #define DSEL_DEVERR_TOKEN_RANGE 1 /* dsel_project met a token id outside [0, vocab) */
+#define DSEL_DEVERR_BLOCK_LEN 2   /* a block_len entry outside [0, block] */
 
 /* Bytes of device workspace dsel_select_topk needs for `rows` = batch*block rows
  * of `vocab` logits of type `dt` (0 when it needs none).  Returns 0 for
@@ -83,8 +97,9 @@ size_t dsel_topk_workspace_bytes(int64_t rows, int64_t vocab, dsel_dtype dt);
  *            (may be NULL when that is 0); contents need no initialisation.
  * Requirements: 16 <= vocab < 2^31, ld >= vocab, batch*block >= 0. */
 dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t batch, int64_t block,
-                             int64_t vocab, int64_t ld, int32_t *cand_id, float *cand_u,
-                             void *workspace, size_t workspace_bytes, dsel_stream_t stream);
+                             const int32_t *block_len, int64_t vocab, int64_t ld, int32_t *cand_id,
+                             float *cand_u, void *workspace, size_t workspace_bytes,
+                             dsel_stream_t stream);
 
 /* project -- [P1] Method (the paragraph after eq. S_t), [P3]: the compact token
  * vectors and the context gate, for every candidate and predecessor.
@@ -97,6 +112,8 @@ dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t batch, i
  *   A_prev   out [batch, block, 16, r] fp32: A of each predecessor.  Position 0
  *            has one predecessor (row 0 = A(verified)); rows 1..15 of position
  *            0 are written as zeros.  Position t >= 1: row i = A(cand_id[t-1][i]).
+ *            (Ragged batches: an empty block reads no verified token and has
+ *            no position 0.)
  *   B_cur    out [batch, block, 16, r] fp32: row j = B(cand_id[t][j]).
  *   G        out [batch, block, r] fp32: sigmoid(W_H h[t]).
  * Products are bf16 x bf16 with fp32 accumulation (MFMA).  A token id outside
@@ -109,8 +126,8 @@ dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t batch, i
 dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
                          const uint16_t *W_B, const uint16_t *W_H, int64_t r, const uint16_t *h,
                          const int32_t *cand_id, const int32_t *verified, int64_t batch,
-                         int64_t block, float *A_prev, float *B_cur, float *G, void *workspace,
-                         size_t workspace_bytes, dsel_stream_t stream);
+                         int64_t block, const int32_t *block_len, float *A_prev, float *B_cur,
+                         float *G, void *workspace, size_t workspace_bytes, dsel_stream_t stream);
 
 /* Bytes of device workspace dsel_project needs (0 when none; also 0 for
  * invalid arguments, which the calls themselves reject).  Small GEMMs are split
@@ -128,22 +145,23 @@ size_t dsel_project_workspace_bytes(int64_t batch, int64_t block, int64_t d, int
  * calls of the same half must not share one workspace concurrently). */
 dsel_status dsel_project_gate(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
                               const uint16_t *W_H, int64_t r, const uint16_t *h,
-                              const int32_t *verified, int64_t batch, int64_t block, float *A_prev,
-                              float *G, void *workspace, size_t workspace_bytes,
-                              dsel_stream_t stream);
+                              const int32_t *verified, int64_t batch, int64_t block,
+                              const int32_t *block_len, float *A_prev, float *G, void *workspace,
+                              size_t workspace_bytes, dsel_stream_t stream);
 /* project_gate for running beside another kernel, e.g. dsel_select_topk on a
  * second stream: the same outputs as dsel_project_gate, bit for bit except
  * for the order of the fp32 sums over d, computed with one workgroup per
  * 128-row output tile, no split along d and no workspace, so it occupies few
  * CUs (9 at 64 x 16 positions) for longer instead of the whole chip briefly.
  * Arguments, layouts and requirements as for dsel_project_gate. */
-dsel_status dsel_project_gate_overlap(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
-                                      const uint16_t *W_H, int64_t r, const uint16_t *h,
-                                      const int32_t *verified, int64_t batch, int64_t block,
-                                      float *A_prev, float *G, dsel_stream_t stream);
+dsel_status dsel_project_gate_overlap(const uint16_t *E, int64_t vocab, int64_t d,
+                                      const uint16_t *W_A, const uint16_t *W_H, int64_t r,
+                                      const uint16_t *h, const int32_t *verified, int64_t batch,
+                                      int64_t block, const int32_t *block_len, float *A_prev,
+                                      float *G, dsel_stream_t stream);
 dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
-                              const uint16_t *W_B, int64_t r, const int32_t *cand_id,
-                              int64_t batch, int64_t block, float *A_prev, float *B_cur,
+                              const uint16_t *W_B, int64_t r, const int32_t *cand_id, int64_t batch,
+                              int64_t block, const int32_t *block_len, float *A_prev, float *B_cur,
                               void *workspace, size_t workspace_bytes, dsel_stream_t stream);
 
 /* Walk arguments ([P1] Method last paragraph, [P3]: the only sequential step;
@@ -185,14 +203,15 @@ typedef struct {
  * Requirements: 1 <= block <= DSEL_MAX_BLOCK, r % 32 == 0, 32 <= r <= 256;
  * pointers 16-byte aligned. */
 dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const float *B_cur,
-                             const float *G, int64_t batch, int64_t block, int64_t r, float *S,
-                             const dsel_walk_args *walk, dsel_stream_t stream);
+                             const float *G, int64_t batch, int64_t block, const int32_t *block_len,
+                             int64_t r, float *S, const dsel_walk_args *walk, dsel_stream_t stream);
 
 /* walk -- the walk alone over given scores S [batch, block, 16, 16] fp32 (same
  * rules as the fused walk of dsel_score_pairs; row 0 is the predecessor at
- * position 0).  Requirements: 1 <= block <= DSEL_MAX_BLOCK. */
-dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const dsel_walk_args *walk,
-                      dsel_stream_t stream);
+ * position 0).  Ragged batches: block b walks its first block_len[b]
+ * positions.  Requirements: 1 <= block <= DSEL_MAX_BLOCK. */
+dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const int32_t *block_len,
+                      const dsel_walk_args *walk, dsel_stream_t stream);
 
 /* verify -- lossless verification of the drafted blocks against the target
  * model, the step after the walk ([P1] Method, last paragraph, and Setup:
@@ -220,14 +239,19 @@ dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const dsel_w
  *   n_accepted     out [batch] int32: accepted positions n (0..block).
  *   out_tok        out [batch, block + 1] int32: the n accepted tokens, the
  *                  extra token at index n, -1 after it.
+ *   Ragged batches: block b has block_len[b] = n_b drafted positions and reads
+ *   target rows 0 .. n_b (row n_b follows its last drafted token: the row
+ *   `block` of the rules above); its whole out_tok row is written.  An empty
+ *   block (n_b = 0) tests nothing and takes its extra token from row 0.
  *   workspace      device scratch of dsel_verify_workspace_bytes() bytes;
  *                  contents need no initialisation.
  * Requirements: 1 <= block <= DSEL_MAX_BLOCK. */
 size_t dsel_verify_workspace_bytes(int64_t batch, int64_t block, int64_t vocab);
 dsel_status dsel_verify(const void *target_logits, dsel_dtype dt, int64_t batch, int64_t block,
-                        int64_t vocab, int64_t ld, const int32_t *cand_id, const int32_t *path_slot,
-                        const float *q, dsel_walk_mode mode, float temperature, const float *u_acc,
-                        const float *u_res, int32_t *n_accepted, int32_t *out_tok, void *workspace,
+                        const int32_t *block_len, int64_t vocab, int64_t ld, const int32_t *cand_id,
+                        const int32_t *path_slot, const float *q, dsel_walk_mode mode,
+                        float temperature, const float *u_acc, const float *u_res,
+                        int32_t *n_accepted, int32_t *out_tok, void *workspace,
                         size_t workspace_bytes, dsel_stream_t stream);
 
 /* Synchronise `stream`, then read and clear the device error word of the
@@ -280,12 +304,13 @@ dsel_status dsel_lmhead_topk(const uint16_t *h, const uint16_t *W, int64_t rows,
  * pointers 16-byte aligned. */
 size_t dsel_dyn_conv_workspace_bytes(int64_t batch, int64_t block, int64_t d);
 dsel_status dsel_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base,
-                          const uint16_t *W_c, int64_t batch, int64_t block, int64_t d, uint16_t *y,
-                          void *workspace, size_t workspace_bytes, dsel_stream_t stream);
+                          const uint16_t *W_c, int64_t batch, int64_t block,
+                          const int32_t *block_len, int64_t d, uint16_t *y, void *workspace,
+                          size_t workspace_bytes, dsel_stream_t stream);
 
 /* ABI version of this header (major * 100 + minor). */
 int32_t dsel_version(void);
-#define DSEL_VERSION 100
+#define DSEL_VERSION 200
 
 #ifdef __cplusplus
 }

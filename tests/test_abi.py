@@ -42,7 +42,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsel_version() == 100
+    assert lib.dsel_version() == 200
     for code in (0, -1, -2, -3, -4, -5):
         assert lib.dsel_status_string(code).startswith(b"DSEL_")
 
@@ -54,13 +54,13 @@ def test_project_workspace_sizing(lib):
     # one block: the candidate GEMM is split too, so the workspace grows
     assert lib.dsel_project_workspace_bytes(1, 16, 2560, 256) > lib.dsel_project_workspace_bytes(64, 16, 2560, 256) / 64
     fake = C.c_void_p(0x100000)
-    args = [fake, 151936, 2560, fake, fake, fake, 256, fake, fake, fake, 64, 16, fake, fake, fake,
+    args = [fake, 151936, 2560, fake, fake, fake, 256, fake, fake, fake, 64, 16, None, fake, fake, fake,
             None, 0, None]
     assert lib.dsel_project(*args) == -4  # workspace missing
     # the candidate half of one block needs its part of the workspace
-    cand_args = [fake, 151936, 2560, fake, fake, 256, fake, 1, 16, fake, fake, None, 0, None]
+    cand_args = [fake, 151936, 2560, fake, fake, 256, fake, 1, 16, None, fake, fake, None, 0, None]
     assert lib.dsel_project_cand(*cand_args) == -4
-    small = list(cand_args); small[11] = fake; small[12] = 64
+    small = list(cand_args); small[12] = fake; small[13] = 64
     assert lib.dsel_project_cand(*small) == -4
 
 
@@ -78,14 +78,14 @@ def test_validation_rejects_before_launch(lib):
     fake = P(0x100000)  # never dereferenced: each call fails validation first
     odd = P(0x100001)
     # select_topk
-    assert lib.dsel_select_topk(None, 1, 1, 1, 1024, 1024, fake, fake, None, 0, None) == -1
-    assert lib.dsel_select_topk(fake, 7, 1, 1, 1024, 1024, fake, fake, None, 0, None) == -2
-    assert lib.dsel_select_topk(fake, 1, 1, 1, 15, 15, fake, fake, None, 0, None) == -1
-    assert lib.dsel_select_topk(fake, 1, 1, 1, 64, 32, fake, fake, None, 0, None) == -1
-    assert lib.dsel_select_topk(odd, 1, 1, 1, 64, 64, fake, fake, None, 0, None) == -3
-    assert lib.dsel_select_topk(fake, 1, 1, 16, 151936, 151936, fake, fake, None, 0, None) == -4
+    assert lib.dsel_select_topk(None, 1, 1, 1, None, 1024, 1024, fake, fake, None, 0, None) == -1
+    assert lib.dsel_select_topk(fake, 7, 1, 1, None, 1024, 1024, fake, fake, None, 0, None) == -2
+    assert lib.dsel_select_topk(fake, 1, 1, 1, None, 15, 15, fake, fake, None, 0, None) == -1
+    assert lib.dsel_select_topk(fake, 1, 1, 1, None, 64, 32, fake, fake, None, 0, None) == -1
+    assert lib.dsel_select_topk(odd, 1, 1, 1, None, 64, 64, fake, fake, None, 0, None) == -3
+    assert lib.dsel_select_topk(fake, 1, 1, 16, None, 151936, 151936, fake, fake, None, 0, None) == -4
     # project
-    args = [fake, 1000, 64, fake, fake, fake, 32, fake, fake, fake, 2, 4, fake, fake, fake, None, 0, None]
+    args = [fake, 1000, 64, fake, fake, fake, 32, fake, fake, fake, 2, 4, None, fake, fake, fake, None, 0, None]
     bad_d = list(args); bad_d[2] = 96
     bad_r = list(args); bad_r[6] = 48
     big_r = list(args); big_r[6] = 512
@@ -95,17 +95,21 @@ def test_validation_rejects_before_launch(lib):
         assert lib.dsel_project(*a) == code
     # score_pairs / walk
     w = ds.WalkArgs(5, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)
-    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, 32, fake, C.byref(w), None) == -2
-    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 33, 32, fake, None, None) == -1
-    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, 32, None, None, None) == -1
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, None, 32, fake, C.byref(w), None) == -2
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 33, None, 32, fake, None, None) == -1
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, None, 32, None, None, None) == -1
     w = ds.WalkArgs(0, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)
-    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, 32, None, C.byref(w), None) == -1
+    assert lib.dsel_score_pairs(fake, fake, fake, fake, 1, 8, None, 32, None, C.byref(w), None) == -1
     w = ds.WalkArgs(1, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)  # sampled, no uniforms
-    assert lib.dsel_walk(fake, 1, 8, C.byref(w), None) == -1
+    assert lib.dsel_walk(fake, 1, 8, None, C.byref(w), None) == -1
     w = ds.WalkArgs(1, 0.0, 0x100000, 0x100000, 0x100000, 0x100000, None, None)  # T = 0
-    assert lib.dsel_walk(fake, 1, 8, C.byref(w), None) == -1
-    assert lib.dsel_walk(fake, 1, 0, C.byref(w), None) == -1
+    assert lib.dsel_walk(fake, 1, 8, None, C.byref(w), None) == -1
+    assert lib.dsel_walk(fake, 1, 0, None, C.byref(w), None) == -1
     assert lib.dsel_device_error(None, None) == -1
+    # ragged batches: a misaligned length array is rejected before any launch
+    assert lib.dsel_select_topk(fake, 1, 1, 16, odd, 1024, 1024, fake, fake, None, 0, None) == -3
+    assert lib.dsel_walk(fake, 1, 8, odd, C.byref(ds.WalkArgs(0, 1.0, None, 0x100000, 0x100000, 0x100000,
+                                                              None, None)), None) == -3
 
 
 def test_verify_validation(lib):
@@ -116,10 +120,10 @@ def test_verify_validation(lib):
     assert lib.dsel_verify_workspace_bytes(4, 8, (1 << 22) + 1) == 0
 
     def call(**kw):
-        a = dict(tl=fake, dt=1, B=4, L=8, V=151936, ld=151936, cand=fake, slot=fake, q=fake, mode=1,
+        a = dict(tl=fake, dt=1, B=4, L=8, lens=None, V=151936, ld=151936, cand=fake, slot=fake, q=fake, mode=1,
                  T=C.c_float(1.0), ua=fake, ur=fake, n=fake, out=fake, ws=fake, wsb=ws)
         a.update(kw)
-        return lib.dsel_verify(a["tl"], a["dt"], a["B"], a["L"], a["V"], a["ld"], a["cand"], a["slot"],
+        return lib.dsel_verify(a["tl"], a["dt"], a["B"], a["L"], a["lens"], a["V"], a["ld"], a["cand"], a["slot"],
                                a["q"], a["mode"], a["T"], a["ua"], a["ur"], a["n"], a["out"], a["ws"],
                                a["wsb"], None)
 
@@ -130,3 +134,4 @@ def test_verify_validation(lib):
     assert call(tl=odd) == -3 and call(ld=151937) == -3     # row starts must be 16-byte aligned
     assert call(ws=None) == -4 and call(wsb=ws - 1) == -4
     assert call(B=0, tl=None, cand=None) == 0               # no work: pointers may be NULL
+    assert call(lens=P(0x100002)) == -3                     # ragged lengths: int32 alignment
