@@ -34,10 +34,6 @@ inline dsel_status launch(const void *kernel, dim3 grid, dim3 block, void *arg, 
 #define DSEL_VERIFY_WGS 2048
 #endif
 
-#ifndef DSEL_TOPK_UNROLL
-#define DSEL_TOPK_UNROLL 4
-#endif
-constexpr int kTopkUnroll = DSEL_TOPK_UNROLL;  // 16-byte vectors in flight per lane
 
 dsel_status check_walk(const dsel_walk_args *w, WalkParams *out) {
     if (!w) return DSEL_E_ARG;
@@ -99,8 +95,8 @@ DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t
     p.cand_id = cand_id;
     p.cand_u = cand_u;
     p.partial = (uint64_t *)workspace;
-    const void *k1 = dt == DSEL_BF16 ? (const void *)topk16_kernel<true, kTopkUnroll>
-                                     : (const void *)topk16_kernel<false, kTopkUnroll>;
+    const void *k1 = dt == DSEL_BF16 ? (const void *)topk16_kernel<true, kTopkUnroll<true>>
+                                     : (const void *)topk16_kernel<false, kTopkUnroll<false>>;
     dsel_status s = launch(k1, dim3((unsigned)(rows * ns)), dim3(256), &p, 0, stream);
     if (s != DSEL_OK || ns == 1) return s;
     const void *k2 = dt == DSEL_BF16 ? (const void *)topk16_merge_kernel<true>
