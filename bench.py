@@ -54,7 +54,8 @@ def algorithmic(cfg):
     b_rows = cfg.batch * cfg.block * K        # candidates that need B
     cand_flop = 2.0 * cfg.d * cfg.r * (a_rows + b_rows)
     gate_flop = 2.0 * cfg.d * cfg.r * (rows + cfg.batch)  # gate rows + verified tokens
-    return dict(topk_bytes=topk_bytes, cand_flop=cand_flop, gate_flop=gate_flop)
+    gather_bytes = rows * K * cfg.d * 2                   # the gathered E rows, bf16
+    return dict(topk_bytes=topk_bytes, cand_flop=cand_flop, gate_flop=gate_flop, gather_bytes=gather_bytes)
 
 
 def kernel_source_hash(names):
@@ -114,6 +115,67 @@ def record_traffic(workload, fetch_dir, write_dir, command):
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(out, rec["fetch_bytes"], rec["write_bytes"])
+
+
+def _counters_by_dispatch(run_dir, match):
+    """{dispatch: {counter: value}} over the dispatches of kernels whose name
+    contains `match` in a rocprofv3 --pmc CSV directory."""
+    import csv
+    import glob
+
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if match in row["Kernel_Name"]:
+                    d = out.setdefault((path, row["Dispatch_Id"]), {})
+                    d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+                    d["ns"] = float(row["End_Timestamp"]) - float(row["Start_Timestamp"])
+    if not out:
+        raise SystemExit(f"no dispatch of {match} in {run_dir}")
+    return list(out.values())
+
+
+XCDS = 8        # MI355X: GRBM_GUI_ACTIVE comes summed over its 8 XCDs
+SIMDS = 1024    # 256 CUs x 4 SIMDs
+
+
+def record_mfma(workload, run_dir, command):
+    """Write profiles/project_cand_<workload>_mfma.json from one rocprofv3
+    --pmc run of SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE: executed bf16 MFMA FLOP per dispatch (MOPS x 512) and the
+    matrix cores' busy fraction (busy cycles summed over SIMDs / (active cycles
+    x SIMDs), rocprofv3's MfmaUtil)."""
+    match, sources = TRAFFIC_KERNELS["project_cand"]
+    ds_ = _counters_by_dispatch(run_dir, match)
+    n = len(ds_)
+    mops = sum(d["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for d in ds_) / n
+    busy = sum(d["SQ_VALU_MFMA_BUSY_CYCLES"] for d in ds_) / n
+    act = sum(d["GRBM_GUI_ACTIVE"] for d in ds_) / n / XCDS
+    ns = sum(d["ns"] for d in ds_) / n
+    rec = {"kernel": match, "workload": workload, "command": command, "dispatches": n,
+           "mfma_flop_per_dispatch": mops * 512, "mfma_busy_cycles": busy, "active_cycles_per_xcd": act,
+           "clock_ghz": round(act / ns, 3), "mfma_util": round(busy / (act * SIMDS), 4),
+           "sources": sources, "source_hash": kernel_source_hash(sources)}
+    out = os.path.join(ROOT, "profiles", f"project_cand_{workload}_mfma.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(out, rec["mfma_util"], rec["clock_ghz"], rec["mfma_flop_per_dispatch"])
+
+
+def mfma_from_profile(workload):
+    """The committed counter record of the candidate GEMM, or None when there
+    is none or its sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"project_cand_{workload}_mfma.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("source_hash") != kernel_source_hash(t.get("sources", [])):
+        return None
+    return {"mfma_util": t["mfma_util"], "clock_ghz": t["clock_ghz"],
+            "mfma_flop_per_dispatch": t["mfma_flop_per_dispatch"]}
 
 
 def calibrate_copy():
@@ -335,8 +397,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--gate", default="serial", choices=["serial", "overlap"],
-                    help="run the gate GEMM before the top-16 or beside it on a second stream")
+    ap.add_argument("--gate", default="serial", choices=["serial", "side", "overlap"],
+                    help="run the gate GEMM before the top-16 (serial), beside it on a second stream "
+                         "(side: split along d, with its reduce; overlap: one workgroup per tile)")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the pass that evicts the caches before every step")
     ap.add_argument("--no-verify", action="store_true",
@@ -347,6 +410,8 @@ def main():
                     help="skip timing the same step on a ragged batch (per-block lengths)")
     ap.add_argument("--lmhead", action="store_true",
                     help="also time the LM head with the fused top-16 (dsel_lmhead_topk) and the unfused route")
+    ap.add_argument("--record-mfma", nargs=2, metavar=("RUN_DIR", "COMMAND"),
+                    help="write profiles/project_cand_<workload>_mfma.json from a rocprofv3 --pmc run")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--record-traffic", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "COMMAND"),
@@ -354,6 +419,9 @@ def main():
     args = ap.parse_args()
     if args.record_traffic:
         record_traffic(args.workload, *args.record_traffic)
+        return
+    if args.record_mfma:
+        record_mfma(args.workload, *args.record_mfma)
         return
     if args.calibrate_copy:
         calibrate_copy()
@@ -408,23 +476,27 @@ def main():
         LN = P(lens) if lens is not None else None
         if ev is not None:
             ev[0].record(strm)
-        if args.gate == "overlap":
+        par = args.gate in ("side", "overlap")
+        if par:
             fork[0].record(strm)
             side.wait_event(fork[0])
-        if args.gate == "overlap":
+        if args.gate == "side":
+            s0 = lib.dsel_project_gate(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
+                                       P(d["verified"]), B, L, LN, P(A_prev), P(G), P(pws), pwsb, ss)
+        elif args.gate == "overlap":
             s0 = lib.dsel_project_gate_overlap(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
                                                P(d["verified"]), B, L, LN, P(A_prev), P(G), ss)
         else:
             s0 = lib.dsel_project_gate(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_H"]), cfg.r, P(d["h"]),
                                        P(d["verified"]), B, L, LN, P(A_prev), P(G), P(pws), pwsb, sp)
-        if args.gate == "overlap":
+        if par:
             fork[1].record(side)
         if ev is not None:
             ev[1].record(strm)
         s1 = lib.dsel_select_topk(P(d["logits"]), dt, B, L, LN, V, V, P(cand_id), P(cand_u), P(ws), wsb, sp)
         if ev is not None:
             ev[2].record(strm)
-        if args.gate == "overlap":
+        if par:
             strm.wait_event(fork[1])
         s2 = lib.dsel_project_cand(P(d["E"]), V, cfg.d, P(d["W_A"]), P(d["W_B"]), cfg.r, P(cand_id),
                                    B, L, LN, P(A_prev), P(B_cur), P(pws), pwsb, sp)
@@ -560,7 +632,10 @@ def main():
         "stages_us": warm,
         "stages_us_cold": cold,
         "select_topk_hbm": {"GB/s": round(topk_gbs, 1), "frac": round(topk_gbs / HBM_PEAK_GBS, 4)},
-        "project_cand_mfma": {"TFLOP/s": round(proj_tfs, 2), "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4)},
+        "project_cand_mfma": {"TFLOP/s": round(proj_tfs, 2), "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4),
+                              "counters": mfma_from_profile(cfg.name)},
+        "project_cand_gather": {"GB/s": round(alg["gather_bytes"] / (st_proj * 1e-6) / 1e9, 1),
+                                "frac": round(alg["gather_bytes"] / (st_proj * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "project_gate": args.gate,
         "roofline": roof,
         "verify": verify,

@@ -752,12 +752,21 @@ inline int gate_bn(int64_t batch, int64_t block, int64_t r) {
         if (bn <= cap && r % bn == 0) return bn;
     return 32;
 }
+#ifndef DSEL_GATE_MIN_STEPS_NARROW
+#define DSEL_GATE_MIN_STEPS_NARROW 10
+#endif
+#ifndef DSEL_GATE_MIN_STEPS_WIDE
+#define DSEL_GATE_MIN_STEPS_WIDE 8
+#endif
+#ifndef DSEL_GATE_TARGET_WG
+#define DSEL_GATE_TARGET_WG 256
+#endif
 inline int gate_nsplit(int64_t batch, int64_t block, int64_t d, int64_t r) {
     const int64_t BN = gate_bn(batch, block, r);
     const int64_t tiles = (int64_t)gate_row_tiles(batch, block) * (r / BN);
     const int64_t nk = d / kBK;
-    const int64_t min_steps = BN <= 64 ? 10 : 8;
-    int64_t s = 256 / (tiles > 0 ? tiles : 1);
+    const int64_t min_steps = BN <= 64 ? DSEL_GATE_MIN_STEPS_NARROW : DSEL_GATE_MIN_STEPS_WIDE;
+    int64_t s = DSEL_GATE_TARGET_WG / (tiles > 0 ? tiles : 1);
     if (s > nk / min_steps) s = nk / min_steps;
     if (s < 1) s = 1;
     return (int)s;
