@@ -97,22 +97,75 @@ __device__ __forceinline__ uint32_t bf16_pk_floor(float t) {
     return ((__float_as_uint(t) >> 16) - 1u) * 0x10001u;
 }
 
+// x of lane (lane ^ J), for J a power of two below 64, without the LDS
+// crossbar: DPP quad_perm for 1 and 2; row_ror:4 / row_ror:12 (lane l reads
+// (l - 4) or (l + 4) mod 16 of its row) for 4; row_ror:8 for 8; and the gfx950
+// row swaps for 16 and 32: with both operands x, v_permlane16_swap returns
+// (rows 0, 2: own, rows 1, 3: x[l - 16]) and (rows 0, 2: x[l + 16], rows 1, 3:
+// own), v_permlane32_swap likewise across the two 32-lane halves.  Every lane
+// must be active.
+template <int J>
+__device__ __forceinline__ uint32_t xor_lane32(uint32_t x) {
+    static_assert(J == 1 || J == 2 || J == 4 || J == 8 || J == 16 || J == 32, "lane distance");
+    if constexpr (J == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (J == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (J == 4) {
+        const uint32_t dn = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x124, 0xF, 0xF, false);
+        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x12C, 0xF, 0xF, false);
+        return (lane_id() & 4u) ? dn : up;
+    } else if constexpr (J == 8) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xF, 0xF, false);
+    } else if constexpr (J == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        return (lane_id() & 16u) ? r[0] : r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        return (lane_id() & 32u) ? r[0] : r[1];
+    }
+}
+template <int J>
+__device__ __forceinline__ uint64_t xor_lane64(uint64_t x) {
+    return ((uint64_t)xor_lane32<J>((uint32_t)(x >> 32)) << 32) | xor_lane32<J>((uint32_t)x);
+}
+
+// One compare-exchange stage of a bitonic network: lanes with bit J clear keep
+// the larger key when `desc` holds for them.
+template <int J>
+__device__ __forceinline__ uint64_t bitonic_stage(uint64_t key, bool desc) {
+    const uint64_t other = xor_lane64<J>(key);
+    const bool lower = (lane_id() & (uint32_t)J) == 0;
+    const uint64_t mx = key > other ? key : other;
+    const uint64_t mn = key > other ? other : key;
+    return (lower == desc) ? mx : mn;
+}
+
 // Bitonic sort of one 64-bit key per lane across the wave, descending
-// (lane 0 receives the largest key).
+// (lane 0 receives the largest key); every lane must be active.
 __device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t key) {
     const uint32_t lane = lane_id();
-#pragma unroll
-    for (int k = 2; k <= kWave; k <<= 1) {
-#pragma unroll
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            uint64_t other = shfl_idx64(key, lane ^ (uint32_t)j);
-            bool lower = (lane & (uint32_t)j) == 0;
-            bool desc = (lane & (uint32_t)k) == 0;
-            uint64_t mx = key > other ? key : other;
-            uint64_t mn = key > other ? other : key;
-            key = (lower == desc) ? mx : mn;
-        }
-    }
+    key = bitonic_stage<1>(key, (lane & 2u) == 0);
+    key = bitonic_stage<2>(key, (lane & 4u) == 0);
+    key = bitonic_stage<1>(key, (lane & 4u) == 0);
+    key = bitonic_stage<4>(key, (lane & 8u) == 0);
+    key = bitonic_stage<2>(key, (lane & 8u) == 0);
+    key = bitonic_stage<1>(key, (lane & 8u) == 0);
+    key = bitonic_stage<8>(key, (lane & 16u) == 0);
+    key = bitonic_stage<4>(key, (lane & 16u) == 0);
+    key = bitonic_stage<2>(key, (lane & 16u) == 0);
+    key = bitonic_stage<1>(key, (lane & 16u) == 0);
+    key = bitonic_stage<16>(key, (lane & 32u) == 0);
+    key = bitonic_stage<8>(key, (lane & 32u) == 0);
+    key = bitonic_stage<4>(key, (lane & 32u) == 0);
+    key = bitonic_stage<2>(key, (lane & 32u) == 0);
+    key = bitonic_stage<1>(key, (lane & 32u) == 0);
+    key = bitonic_stage<32>(key, true);
+    key = bitonic_stage<16>(key, true);
+    key = bitonic_stage<8>(key, true);
+    key = bitonic_stage<4>(key, true);
+    key = bitonic_stage<2>(key, true);
+    key = bitonic_stage<1>(key, true);
     return key;
 }
 

@@ -54,12 +54,11 @@ __device__ __forceinline__ uint64_t list_merge64(uint64_t list, uint64_t cand) {
     const uint64_t srt = wave_sort64_desc(cand);
     const uint64_t rev = shfl_idx64(srt, lane >= 16 && lane < 32 ? 31 - lane : lane);
     uint64_t k = lane < 16 ? list : (lane < 32 ? rev : 0ull);
-#pragma unroll
-    for (int j = 16; j >= 1; j >>= 1) {
-        const uint64_t o = shfl_idx64(k, lane ^ (uint32_t)j);
-        const bool lower = (lane & (uint32_t)j) == 0;
-        k = lower ? (k > o ? k : o) : (k > o ? o : k);
-    }
+    k = bitonic_stage<16>(k, true);
+    k = bitonic_stage<8>(k, true);
+    k = bitonic_stage<4>(k, true);
+    k = bitonic_stage<2>(k, true);
+    k = bitonic_stage<1>(k, true);
     return lane < 16 ? k : 0ull;
 }
 

@@ -79,12 +79,16 @@ struct WaveTop {
         thr = readlane64(key, 15);
         thr_f = key_threshold(thr);
     }
-    // Insert a wave-uniform key known to rank above thr.
+    // Insert a wave-uniform key known to rank above thr.  The list is DPP row
+    // 0 (lanes 0..15), so the shift by one slot is a row_shr:1 of both halves
+    // (VALU, no trip through the LDS crossbar).
     __device__ __forceinline__ void insert(uint64_t c) {
         const uint32_t lane = lane_id();
         bool gt = lane < (uint32_t)kK && c > key;
         uint64_t m = ballot(gt);
-        uint64_t prev = shfl_idx64(key, lane == 0 ? 0 : lane - 1);
+        const uint32_t plo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)key, 0x111, 0xF, 0xF, false);
+        const uint32_t phi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(key >> 32), 0x111, 0xF, 0xF, false);
+        uint64_t prev = ((uint64_t)phi << 32) | plo;  // key of lane - 1 (lanes 1..15)
         bool prev_gt = lane >= 1 && ((m >> (lane - 1)) & 1ull);
         key = gt ? (prev_gt ? prev : c) : key;
         refresh();

@@ -66,25 +66,35 @@ struct VerifyParams {
     float2 *chunk;       // [rows][nchunk]: chunk max, sum of exp2((z - max) s) (sampled)
 };
 
+// Butterfly reductions over the wave (partners lane ^ 32, ^ 16, ..., ^ 1; the
+// same order on every lane, so every lane ends with the same bits).
+__device__ __forceinline__ float fxor_max(float x, uint32_t y) { return __builtin_fmaxf(x, __uint_as_float(y)); }
 __device__ __forceinline__ float wave_max_f(float x) {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x = __builtin_fmaxf(x, shfl_idxf(x, lane ^ (uint32_t)o));
+    x = fxor_max(x, xor_lane32<32>(__float_as_uint(x)));
+    x = fxor_max(x, xor_lane32<16>(__float_as_uint(x)));
+    x = fxor_max(x, xor_lane32<8>(__float_as_uint(x)));
+    x = fxor_max(x, xor_lane32<4>(__float_as_uint(x)));
+    x = fxor_max(x, xor_lane32<2>(__float_as_uint(x)));
+    x = fxor_max(x, xor_lane32<1>(__float_as_uint(x)));
     return x;
 }
 __device__ __forceinline__ float wave_sum_f(float x) {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) x += shfl_idxf(x, lane ^ (uint32_t)o);
+    x += __uint_as_float(xor_lane32<32>(__float_as_uint(x)));
+    x += __uint_as_float(xor_lane32<16>(__float_as_uint(x)));
+    x += __uint_as_float(xor_lane32<8>(__float_as_uint(x)));
+    x += __uint_as_float(xor_lane32<4>(__float_as_uint(x)));
+    x += __uint_as_float(xor_lane32<2>(__float_as_uint(x)));
+    x += __uint_as_float(xor_lane32<1>(__float_as_uint(x)));
     return x;
 }
+__device__ __forceinline__ uint64_t u64_max(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
-    const uint32_t lane = lane_id();
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        const uint64_t y = shfl_idx64(x, lane ^ (uint32_t)o);
-        x = y > x ? y : x;
-    }
+    x = u64_max(x, xor_lane64<32>(x));
+    x = u64_max(x, xor_lane64<16>(x));
+    x = u64_max(x, xor_lane64<8>(x));
+    x = u64_max(x, xor_lane64<4>(x));
+    x = u64_max(x, xor_lane64<2>(x));
+    x = u64_max(x, xor_lane64<1>(x));
     return x;
 }
 // inclusive prefix sum across the wave
