@@ -406,6 +406,8 @@ def main():
                     help="skip timing the verification of the drafted blocks (dsel_verify)")
     ap.add_argument("--no-conv", action="store_true",
                     help="skip timing the dynamic two-tap convolution unit (dsel_dyn_conv)")
+    ap.add_argument("--separate", action="store_true",
+                    help="time the graph of separate calls instead of one dsel_select_path call")
     ap.add_argument("--no-ragged", action="store_true",
                     help="skip timing the same step on a ragged batch (per-block lengths)")
     ap.add_argument("--lmhead", action="store_true",
@@ -468,11 +470,35 @@ def main():
     ss = C.c_void_p(side.cuda_stream)
     fork = [torch.cuda.Event() for _ in range(2)]
 
+    # the whole step as one dsel_select_path call (the gate's split-K
+    # reduction rides in the top-16 launch); the eager stage timing below uses
+    # the separate calls, which give the same bits
+    fused = args.gate == "serial" and not args.separate
+    xwsb = lib.dsel_select_path_workspace_bytes(B, L, V, dt, cfg.d, cfg.r)
+    xws = torch.empty(max(xwsb, 16), dtype=torch.uint8, device=dev)
+
+    def path_args(lens):
+        return ds.PathArgs(d["logits"].data_ptr(), dt, V, V, d["E"].data_ptr(), cfg.d, d["W_A"].data_ptr(),
+                           d["W_B"].data_ptr(), d["W_H"].data_ptr(), cfg.r, d["h"].data_ptr(),
+                           d["verified"].data_ptr(), B, L, None if lens is None else lens.data_ptr(),
+                           cand_id.data_ptr(), cand_u.data_ptr(), A_prev.data_ptr(), B_cur.data_ptr(),
+                           G.data_ptr(), S.data_ptr())
+
+    pargs = {}
+
     def step(strm, ev=None, lens=None):
         # the gate GEMM needs no candidates: either it runs first, or on a side
         # stream beside the top-16 (the side stream first waits for the
         # previous step).  `lens`: per-block lengths of a ragged batch.
         sp = C.c_void_p(strm.cuda_stream)
+        if fused and ev is None:
+            key = lens is not None
+            if key not in pargs:
+                pargs[key] = path_args(lens)
+            st = lib.dsel_select_path(C.byref(pargs[key]), C.byref(wargs), P(xws), xwsb, sp)
+            if st:
+                raise RuntimeError(f"dsel_select_path status {st}")
+            return
         LN = P(lens) if lens is not None else None
         if ev is not None:
             ev[0].record(strm)
@@ -627,7 +653,7 @@ def main():
                    "r": cfg.r, "logits": cfg.logits_dtype, "walk": "sampled" if mode else "greedy"},
         "us_per_block": round(ms_step * 1e3 / B, 4),
         "ms_per_step_eager": round(wall_eager * 1e3 / args.steps, 5),
-        "timing": "value: the step as one HIP graph replayed K times; stages: eager launches with "
+        "timing": "value: the step (step_call) as one HIP graph replayed K times; stages: eager separate calls with "
                   "HIP events on the launch stream (stages_us_cold: after a 1 GiB cache-evicting write)",
         "stages_us": warm,
         "stages_us_cold": cold,
@@ -637,6 +663,7 @@ def main():
         "project_cand_gather": {"GB/s": round(alg["gather_bytes"] / (st_proj * 1e-6) / 1e9, 1),
                                 "frac": round(alg["gather_bytes"] / (st_proj * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
         "project_gate": args.gate,
+        "step_call": "dsel_select_path" if fused else "separate calls",
         "roofline": roof,
         "verify": verify,
         "dyn_conv": conv,

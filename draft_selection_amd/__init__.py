@@ -45,6 +45,15 @@ class WalkArgs(C.Structure):
                 ("path_s", C.c_void_p), ("q", C.c_void_p)]
 
 
+class PathArgs(C.Structure):
+    _fields_ = [("logits", C.c_void_p), ("dt", C.c_int32), ("vocab", C.c_int64), ("ld", C.c_int64),
+                ("E", C.c_void_p), ("d", C.c_int64), ("W_A", C.c_void_p), ("W_B", C.c_void_p),
+                ("W_H", C.c_void_p), ("r", C.c_int64), ("h", C.c_void_p), ("verified", C.c_void_p),
+                ("batch", C.c_int64), ("block", C.c_int64), ("block_len", C.c_void_p),
+                ("cand_id", C.c_void_p), ("cand_u", C.c_void_p), ("A_prev", C.c_void_p), ("B_cur", C.c_void_p),
+                ("G", C.c_void_p), ("S", C.c_void_p)]
+
+
 _lib = None
 
 
@@ -66,6 +75,8 @@ def _load():
             "dsel_project_cand": ([P, I64, I64, P, P, I64, P, I64, I64, P, P, P, P, SZ, P], I32),
             "dsel_score_pairs": ([P, P, P, P, I64, I64, P, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_walk": ([P, I64, I64, P, C.POINTER(WalkArgs), P], I32),
+            "dsel_select_path_workspace_bytes": ([I64, I64, I64, I32, I64, I64], SZ),
+            "dsel_select_path": ([C.POINTER(PathArgs), C.POINTER(WalkArgs), P, SZ, P], I32),
             "dsel_verify_workspace_bytes": ([I64, I64, I64], SZ),
             "dsel_dyn_conv_workspace_bytes": ([I64, I64, I64], SZ),
             "dsel_lmhead_topk_workspace_bytes": ([I64, I64], SZ),
@@ -127,14 +138,9 @@ def topk_workspace_bytes(rows: int, vocab: int, dtype: torch.dtype) -> int:
     return int(_load().dsel_topk_workspace_bytes(rows, vocab, dt))
 
 
-def select_topk(logits: torch.Tensor, vocab: Optional[int] = None, out=None, workspace=None,
-                stream=None, block_len=None):
-    """Top-16 of every draft position.  ``logits [batch, block, ld]`` fp32 or bf16
-    with unit stride in the last dim; the first ``vocab`` (default ``ld``) entries
-    of each row are used.  Returns ``cand_id [B,L,16] int32``, ``cand_u [B,L,16] fp32``.
-    ``block_len`` (every call below takes it too): optional int32 ``[batch]`` of
-    valid positions per block (a ragged batch); padding is neither read nor
-    written."""
+def _logits_geometry(logits: torch.Tensor, vocab: Optional[int]):
+    """``(batch, block, ld, vocab)`` of logits ``[batch, block, >= vocab]`` whose
+    rows are evenly spaced with unit stride inside a row."""
     if logits.dim() != 3:
         raise ValueError("logits must be [batch, block, ld]")
     if logits.dtype not in (torch.float32, torch.bfloat16):
@@ -155,6 +161,18 @@ def select_topk(logits: torch.Tensor, vocab: Optional[int] = None, out=None, wor
     V = ld_shape if vocab is None else int(vocab)
     if V > ld_shape:
         raise ValueError("vocab exceeds the logits width")
+    return B, L, ld, V
+
+
+def select_topk(logits: torch.Tensor, vocab: Optional[int] = None, out=None, workspace=None,
+                stream=None, block_len=None):
+    """Top-16 of every draft position.  ``logits [batch, block, ld]`` fp32 or bf16
+    with unit stride in the last dim; the first ``vocab`` (default ``ld``) entries
+    of each row are used.  Returns ``cand_id [B,L,16] int32``, ``cand_u [B,L,16] fp32``.
+    ``block_len`` (every call below takes it too): optional int32 ``[batch]`` of
+    valid positions per block (a ragged batch); padding is neither read nor
+    written."""
+    B, L, ld, V = _logits_geometry(logits, vocab)
     dt = BF16 if logits.dtype == torch.bfloat16 else F32
     dev = logits.device
     if out is None:
@@ -425,16 +443,21 @@ def verify(target_logits, cand_id, path_slot, q=None, mode: int = GREEDY, temper
     return n_acc, out_tok
 
 
+def select_path_workspace_bytes(batch: int, block: int, vocab: int, dtype: torch.dtype, d: int, r: int) -> int:
+    dt = BF16 if dtype == torch.bfloat16 else F32
+    return int(_load().dsel_select_path_workspace_bytes(batch, block, vocab, dt, d, r))
+
+
 def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
                 temperature: float = 1.0, uniforms=None, vocab: Optional[int] = None,
                 want_S: bool = False, want_q: bool = False, overlap: bool = False, stream=None,
-                block_len=None):
-    """The whole selector: top-16, projections, pair scores and the fused walk.
+                block_len=None, workspace=None):
+    """The whole selector: top-16, projections, pair scores and the walk.
 
-    With ``overlap`` the gate GEMM (which needs no candidates) runs on a side
-    stream, one workgroup per output tile (dsel_project_gate_overlap), while
-    the top-16 runs on the caller's stream; otherwise it runs first, split
-    along d over the whole chip."""
+    By default one call of dsel_select_path (the gate's reduction rides in the
+    top-16 launch).  With ``overlap`` the steps are separate calls and the gate
+    GEMM (which needs no candidates) runs on a side stream, one workgroup per
+    output tile (dsel_project_gate_overlap), beside the top-16."""
     main = torch.cuda.current_stream() if stream is None else stream
     B, L = h.shape[:2]
     r = W_A.shape[0]
@@ -442,19 +465,46 @@ def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
     A_prev = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
     B_cur = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
     G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
-    ws = _project_workspace(B, L, E.shape[1], r, dev)  # one workspace serves both halves
     if overlap:
+        ws = _project_workspace(B, L, E.shape[1], r, dev)  # one workspace serves both halves
         side = side_stream(dev)
         side.wait_stream(main)
         project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=side, block_len=block_len)
         cand_id, cand_u = select_topk(logits, vocab, stream=main, block_len=block_len)
         main.wait_stream(side)
-    else:
-        project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=ws, stream=main, block_len=block_len)
-        cand_id, cand_u = select_topk(logits, vocab, stream=main, block_len=block_len)
-    project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=ws, stream=main, block_len=block_len)
-    res = score_pairs(cand_u, A_prev, B_cur, G, want_S=want_S, walk_mode=mode, cand_id=cand_id,
-                      temperature=temperature, uniforms=uniforms, want_q=want_q, stream=main,
-                      block_len=block_len)
+        project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=ws, stream=main, block_len=block_len)
+        res = score_pairs(cand_u, A_prev, B_cur, G, want_S=want_S, walk_mode=mode, cand_id=cand_id,
+                          temperature=temperature, uniforms=uniforms, want_q=want_q, stream=main,
+                          block_len=block_len)
+        res.update(cand_id=cand_id, cand_u=cand_u, A_prev=A_prev, B_cur=B_cur, G=G)
+        return res
+    Bl, Ll, ld, V = _logits_geometry(logits, vocab)
+    if (Bl, Ll) != (B, L):
+        raise ValueError("logits and h disagree on [batch, block]")
+    VE, d = E.shape
+    if VE < V:
+        raise ValueError("E needs a row for every token id below vocab")
+    for t, n, shp in ((E, "E", (VE, d)), (W_A, "W_A", (r, d)), (W_B, "W_B", (r, d)), (W_H, "W_H", (r, d)),
+                      (h, "h", (B, L, d))):
+        _need(t, n, torch.bfloat16, shp)
+    _need(verified, "verified", torch.int32, (B,))
+    cand_id = torch.empty((B, L, K), dtype=torch.int32, device=dev)
+    cand_u = torch.empty((B, L, K), dtype=torch.float32, device=dev)
+    S = torch.empty((B, L, K, K), dtype=torch.float32, device=dev)
+    wa, res = _walk_args(cand_id, mode, temperature, uniforms, want_q, True)
+    dt = BF16 if logits.dtype == torch.bfloat16 else F32
+    if workspace is None:
+        workspace = torch.empty(max(select_path_workspace_bytes(B, L, V, logits.dtype, d, r), 16),
+                                dtype=torch.uint8, device=dev)
+    wsb = workspace.numel() * workspace.element_size()
+    pa = PathArgs(logits.data_ptr(), dt, V, ld, E.data_ptr(), d, W_A.data_ptr(), W_B.data_ptr(), W_H.data_ptr(),
+                  r, h.data_ptr(), verified.data_ptr(), B, L,
+                  _lens(block_len, B).value if block_len is not None else None,
+                  cand_id.data_ptr(), cand_u.data_ptr(), A_prev.data_ptr(), B_cur.data_ptr(), G.data_ptr(),
+                  S.data_ptr())
+    _check(_load().dsel_select_path(C.byref(pa), C.byref(wa), _ptr(workspace), wsb, _stream(main)),
+           "dsel_select_path")
+    if want_S:
+        res["S"] = S
     res.update(cand_id=cand_id, cand_u=cand_u, A_prev=A_prev, B_cur=B_cur, G=G)
     return res

@@ -11,6 +11,7 @@
 #include "conv.h"
 #include "lmhead.h"
 #include "pairwalk.h"
+#include "path.h"
 #include "project.h"
 #include "topk16.h"
 #include "verify.h"
@@ -63,16 +64,24 @@ DSEL_API size_t dsel_topk_workspace_bytes(int64_t rows, int64_t vocab, dsel_dtyp
     return ns > 1 ? (size_t)rows * (size_t)ns * kK * sizeof(uint64_t) : 0;
 }
 
-DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t batch,
-                                      int64_t block, const int32_t *block_len, int64_t vocab, int64_t ld,
-                                      int32_t *cand_id,
-                                      float *cand_u, void *workspace, size_t workspace_bytes,
-                                      dsel_stream_t stream) {
+namespace {
+
+// Validation and launch geometry of each step, shared by its own entry point
+// and by dsel_select_path.  A plan with `empty` set has nothing to launch.
+struct TopkPlan {
+    TopkParams p;
+    bool bf16 = false, empty = false;
+};
+
+dsel_status plan_topk(const void *logits, dsel_dtype dt, int64_t batch, int64_t block, const int32_t *block_len,
+                      int64_t vocab, int64_t ld, int32_t *cand_id, float *cand_u, void *workspace,
+                      size_t workspace_bytes, TopkPlan *t) {
     if (dt != DSEL_F32 && dt != DSEL_BF16) return DSEL_E_DTYPE;
     if (batch < 0 || block < 0 || vocab < kK || vocab >= (int64_t)INT_MAX || ld < vocab) return DSEL_E_ARG;
     const int64_t rows = batch * block;
     if (block != 0 && rows / block != batch) return DSEL_E_ARG;
-    if (rows == 0) return DSEL_OK;  // nothing to read or write; pointers may be NULL
+    t->empty = rows == 0;
+    if (t->empty) return DSEL_OK;  // nothing to read or write; pointers may be NULL
     if (!logits || !cand_id || !cand_u) return DSEL_E_ARG;
     const size_t es = dt == DSEL_BF16 ? 2 : 4;
     if (!aligned(logits, es) || !aligned(cand_id, 4) || !aligned(cand_u, 4) || !aligned(block_len, 4))
@@ -83,8 +92,7 @@ DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t
     const size_t need = dsel_topk_workspace_bytes(rows, vocab, dt);
     if (need && (!workspace || workspace_bytes < need)) return DSEL_E_WORKSPACE;
     if (need && !aligned(workspace, 8)) return DSEL_E_ALIGN;
-
-    TopkParams p;
+    TopkParams &p = t->p;
     p.logits = (const char *)logits;
     p.rows = rows;
     p.V = vocab;
@@ -95,13 +103,47 @@ DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t
     p.cand_id = cand_id;
     p.cand_u = cand_u;
     p.partial = (uint64_t *)workspace;
-    const void *k1 = dt == DSEL_BF16 ? (const void *)topk16_kernel<true, kTopkUnroll<true>>
-                                     : (const void *)topk16_kernel<false, kTopkUnroll<false>>;
-    dsel_status s = launch(k1, dim3((unsigned)(rows * ns)), dim3(256), &p, 0, stream);
-    if (s != DSEL_OK || ns == 1) return s;
-    const void *k2 = dt == DSEL_BF16 ? (const void *)topk16_merge_kernel<true>
-                                     : (const void *)topk16_merge_kernel<false>;
-    return launch(k2, dim3((unsigned)rows), dim3(256), &p, 0, stream);
+    t->bf16 = dt == DSEL_BF16;
+    return DSEL_OK;
+}
+
+// The top-16 launch; with `gate` (a split gate job) its reduction rides along
+// as extra workgroups (path.h).
+dsel_status launch_topk(const TopkPlan &t, const GateParams *gate, int64_t gate_elems, dsel_stream_t stream) {
+    TopkParams p = t.p;
+    const int64_t wgs = p.rows * p.nsplit;
+    dsel_status s;
+    if (gate) {
+        GateParams gp = *gate;
+        int64_t tw = wgs;
+        const int64_t grid = wgs + (gate_elems + 255) / 256;
+        if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
+        const void *k = t.bf16 ? (const void *)topk16_gate_kernel<true, kTopkUnroll<true>>
+                               : (const void *)topk16_gate_kernel<false, kTopkUnroll<false>>;
+        void *args[] = {&p, &gp, &tw};
+        s = hipLaunchKernel(k, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream) == hipSuccess
+                ? DSEL_OK : DSEL_E_HIP;
+    } else {
+        const void *k = t.bf16 ? (const void *)topk16_kernel<true, kTopkUnroll<true>>
+                               : (const void *)topk16_kernel<false, kTopkUnroll<false>>;
+        s = launch(k, dim3((unsigned)wgs), dim3(256), &p, 0, stream);
+    }
+    if (s != DSEL_OK || p.nsplit == 1) return s;
+    const void *k2 = t.bf16 ? (const void *)topk16_merge_kernel<true> : (const void *)topk16_merge_kernel<false>;
+    return launch(k2, dim3((unsigned)p.rows), dim3(256), &p, 0, stream);
+}
+
+}  // namespace
+
+DSEL_API dsel_status dsel_select_topk(const void *logits, dsel_dtype dt, int64_t batch,
+                                      int64_t block, const int32_t *block_len, int64_t vocab, int64_t ld,
+                                      int32_t *cand_id, float *cand_u, void *workspace, size_t workspace_bytes,
+                                      dsel_stream_t stream) {
+    TopkPlan t;
+    dsel_status st = plan_topk(logits, dt, batch, block, block_len, vocab, ld, cand_id, cand_u, workspace,
+                               workspace_bytes, &t);
+    if (st != DSEL_OK || t.empty) return st;
+    return launch_topk(t, nullptr, 0, stream);
 }
 
 namespace {
@@ -134,14 +176,21 @@ DSEL_API size_t dsel_project_workspace_bytes(int64_t batch, int64_t block, int64
 
 namespace {
 
+struct GatePlan {
+    GateParams p;
+    int BN = 0;
+    bool empty = false;
+};
+
 // The gate job; `split` = false runs one workgroup per output tile with no
 // K split and no workspace.
-dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
-                              const uint16_t *W_H, int64_t r, const uint16_t *h, const int32_t *verified,
-                              int64_t batch, int64_t block, const int32_t *block_len, float *A_prev, float *G,
-                              void *workspace, size_t workspace_bytes, bool split, dsel_stream_t stream) {
+dsel_status plan_gate(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A, const uint16_t *W_H,
+                      int64_t r, const uint16_t *h, const int32_t *verified, int64_t batch, int64_t block,
+                      const int32_t *block_len, float *A_prev, float *G, void *workspace, size_t workspace_bytes,
+                      bool split, GatePlan *g) {
     dsel_status st = check_project_common(E, vocab, d, r, batch, block);
-    if (st != DSEL_OK || batch == 0) return st;
+    g->empty = batch == 0;
+    if (st != DSEL_OK || g->empty) return st;
     if (!W_A || !W_H || !h || !verified || !A_prev || !G) return DSEL_E_ARG;
     if (!aligned(W_A, 16) || !aligned(W_H, 16) || !aligned(h, 16) || !aligned(verified, 4) ||
         !aligned(A_prev, 16) || !aligned(G, 16) || !aligned(block_len, 4))
@@ -149,7 +198,7 @@ dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const
     const size_t need = split ? gate_workspace_bytes(batch, block, d, r) : 0;
     if (need && (!workspace || workspace_bytes < need)) return DSEL_E_WORKSPACE;
     if (need && !aligned(workspace, 16)) return DSEL_E_ALIGN;
-    GateParams p;
+    GateParams &p = g->p;
     p.E = E;
     p.V = vocab;
     p.d = (int)d;
@@ -164,23 +213,50 @@ dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const
     p.A_prev = A_prev;
     p.G = G;
     p.part = (float *)workspace;
-    const int BN = gate_bn(batch, block, r);
-    p.nside = (int)(r / BN);
+    g->BN = gate_bn(batch, block, r);
+    p.nside = (int)(r / g->BN);
     p.mt_gate = (int)((batch * block + 127) / 128);
     p.mt_ver = (int)((batch + 127) / 128);
     p.nsplit = split ? gate_nsplit(batch, block, d, r) : 1;
     const int64_t grid = (int64_t)(p.mt_gate + p.mt_ver) * p.nside * p.nsplit;
     if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
-    const void *k = BN == 256 ? (const void *)project_gate_kernel<256>
-                  : BN == 128 ? (const void *)project_gate_kernel<128>
-                  : BN == 64  ? (const void *)project_gate_kernel<64>
-                              : (const void *)project_gate_kernel<32>;
-    const int nt = tile_threads(BN);
-    st = launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
-    if (st != DSEL_OK || p.nsplit == 1) return st;
-    const int64_t elems = (batch * block + batch) * r;
-    return launch((const void *)project_gate_reduce_kernel, dim3((unsigned)((elems + 255) / 256)), dim3(256),
-                  &p, 0, stream);
+    return DSEL_OK;
+}
+
+// Output elements of the gate's reduction (0 when it is not split).
+int64_t gate_reduce_elems(const GatePlan &g) {
+    return g.p.nsplit > 1 ? ((int64_t)g.p.B * g.p.L + g.p.B) * g.p.r : 0;
+}
+
+dsel_status launch_gate_gemm(const GatePlan &g, dsel_stream_t stream) {
+    GateParams p = g.p;
+    const int64_t grid = (int64_t)(p.mt_gate + p.mt_ver) * p.nside * p.nsplit;
+    const void *k = g.BN == 256 ? (const void *)project_gate_kernel<256>
+                  : g.BN == 128 ? (const void *)project_gate_kernel<128>
+                  : g.BN == 64  ? (const void *)project_gate_kernel<64>
+                                : (const void *)project_gate_kernel<32>;
+    return launch(k, dim3((unsigned)grid), dim3(tile_threads(g.BN)), &p, 0, stream);
+}
+
+dsel_status launch_gate_reduce(const GatePlan &g, dsel_stream_t stream) {
+    GateParams p = g.p;
+    const int64_t elems = gate_reduce_elems(g);
+    if (elems == 0) return DSEL_OK;
+    return launch((const void *)project_gate_reduce_kernel, dim3((unsigned)((elems + 255) / 256)), dim3(256), &p,
+                  0, stream);
+}
+
+dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                              const uint16_t *W_H, int64_t r, const uint16_t *h, const int32_t *verified,
+                              int64_t batch, int64_t block, const int32_t *block_len, float *A_prev, float *G,
+                              void *workspace, size_t workspace_bytes, bool split, dsel_stream_t stream) {
+    GatePlan g;
+    dsel_status st = plan_gate(E, vocab, d, W_A, W_H, r, h, verified, batch, block, block_len, A_prev, G, workspace,
+                               workspace_bytes, split, &g);
+    if (st != DSEL_OK || g.empty) return st;
+    st = launch_gate_gemm(g, stream);
+    if (st != DSEL_OK) return st;
+    return launch_gate_reduce(g, stream);
 }
 
 }  // namespace
@@ -203,13 +279,20 @@ DSEL_API dsel_status dsel_project_gate_overlap(const uint16_t *E, int64_t vocab,
                              0, false, stream);
 }
 
-DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d,
-                                       const uint16_t *W_A, const uint16_t *W_B, int64_t r,
-                                       const int32_t *cand_id, int64_t batch, int64_t block,
-                                       const int32_t *block_len, float *A_prev, float *B_cur,
-                                       void *workspace, size_t workspace_bytes, dsel_stream_t stream) {
+namespace {
+
+struct CandPlan {
+    CandParams p;
+    int BN = 0;
+    bool empty = false;
+};
+
+dsel_status plan_cand(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A, const uint16_t *W_B,
+                      int64_t r, const int32_t *cand_id, int64_t batch, int64_t block, const int32_t *block_len,
+                      float *A_prev, float *B_cur, void *workspace, size_t workspace_bytes, CandPlan *c) {
     dsel_status st = check_project_common(E, vocab, d, r, batch, block);
-    if (st != DSEL_OK || batch == 0) return st;
+    c->empty = batch == 0;
+    if (st != DSEL_OK || c->empty) return st;
     if (!W_A || !W_B || !cand_id || !A_prev || !B_cur) return DSEL_E_ARG;
     if (!aligned(W_A, 16) || !aligned(W_B, 16) || !aligned(cand_id, 4) || !aligned(A_prev, 16) ||
         !aligned(B_cur, 16) || !aligned(block_len, 4))
@@ -218,7 +301,7 @@ DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t
     const size_t coff = cand_workspace_offset(batch, block, d, r);
     if (cneed && (!workspace || workspace_bytes < coff + cneed)) return DSEL_E_WORKSPACE;
     if (cneed && !aligned(workspace, 16)) return DSEL_E_ALIGN;
-    CandParams p;
+    CandParams &p = c->p;
     p.E = E;
     p.V = vocab;
     p.d = (int)d;
@@ -231,28 +314,48 @@ DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t
     p.M = batch * block * kK;
     p.A_prev = A_prev;
     p.B_cur = B_cur;
-    const int BM = 128;
-    const int BN = r % 256 == 0 ? 256 : r % 128 == 0 ? 128 : r % 64 == 0 ? 64 : 32;
-    p.nside = (int)(r / BN);
+    constexpr int BM = 128;
+    c->BN = r % 256 == 0 ? 256 : r % 128 == 0 ? 128 : r % 64 == 0 ? 64 : 32;
+    p.nside = (int)(r / c->BN);
     p.mt = (int)((p.M + BM - 1) / BM);
     p.mt_pad = (p.mt + 7) / 8 * 8;
     p.nsplit = cand_nsplit(batch, block, d, r);
     p.part = cneed ? (float *)((char *)workspace + coff) : nullptr;
     const int64_t grid = (int64_t)p.mt_pad * 2 * p.nside * p.nsplit;
     if (grid >= (int64_t)INT_MAX || p.M * 2 * r >= (int64_t)INT_MAX * 256) return DSEL_E_ARG;
+    return DSEL_OK;
+}
+
+dsel_status launch_cand(const CandPlan &c, dsel_stream_t stream) {
+    CandParams p = c.p;
+    const int BN = c.BN;
+    const int64_t grid = (int64_t)p.mt_pad * 2 * p.nside * p.nsplit;
     const void *k = BN == 256 ? (const void *)project_cand_kernel<256>
                   : BN == 128 ? (const void *)project_cand_kernel<128>
                   : BN == 64  ? (const void *)project_cand_kernel<64>
                               : (const void *)project_cand_kernel<32>;
-    const int nt = tile_threads(BN);
-    st = launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
+    dsel_status st = launch(k, dim3((unsigned)grid), dim3(tile_threads(BN)), &p, 0, stream);
     if (st != DSEL_OK || p.nsplit == 1) return st;
-    const int64_t elems = p.M * 2 * r;
+    const int64_t elems = p.M * 2 * p.r;
     const void *kr = BN == 256 ? (const void *)project_cand_reduce_kernel<256>
                    : BN == 128 ? (const void *)project_cand_reduce_kernel<128>
                    : BN == 64  ? (const void *)project_cand_reduce_kernel<64>
                                : (const void *)project_cand_reduce_kernel<32>;
     return launch(kr, dim3((unsigned)((elems + 255) / 256)), dim3(256), &p, 0, stream);
+}
+
+}  // namespace
+
+DSEL_API dsel_status dsel_project_cand(const uint16_t *E, int64_t vocab, int64_t d,
+                                       const uint16_t *W_A, const uint16_t *W_B, int64_t r,
+                                       const int32_t *cand_id, int64_t batch, int64_t block,
+                                       const int32_t *block_len, float *A_prev, float *B_cur,
+                                       void *workspace, size_t workspace_bytes, dsel_stream_t stream) {
+    CandPlan c;
+    dsel_status st = plan_cand(E, vocab, d, W_A, W_B, r, cand_id, batch, block, block_len, A_prev, B_cur,
+                               workspace, workspace_bytes, &c);
+    if (st != DSEL_OK || c.empty) return st;
+    return launch_cand(c, stream);
 }
 
 DSEL_API dsel_status dsel_project(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
@@ -298,24 +401,32 @@ dsel_status launch_walk(PairParams &p, dsel_stream_t stream) {
 
 }  // namespace
 
-DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const float *B_cur,
-                                      const float *G, int64_t batch, int64_t block,
-                                      const int32_t *block_len, int64_t r, float *S,
-                                      const dsel_walk_args *walk, dsel_stream_t stream) {
+namespace {
+
+struct PairPlan {
+    PairParams p = {};
+    bool walk = false, empty = false;
+};
+
+dsel_status plan_pairs(const float *cand_u, const float *A_prev, const float *B_cur, const float *G, int64_t batch,
+                       int64_t block, const int32_t *block_len, int64_t r, float *S, const dsel_walk_args *walk,
+                       PairPlan *q) {
     if (batch < 0 || batch >= (int64_t)INT_MAX / DSEL_MAX_BLOCK || block < 1 || block > DSEL_MAX_BLOCK)
         return DSEL_E_ARG;
     if (r < 32 || r > DSEL_MAX_RANK || r % 32 != 0) return DSEL_E_ARG;
     if (walk && walk->mode != DSEL_GREEDY && walk->mode != DSEL_SAMPLED) return DSEL_E_DTYPE;
-    if (batch == 0) return DSEL_OK;  // nothing to read or write; pointers may be NULL
+    q->empty = batch == 0;
+    if (q->empty) return DSEL_OK;  // nothing to read or write; pointers may be NULL
     if (!cand_u || !A_prev || !B_cur || !G || !S) return DSEL_E_ARG;
     if (!aligned(A_prev, 16) || !aligned(B_cur, 16) || !aligned(G, 16) || !aligned(cand_u, 4) ||
         !aligned(S, 4) || !aligned(block_len, 4))
         return DSEL_E_ALIGN;
-    PairParams p = {};
+    PairParams &p = q->p;
     if (walk) {
         dsel_status s = check_walk(walk, &p.w);
         if (s != DSEL_OK) return s;
     }
+    q->walk = walk != nullptr;
     p.cand_u = cand_u;
     p.A_prev = A_prev;
     p.B_cur = B_cur;
@@ -326,10 +437,27 @@ DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, 
     p.r = (int)r;
     p.S = S;
     p.S_in = S;
-    const int64_t positions = batch * block;
-    dsel_status st = launch(pair_kernel_for(r), dim3((unsigned)positions), dim3(256), &p, 0, stream);
-    if (st != DSEL_OK || !walk) return st;
+    return DSEL_OK;
+}
+
+dsel_status launch_pairs(const PairPlan &q, dsel_stream_t stream) {
+    PairParams p = q.p;
+    const int64_t positions = (int64_t)p.B * p.L;
+    dsel_status st = launch(pair_kernel_for(p.r), dim3((unsigned)positions), dim3(256), &p, 0, stream);
+    if (st != DSEL_OK || !q.walk) return st;
     return launch_walk(p, stream);
+}
+
+}  // namespace
+
+DSEL_API dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const float *B_cur,
+                                      const float *G, int64_t batch, int64_t block,
+                                      const int32_t *block_len, int64_t r, float *S,
+                                      const dsel_walk_args *walk, dsel_stream_t stream) {
+    PairPlan q;
+    dsel_status st = plan_pairs(cand_u, A_prev, B_cur, G, batch, block, block_len, r, S, walk, &q);
+    if (st != DSEL_OK || q.empty) return st;
+    return launch_pairs(q, stream);
 }
 
 DSEL_API dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const int32_t *block_len,
@@ -348,6 +476,61 @@ DSEL_API dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, con
     p.L = (int)block;
     p.len = block_len;
     return launch_walk(p, stream);
+}
+
+// ---- the whole selector ----------------------------------------------------
+
+namespace {
+
+// Workspace of dsel_select_path: the top-16's partial lists, then (256-byte
+// aligned) the projections' workspace.
+size_t path_topk_bytes(int64_t rows, int64_t vocab, dsel_dtype dt) {
+    return (dsel_topk_workspace_bytes(rows, vocab, dt) + 255) / 256 * 256;
+}
+
+}  // namespace
+
+DSEL_API size_t dsel_select_path_workspace_bytes(int64_t batch, int64_t block, int64_t vocab, dsel_dtype dt,
+                                                 int64_t d, int64_t r) {
+    if (batch <= 0 || block < 1 || batch > (int64_t)INT_MAX / block) return 0;
+    return path_topk_bytes(batch * block, vocab, dt) + dsel_project_workspace_bytes(batch, block, d, r);
+}
+
+DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_args *walk, void *workspace,
+                                      size_t workspace_bytes, dsel_stream_t stream) {
+    if (!a || !walk) return DSEL_E_ARG;
+    if (a->batch < 0 || a->block < 1 || a->batch > (int64_t)INT_MAX / a->block) return DSEL_E_ARG;
+    const size_t tb = a->batch ? path_topk_bytes(a->batch * a->block, a->vocab, a->dt) : 0;
+    if (tb > workspace_bytes) return DSEL_E_WORKSPACE;
+    void *pws = workspace ? (char *)workspace + tb : nullptr;
+    const size_t pwsb = workspace_bytes - tb;
+    // every step is validated before anything is launched
+    TopkPlan t;
+    GatePlan g;
+    CandPlan c;
+    PairPlan q;
+    dsel_status st = plan_topk(a->logits, a->dt, a->batch, a->block, a->block_len, a->vocab, a->ld, a->cand_id,
+                               a->cand_u, workspace, workspace_bytes, &t);
+    if (st == DSEL_OK)
+        st = plan_gate(a->E, a->vocab, a->d, a->W_A, a->W_H, a->r, a->h, a->verified, a->batch, a->block,
+                       a->block_len, a->A_prev, a->G, pws, pwsb, true, &g);
+    if (st == DSEL_OK)
+        st = plan_cand(a->E, a->vocab, a->d, a->W_A, a->W_B, a->r, a->cand_id, a->batch, a->block, a->block_len,
+                       a->A_prev, a->B_cur, pws, pwsb, &c);
+    if (st == DSEL_OK)
+        st = plan_pairs(a->cand_u, a->A_prev, a->B_cur, a->G, a->batch, a->block, a->block_len, a->r, a->S, walk,
+                        &q);
+    if (st != DSEL_OK || a->batch == 0) return st;
+    // gate GEMM; top-16 with the gate's reduction beside it; candidate GEMM;
+    // pair scores and the walk
+    st = launch_gate_gemm(g, stream);
+    if (st == DSEL_OK) {
+        const int64_t ge = gate_reduce_elems(g);
+        st = launch_topk(t, ge ? &g.p : nullptr, ge, stream);
+    }
+    if (st == DSEL_OK) st = launch_cand(c, stream);
+    if (st == DSEL_OK) st = launch_pairs(q, stream);
+    return st;
 }
 
 DSEL_API dsel_status dsel_device_error(int32_t *out_code, dsel_stream_t stream) {

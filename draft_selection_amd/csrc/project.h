@@ -713,9 +713,9 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
 }
 
 // Sum the K splits of the gate job in split order, then the epilogue.
-__global__ __launch_bounds__(256) void project_gate_reduce_kernel(GateParams p) {
+// Output element e (row e / r, column e % r).
+__device__ __forceinline__ void gate_reduce_elem(const GateParams &p, int64_t e) {
     const int64_t rows_all = (int64_t)p.B * p.L + p.B;
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (e >= rows_all * p.r) return;
     const int64_t row = e / p.r;
     const int n = (int)(e % p.r);
@@ -734,6 +734,10 @@ __global__ __launch_bounds__(256) void project_gate_reduce_kernel(GateParams p) 
         base[0] = sum;
         for (int z = 1; z < kK; ++z) base[(int64_t)z * p.r] = 0.0f;
     }
+}
+
+__global__ __launch_bounds__(256) void project_gate_reduce_kernel(GateParams p) {
+    gate_reduce_elem(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 // Column tile and K splits of the gate job (M = batch*block + batch rows, a

@@ -223,12 +223,13 @@ __device__ __forceinline__ void chunk_seed(WaveTop &st, const u32x4 (&w)[U], int
     chunk_offer<BF16, U>(st, w, v0, ve, h0, skip);
 }
 
+// The work of workgroup `bid`: split `bid % nsplit` of row `bid / nsplit`.
 template <bool BF16, int U>
-__global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
+__device__ __forceinline__ void topk16_block(const TopkParams &p, int64_t bid) {
     constexpr int ES = BF16 ? 2 : 4;
     constexpr int EPV = 16 / ES;
-    const int64_t row = blockIdx.x / p.nsplit;
-    const int split = (int)(blockIdx.x % p.nsplit);
+    const int64_t row = bid / p.nsplit;
+    const int split = (int)(bid % p.nsplit);
     if (!position_live(p.len, (uint32_t)row, p.L)) return;  // padding row (ragged batches)
     const int wave = (int)(threadIdx.x / kWave);
     const uint32_t lane = lane_id();
@@ -312,6 +313,11 @@ __global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
             }
         }
     }
+}
+
+template <bool BF16, int U>
+__global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
+    topk16_block<BF16, U>(p, blockIdx.x);
 }
 
 // Merge the nsplit partial lists of a row: one workgroup (4 waves) per row.

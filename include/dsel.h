@@ -213,6 +213,44 @@ dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const flo
 dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const int32_t *block_len,
                       const dsel_walk_args *walk, dsel_stream_t stream);
 
+/* select_path -- the whole selector in one call ([P1] Method > Lightweight Path
+ * Selector, [P3] "Selection beats correction"): dsel_select_topk, dsel_project
+ * (gate and candidates), dsel_score_pairs and the walk, on one stream, with the
+ * same outputs bit for bit as those calls made one after the other.  The gate
+ * GEMM's split-K reduction runs inside the top-16 launch, beside it, instead of
+ * as a launch of its own.
+ *   Inputs and outputs are those of the separate calls; `vocab` is the
+ *   logits' width in use, and E needs at least `vocab` rows (every candidate
+ *   id is below it; the projections' id check uses it).  All outputs (cand_id,
+ *   cand_u, A_prev, B_cur, G, S) are required.
+ *   walk       the walk arguments (required), as for dsel_score_pairs.
+ *   workspace  at least dsel_select_path_workspace_bytes() bytes (16-byte
+ *              aligned); contents need no initialisation.
+ * Requirements: those of every step (d % 64 == 0; r % 32 == 0, 32 <= r <= 256;
+ * 1 <= block <= DSEL_MAX_BLOCK; 16 <= vocab < 2^31; ld >= vocab). */
+typedef struct {
+    const void *logits;   /* [batch*block][ld] of dtype dt */
+    dsel_dtype dt;
+    int64_t vocab, ld;
+    const uint16_t *E;    /* [>= vocab, d] bf16 */
+    int64_t d;
+    const uint16_t *W_A, *W_B, *W_H; /* [r, d] bf16 */
+    int64_t r;
+    const uint16_t *h;    /* [batch, block, d] bf16 */
+    const int32_t *verified; /* [batch] */
+    int64_t batch, block;
+    const int32_t *block_len; /* [batch] or NULL (see "Ragged batches") */
+    int32_t *cand_id;     /* out [batch, block, 16] */
+    float *cand_u;        /* out [batch, block, 16] */
+    float *A_prev, *B_cur; /* out [batch, block, 16, r] */
+    float *G;             /* out [batch, block, r] */
+    float *S;             /* out [batch, block, 16, 16] */
+} dsel_path_args;
+size_t dsel_select_path_workspace_bytes(int64_t batch, int64_t block, int64_t vocab, dsel_dtype dt, int64_t d,
+                                        int64_t r);
+dsel_status dsel_select_path(const dsel_path_args *args, const dsel_walk_args *walk, void *workspace,
+                             size_t workspace_bytes, dsel_stream_t stream);
+
 /* verify -- lossless verification of the drafted blocks against the target
  * model, the step after the walk ([P1] Method, last paragraph, and Setup:
  * sampling stays lossless through rejection sampling; [P3] "One pass to draft,

@@ -135,3 +135,32 @@ def test_verify_validation(lib):
     assert call(ws=None) == -4 and call(wsb=ws - 1) == -4
     assert call(B=0, tl=None, cand=None) == 0               # no work: pointers may be NULL
     assert call(lens=P(0x100002)) == -3                     # ragged lengths: int32 alignment
+
+
+def test_select_path_validation(lib):
+    """dsel_select_path validates every step before launching anything."""
+    import draft_selection_amd as ds
+
+    P = C.c_void_p
+    f = 0x100000  # never dereferenced
+    w = ds.WalkArgs(0, 1.0, None, f, f, f, None, None)
+    ws = lib.dsel_select_path_workspace_bytes(1, 16, 151936, 1, 2560, 256)
+    assert ws > lib.dsel_project_workspace_bytes(1, 16, 2560, 256)  # top-16 partials come first
+
+    def args(**kw):
+        a = dict(logits=f, dt=1, vocab=151936, ld=151936, E=f, d=2560, W_A=f, W_B=f, W_H=f, r=256, h=f,
+                 verified=f, batch=1, block=16, block_len=None, cand_id=f, cand_u=f, A_prev=f, B_cur=f, G=f, S=f)
+        a.update(kw)
+        return ds.PathArgs(*[a[n] for n, _ in ds.PathArgs._fields_])
+
+    call = lambda a, walk=w, wsp=f, wsb=ws: lib.dsel_select_path(C.byref(a), C.byref(walk) if walk else None,
+                                                                  P(wsp) if wsp else None, wsb, None)
+    assert lib.dsel_select_path(None, C.byref(w), P(f), ws, None) == -1
+    assert call(args(), walk=None) == -1
+    assert call(args(), wsb=0) == -4 and call(args(), wsp=None) == -4
+    assert call(args(dt=5)) == -2
+    assert call(args(d=96)) == -1 and call(args(r=48)) == -1 and call(args(block=33), wsb=1 << 40) == -1
+    assert call(args(S=None)) == -1 and call(args(G=None)) == -1
+    assert call(args(h=0x100002)) == -3 and call(args(block_len=0x100002)) == -3
+    assert call(args(batch=0, logits=None, E=None)) == 0  # no work
+

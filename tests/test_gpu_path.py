@@ -1,0 +1,78 @@
+"""dsel_select_path (the whole selector in one call) against the separate calls.
+
+Same kernels, same order, same arithmetic: every output must come out bit for
+bit as from dsel_select_topk, dsel_project_gate, dsel_project_cand and
+dsel_score_pairs called one after the other (which the other GPU tests pin to
+the oracle).  Shapes cover the gate split (reduction inside the top-16 launch),
+split top-16 rows (merge kernel), the unsplit gate of large batches, ragged
+batches and both walks."""
+import numpy as np
+import pytest
+import torch
+
+import draft_selection_amd as ds
+import synth
+from helpers import to_dev
+
+pytestmark = pytest.mark.gpu
+K = 16
+KEYS = ("cand_id", "cand_u", "A_prev", "B_cur", "G", "S", "path_tok", "path_slot", "path_s", "q")
+
+
+def _separate(d, mode, lens, T=1.0):
+    B, L = d["h"].shape[:2]
+    r = d["W_A"].shape[0]
+    dev = d["E"].device
+    A = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+    Bc = torch.empty_like(A)
+    G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
+    ds.project_gate(d["E"], d["W_A"], d["W_H"], d["h"], d["verified"], A, G, block_len=lens)
+    cid, cu = ds.select_topk(d["logits"], block_len=lens)
+    ds.project_cand(d["E"], d["W_A"], d["W_B"], cid, A, Bc, block_len=lens)
+    res = ds.score_pairs(cu, A, Bc, G, want_S=True, walk_mode=mode, cand_id=cid, temperature=T,
+                         uniforms=d["uniforms"], want_q=True, block_len=lens)
+    res.update(cand_id=cid, cand_u=cu, A_prev=A, B_cur=Bc, G=G)
+    torch.cuda.synchronize()
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def _fused(d, mode, lens, T=1.0):
+    res = ds.select_path(d["logits"], d["E"], d["W_A"], d["W_B"], d["W_H"], d["h"], d["verified"], mode=mode,
+                         temperature=T, uniforms=d["uniforms"], want_S=True, want_q=True, block_len=lens)
+    torch.cuda.synchronize()
+    assert ds.device_error() == 0
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def _equal(a, b, lens, L):
+    n_of = [L] * a["cand_id"].shape[0] if lens is None else lens
+    for k in KEYS:
+        for blk, n in enumerate(n_of):
+            x, y = a[k][blk, :n], b[k][blk, :n]
+            if x.dtype.kind == "f":
+                x, y = x.view(np.uint32), y.view(np.uint32)
+            np.testing.assert_array_equal(x, y, err_msg=f"{k} block {blk}")
+
+
+@pytest.mark.parametrize("name,mode,ragged", [
+    ("c0", 0, False), ("c0", 1, True), ("c1", 0, False), ("c1", 1, False),
+    ("c2", 0, False), ("c2", 0, True), ("c3", 1, False), ("c3", 1, True)])
+def test_path_equals_separate_calls(dev, name, mode, ragged):
+    cfg = synth.CONFIGS[name]
+    d = to_dev(synth.make(cfg, seed=11), dev)
+    lens_np = synth.make_block_len(cfg, seed=11) if ragged else None
+    if ragged and name == "c0":
+        lens_np = np.array([0, 8, 3, 5], np.int32)
+    lens = None if lens_np is None else torch.from_numpy(lens_np).to(dev)
+    a = _fused(d, mode, lens)
+    b = _separate(d, mode, lens)
+    _equal(a, b, None if lens_np is None else lens_np, cfg.block)
+
+
+def test_path_large_batch_unsplit_gate(dev):
+    """256 blocks of 16 at d 2560: the gate GEMM needs no split, so nothing
+    rides in the top-16 launch."""
+    cfg = synth.CONFIGS["c2"].replace(batch=256)
+    d = to_dev(synth.make(cfg, seed=12), dev)
+    assert ds.lib().dsel_project_workspace_bytes(256, 16, 2560, 256) >= 0
+    _equal(_fused(d, 0, None), _separate(d, 0, None), None, cfg.block)
