@@ -76,3 +76,22 @@ def test_path_large_batch_unsplit_gate(dev):
     d = to_dev(synth.make(cfg, seed=12), dev)
     assert ds.lib().dsel_project_workspace_bytes(256, 16, 2560, 256) >= 0
     _equal(_fused(d, 0, None), _separate(d, 0, None), None, cfg.block)
+
+
+def test_path_with_padded_logit_rows(dev):
+    """bf16 logit rows padded past the vocabulary (ld > vocab) and E with more
+    rows than the vocabulary in use: the same bits as the separate calls."""
+    cfg = synth.CONFIGS["c1"].replace(batch=3, vocab=150000)
+    inp = synth.make(cfg, seed=14)
+    d = to_dev(inp, dev)
+    V, ld = 149000, 150016
+    wide = torch.full((cfg.batch, cfg.block, ld), -3.0e38, dtype=torch.bfloat16, device=dev)
+    wide[..., :V] = d["logits"][..., :V]
+    d["logits"] = wide
+    a = ds.select_path(wide, d["E"], d["W_A"], d["W_B"], d["W_H"], d["h"], d["verified"], vocab=V, want_S=True,
+                       want_q=True, uniforms=d["uniforms"])
+    torch.cuda.synchronize()
+    assert ds.device_error() == 0
+    cid, cu = ds.select_topk(wide, vocab=V)
+    assert torch.equal(a["cand_id"], cid) and torch.equal(a["cand_u"].view(torch.int32), cu.view(torch.int32))
+    assert int(a["cand_id"].max()) < V

@@ -234,3 +234,34 @@ def test_empty_batch_of_blocks(dev):
     t = tok.cpu().numpy()
     np.testing.assert_array_equal(t[:, 0], np.argmax(tl[:, 0], axis=1))
     assert np.all(t[:, 1:] == -1)
+
+
+def test_ragged_longest_block_and_padded_rows(ora, dev):
+    """Blocks of up to 32 positions (the longest the walk takes) with fp32
+    logit rows padded past the vocabulary (ld > vocab)."""
+    cfg = synth.CONFIGS["c0"].replace(batch=5, block=32, vocab=700)
+    inp = synth.make(cfg, seed=31)
+    lens = np.array([32, 0, 17, 1, 31], np.int32)
+    V, ld = cfg.vocab, 704
+    wide = np.full((cfg.batch, cfg.block, ld), np.float32(1e30), np.float32)  # never read past vocab
+    wide[..., :V] = inp["logits"]
+    d = to_dev(inp, dev)
+    d["logits"] = torch.from_numpy(wide).to(dev)
+    for mode in (0, 1):
+        res = ds.select_path(d["logits"], d["E"], d["W_A"], d["W_B"], d["W_H"], d["h"], d["verified"], mode=mode,
+                             uniforms=d["uniforms"], vocab=V, want_S=True, block_len=_lens_dev(lens, dev))
+        torch.cuda.synchronize()
+        assert ds.device_error() == 0
+        g = {k: v.cpu().numpy() for k, v in res.items()}
+        ref = ora.run_ragged(inp, lens, mode)
+        flagged = 0
+        for b, n in enumerate(lens):
+            if n == 0:
+                continue
+            sl = lambda a: a[b:b + 1, :n]
+            gb = {k: sl(v) for k, v in g.items()}
+            np.testing.assert_array_equal(gb["cand_id"], sl(ref["cand_id"]))
+            eps, _, _, _ = check_scores(gb["S"], sl(ref["S"]), sl(ref["cand_u"]))
+            flagged += check_walk(ora, gb, sl(ref["S"]), gb["S"], sl(ref["cand_id"]), mode, sl(inp["uniforms"]),
+                                  1.0, eps)
+        assert flagged <= 1
