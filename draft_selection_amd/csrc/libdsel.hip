@@ -116,17 +116,18 @@ dsel_status launch_topk(const TopkPlan &t, const GateParams *gate, int64_t gate_
     if (gate) {
         GateParams gp = *gate;
         int64_t tw = wgs;
-        const int64_t grid = wgs + (gate_elems + 255) / 256;
+        constexpr int TT = 64 * kTopkWaves;
+        const int64_t grid = wgs + (gate_elems + TT - 1) / TT;
         if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
         const void *k = t.bf16 ? (const void *)topk16_gate_kernel<true, kTopkUnroll<true>>
                                : (const void *)topk16_gate_kernel<false, kTopkUnroll<false>>;
         void *args[] = {&p, &gp, &tw};
-        s = hipLaunchKernel(k, dim3((unsigned)grid), dim3(256), args, 0, (hipStream_t)stream) == hipSuccess
+        s = hipLaunchKernel(k, dim3((unsigned)grid), dim3(64 * kTopkWaves), args, 0, (hipStream_t)stream) == hipSuccess
                 ? DSEL_OK : DSEL_E_HIP;
     } else {
         const void *k = t.bf16 ? (const void *)topk16_kernel<true, kTopkUnroll<true>>
                                : (const void *)topk16_kernel<false, kTopkUnroll<false>>;
-        s = launch(k, dim3((unsigned)wgs), dim3(256), &p, 0, stream);
+        s = launch(k, dim3((unsigned)wgs), dim3(64 * kTopkWaves), &p, 0, stream);
     }
     if (s != DSEL_OK || p.nsplit == 1) return s;
     const void *k2 = t.bf16 ? (const void *)topk16_merge_kernel<true> : (const void *)topk16_merge_kernel<false>;

@@ -23,6 +23,14 @@
 // Register buffers per wave: DEPTH - 1 chunks in flight while one is filtered
 // (MI355X, 1,024 bf16 rows of 151,936: 3 is 1-2 us faster than 2, and 4-5 us
 // faster on ragged batches of the 5 / 8 / 16 mix).
+// Waves per row workgroup, 4 or 8 (MI355X, 1,024 bf16 rows of 151,936: 54.5 us
+// at 4 waves against 60.3 at 8, which doubles each row's loads in flight).
+#ifndef DSEL_TOPK_WAVES
+#define DSEL_TOPK_WAVES 4
+#endif
+constexpr int kTopkWaves = DSEL_TOPK_WAVES;
+static_assert(kTopkWaves == 4 || kTopkWaves == 8, "top-16 waves per workgroup");
+
 #ifndef DSEL_TOPK_DEPTH
 #define DSEL_TOPK_DEPTH 3
 #endif
@@ -253,10 +261,10 @@ __device__ __forceinline__ void topk16_block(const TopkParams &p, int64_t bid) {
     // The workgroup owns vectors [wb, we) of the row; its waves take turns
     // chunk by chunk, so the four waves sweep one contiguous stretch together.
     const int64_t wb = nvec * split / p.nsplit, we = nvec * (split + 1) / p.nsplit;
-    const int64_t gw = (int64_t)split * 4 + wave;
+    const int64_t gw = (int64_t)split * kTopkWaves + wave;
 #else
-    const int64_t nw = (int64_t)p.nsplit * 4;
-    const int64_t gw = (int64_t)split * 4 + wave;
+    const int64_t nw = (int64_t)p.nsplit * kTopkWaves;
+    const int64_t gw = (int64_t)split * kTopkWaves + wave;
     const int64_t vb = nvec * gw / nw, ve = nvec * (gw + 1) / nw;
 #endif
 
@@ -269,7 +277,7 @@ __device__ __forceinline__ void topk16_block(const TopkParams &p, int64_t bid) {
     // flight while the current one is filtered (DSEL_TOPK_DEPTH register buffers).
     constexpr int STEP = U * kWave;
 #if DSEL_TOPK_INTERLEAVE
-    constexpr int64_t CS = 4 * STEP;  // distance between a wave's chunks
+    constexpr int64_t CS = kTopkWaves * STEP;  // distance between a wave's chunks
     const int64_t vb = wb + wave * STEP, ve = we;
     if (vb < ve) {
         const int64_t nch = (ve - vb + CS - 1) / CS;
@@ -322,11 +330,19 @@ __device__ __forceinline__ void topk16_block(const TopkParams &p, int64_t bid) {
         });
     }
 
-    __shared__ uint64_t sk[4 * kK];
+    __shared__ uint64_t sk[kTopkWaves * kK];
     if (lane < (uint32_t)kK) sk[wave * kK + lane] = st.key;
     __syncthreads();
+    if constexpr (kTopkWaves == 8) {
+        // waves 0 and 4 each sort four lists; wave 0 then sorts the two bests
+        uint64_t best = 0ull;
+        if (wave == 0 || wave == 4) best = wave_sort64_desc(sk[wave * kK + lane]);
+        __syncthreads();
+        if ((wave == 0 || wave == 4) && lane < (uint32_t)kK) sk[(wave / 4) * kK + lane] = best;
+        __syncthreads();
+    }
     if (wave == 0) {
-        uint64_t srt = wave_sort64_desc(sk[lane]);
+        uint64_t srt = wave_sort64_desc(kTopkWaves == 8 ? (lane < 2u * kK ? sk[lane] : 0ull) : sk[lane]);
         if (lane < (uint32_t)kK) {
             if (p.nsplit == 1) {
                 uint32_t id = key_id(srt);  // always < V: every row has >= 16 real keys
@@ -342,7 +358,7 @@ __device__ __forceinline__ void topk16_block(const TopkParams &p, int64_t bid) {
 }
 
 template <bool BF16, int U>
-__global__ __launch_bounds__(256) void topk16_kernel(TopkParams p) {
+__global__ __launch_bounds__(64 * kTopkWaves) void topk16_kernel(TopkParams p) {
     topk16_block<BF16, U>(p, blockIdx.x);
 }
 
