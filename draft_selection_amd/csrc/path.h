@@ -6,10 +6,11 @@
 // The kernels are those of the separate calls, in the same order and with the
 // same arithmetic, so every output has the same bits.  One fusion: the gate's
 // split-K reduction, which needs neither the top-16 nor LDS, rides in the
-// top-16 launch as extra workgroups after the top-16 ones.  They fill the slots
-// the top-16 leaves free (it holds 4 of the 8 four-wave workgroups a CU can
-// keep), so the reduction runs beside the HBM-bound top-16 instead of as a
-// launch of its own between the gate GEMM and the top-16.
+// top-16 launch as extra workgroups after the top-16 ones.  They fill the
+// workgroup slots the top-16 leaves free (at 1,024 rows it holds 4 per CU of
+// the 7 its registers allow), so the reduction runs beside the HBM-bound
+// top-16 instead of as a launch of its own between the gate GEMM and the
+// top-16.
 #pragma once
 
 #include "project.h"
