@@ -9,10 +9,17 @@ is no CPU fallback, and a missing library is an error.
 Entry points (same names as the C ABI):
   select_topk(logits, vocab=None)                   -> cand_id, cand_u
   project(E, W_A, W_B, W_H, h, cand_id, verified)   -> A_prev, B_cur, G
+  project_gate(...), project_gate_overlap(...), project_cand(...)  (its halves)
   score_pairs(cand_u, A_prev, B_cur, G, ...)        -> S and/or the walk
   walk(S, cand_id, ...)                             -> the walk alone
+  select_path(logits, E, W_A, W_B, W_H, h, verified, ...)  -> all of the above
+                                                       in one dsel_select_path call
+  verify(target_logits, cand_id, path_slot, ...)    -> n_accepted, out_tok
+  dyn_conv(x, x_prev, base, W_c)                    -> y
+  lmhead_topk(h, W)                                 -> cand_id, cand_u
   device_error()                                    -> sticky device error bits
-and ``select_path`` running the whole selector.
+Every batch call takes ``block_len`` (a ragged batch: valid positions per
+block, int32 on the GPU) and ``stream``.
 """
 from __future__ import annotations
 

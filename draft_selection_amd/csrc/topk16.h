@@ -3,16 +3,17 @@
 // selector keeps the top-16 candidates of each position.)
 //
 // HBM-bound streaming selection.  One workgroup (4 waves) scans one row, or a
-// 1/nsplit slice of it when there are too few rows to fill the chip; each wave
-// streams a contiguous range of 16-byte vectors with non-temporal loads.
-// Every wave keeps its running top-16 as one 64-bit key per lane in lanes
-// 0..15 (sorted, lane 0 best) and filters incoming elements against the float
-// value of its 16th key: almost every element fails that single compare, and
-// the rare survivors are inserted one at a time with a cross-lane shift.  The
-// first 64 x U elements of a wave seed the list with the sorted lane maxima
-// (the 16 best of them bound the rest).  Loads are triple-buffered in
-// registers, so a chunk's HBM latency hides behind the previous chunks' filters.  Waves merge through LDS with a 64-key
-// bitonic sort; split rows merge in a second, one-wave-per-row kernel.
+// 1/nsplit slice of it when there are too few rows to fill the chip; its waves
+// take turns chunk by chunk over one contiguous stretch, with 16-byte
+// non-temporal loads.  Every wave keeps its running top-16 as one 64-bit key
+// per lane in lanes 0..15 (sorted, lane 0 best) and filters incoming elements
+// against the value of its 16th key: almost every chunk fails that single
+// compare, and the rare survivors are inserted one at a time (a DPP shift of
+// the list).  The first chunk of a wave seeds the list with its sorted lane
+// maxima (the 16 best of them bound the rest).  Loads are triple-buffered in
+// registers, so a chunk's HBM latency hides behind the previous chunks'
+// filters.  Waves merge through LDS with a 64-key bitonic sort (DPP and
+// permlane swaps); split rows merge in a second kernel, one workgroup per row.
 #pragma once
 
 #include "common.h"
@@ -23,19 +24,19 @@
 // Register buffers per wave: DEPTH - 1 chunks in flight while one is filtered
 // (MI355X, 1,024 bf16 rows of 151,936: 3 is 1-2 us faster than 2, and 4-5 us
 // faster on ragged batches of the 5 / 8 / 16 mix).
+#ifndef DSEL_TOPK_DEPTH
+#define DSEL_TOPK_DEPTH 3
+#endif
 // Waves per row workgroup, 4 or 8 (MI355X, 1,024 bf16 rows of 151,936: 54.5 us
 // at 4 waves against 60.3 at 8, which doubles each row's loads in flight).
 #ifndef DSEL_TOPK_WAVES
 #define DSEL_TOPK_WAVES 4
 #endif
-constexpr int kTopkWaves = DSEL_TOPK_WAVES;
-static_assert(kTopkWaves == 4 || kTopkWaves == 8, "top-16 waves per workgroup");
-
-#ifndef DSEL_TOPK_DEPTH
-#define DSEL_TOPK_DEPTH 3
-#endif
 
 namespace dsel {
+
+constexpr int kTopkWaves = DSEL_TOPK_WAVES;
+static_assert(kTopkWaves == 4 || kTopkWaves == 8, "top-16 waves per workgroup");
 
 // 16-byte vectors per lane and chunk (a wave's chunk is 64 U vectors).  Measured
 // on MI355X (one row per workgroup, 1,024 rows): bf16 rows of 151,936 take
