@@ -270,6 +270,34 @@ def time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream):
             "data": "synthetic target logits: draft logits + N(0,1) noise, fresh row after the block"}
 
 
+def time_gather(args, cfg, E, cand_id, stream):
+    """The candidate GEMM's gather alone (dsel_gather_probe: the same LDS-DMA
+    addressing, no MFMA) on the step's candidates: its HBM rate over the
+    algorithmic bytes, every gathered row once."""
+    import torch
+
+    import draft_selection_amd as ds
+
+    out = torch.empty(max(ds.lib().dsel_gather_probe_words(cfg.batch, cfg.block, cfg.d), 1), dtype=torch.int32,
+                      device=E.device)
+    for _ in range(3):
+        ds.gather_probe(E, cand_id, out=out, stream=stream)
+    torch.cuda.synchronize()
+    k = min(args.steps, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(k):
+        ds.gather_probe(E, cand_id, out=out, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / k
+    nbytes = algorithmic(cfg)["gather_bytes"]
+    gbs = nbytes / (us * 1e-6) / 1e9
+    return {"us_per_call": round(us, 2), "gathered_bytes": nbytes, "GB/s": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "what": "E[cand_id] rows into LDS through the candidate GEMM's LDS-DMA addressing, no MFMA"}
+
+
 def time_conv(args, cfg, stream):
     """The dynamic two-tap convolution unit at the workload's drafter shape
     (x [batch, block, d]): HIP-event time per call, its HBM rate over the
@@ -617,6 +645,7 @@ def main():
 
     verify = None if args.no_verify else time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream)
     conv = None if args.no_conv or cfg.d % 512 else time_conv(args, cfg, stream)
+    gather = time_gather(args, cfg, d["E"], cand_id, stream)
     lmhead = time_lmhead(args, cfg, d["E"], stream) if args.lmhead else None
 
     ms_step = wall * 1e3 / args.steps
@@ -662,6 +691,7 @@ def main():
                               "counters": mfma_from_profile(cfg.name)},
         "project_cand_gather": {"GB/s": round(alg["gather_bytes"] / (st_proj * 1e-6) / 1e9, 1),
                                 "frac": round(alg["gather_bytes"] / (st_proj * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)},
+        "gather_probe": gather,
         "project_gate": args.gate,
         "step_call": "dsel_select_path" if fused else "separate calls",
         "roofline": roof,

@@ -83,6 +83,8 @@ def _load():
             "dsel_score_pairs": ([P, P, P, P, I64, I64, P, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_walk": ([P, I64, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_select_path_workspace_bytes": ([I64, I64, I64, I32, I64, I64], SZ),
+            "dsel_gather_probe_words": ([I64, I64, I64], SZ),
+            "dsel_gather_probe": ([P, I64, I64, P, I64, I64, P, SZ, P], I32),
             "dsel_select_path": ([C.POINTER(PathArgs), C.POINTER(WalkArgs), P, SZ, P], I32),
             "dsel_verify_workspace_bytes": ([I64, I64, I64], SZ),
             "dsel_dyn_conv_workspace_bytes": ([I64, I64, I64], SZ),
@@ -355,6 +357,22 @@ def walk(S, cand_id, mode: int = GREEDY, temperature: float = 1.0, uniforms=None
     wa, res = _walk_args(cand_id, mode, temperature, uniforms, want_q, True)
     _check(_load().dsel_walk(_ptr(S), B, L, _lens(block_len, B), C.byref(wa), _stream(stream)), "dsel_walk")
     return res
+
+
+def gather_probe(E, cand_id, out=None, stream=None):
+    """Measurement aid: the candidate GEMM's gather of ``E[cand_id]`` rows into
+    LDS, alone (dsel_gather_probe).  Returns the scratch words it folds its loads
+    into (meaningless apart from keeping the loads alive)."""
+    V, d = E.shape
+    B, L = cand_id.shape[:2]
+    _need(E, "E", torch.bfloat16, (V, d))
+    _need(cand_id, "cand_id", torch.int32, (B, L, K))
+    n = int(_load().dsel_gather_probe_words(B, L, d))
+    if out is None:
+        out = torch.empty(max(n, 1), dtype=torch.int32, device=E.device)
+    _check(_load().dsel_gather_probe(_ptr(E), V, d, _ptr(cand_id), B, L, _ptr(out), out.numel(), _stream(stream)),
+           "dsel_gather_probe")
+    return out
 
 
 def device_error(stream=None) -> int:

@@ -479,6 +479,36 @@ DSEL_API dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, con
     return launch_walk(p, stream);
 }
 
+// ---- measurement aid: the candidate gather alone -----------------------------
+
+DSEL_API dsel_status dsel_gather_probe(const uint16_t *E, int64_t vocab, int64_t d, const int32_t *cand_id,
+                                       int64_t batch, int64_t block, uint32_t *out, size_t out_words,
+                                       dsel_stream_t stream) {
+    dsel_status st = check_project_common(E, vocab, d, 32, batch, block);
+    if (st != DSEL_OK || batch == 0) return st;
+    if (!cand_id || !out) return DSEL_E_ARG;
+    if (!aligned(cand_id, 4) || !aligned(out, 4)) return DSEL_E_ALIGN;
+    GatherProbeParams p;
+    p.E = E;
+    p.V = vocab;
+    p.d = (int)d;
+    p.cand = cand_id;
+    p.M = batch * block * kK;
+    const int64_t mt = (p.M + 127) / 128;
+    p.nsplit = gather_probe_nsplit(p.M, d);
+    const int64_t grid = mt * p.nsplit;
+    if (grid >= (int64_t)INT_MAX / 256 || out_words < (size_t)grid * 256) return DSEL_E_ARG;
+    p.mt = (int)mt;
+    p.out = out;
+    return launch((const void *)gather_probe_kernel, dim3((unsigned)grid), dim3(256), &p, 0, stream);
+}
+
+DSEL_API size_t dsel_gather_probe_words(int64_t batch, int64_t block, int64_t d) {
+    if (batch <= 0 || block < 1 || d < 64 || d % 64 != 0) return 0;
+    const int64_t M = batch * block * kK;
+    return (size_t)((M + 127) / 128) * (size_t)gather_probe_nsplit(M, d) * 256;
+}
+
 // ---- the whole selector ----------------------------------------------------
 
 namespace {

@@ -11,7 +11,8 @@
 //       is done), and each wave updates the running top-16 of its 16 rows:
 //       lane l takes columns 4l .. 4l+3.  While a row's list is not full
 //       (its first tile) the 16 best of the 64 lane maxima are sorted in
-//       (bitonic, ds_bpermute, then a 32-lane bitonic merge with the list);
+//       (64-lane bitonic sort on DPP and row swaps, one ds_bpermute to
+//       reverse it, then a 32-lane bitonic merge with the list);
 //       every other value is screened against the row's 16th key and the rare
 //       survivors are inserted one at a time.  The lists live in LDS
 //       between tiles; at the end they go out as 64-bit keys, one list per

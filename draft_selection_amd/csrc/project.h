@@ -586,6 +586,77 @@ __global__ __launch_bounds__(256) void project_cand_reduce_kernel(CandParams p) 
     else p.B_cur[m * r + n] = ok ? sum : 0.0f;
 }
 
+// Measurement aid: the candidate job's gather alone.  Gathered rows E[cand[m]]
+// go into a three-stage LDS ring through the same LDS-DMA addressing as
+// project_cand_kernel (128-row tiles, chunk swizzle, waits and barriers per
+// 64-deep step), with no MFMA; each thread folds its four 16-byte LDS chunks per
+// step into an XOR word and stores it, so no load can be dropped.  The K range of a
+// tile is split over workgroups so that about 512 of them run.  Algorithmic
+// bytes: every gathered row once, M d 2.
+struct GatherProbeParams {
+    const uint16_t *E;
+    int64_t V;
+    int d;
+    const int32_t *cand;
+    int64_t M;       // gathered rows
+    int mt, nsplit;  // 128-row tiles, K splits
+    uint32_t *out;   // [grid * 256]
+};
+
+__global__ __launch_bounds__(256) void gather_probe_kernel(GatherProbeParams p) {
+    constexpr int BM = 128, NW = 4, XI = BM / 8 / NW;
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[3 * BM * kBK];
+    const int ks = (int)(blockIdx.x / p.mt), mt = (int)(blockIdx.x % p.mt);
+    const int64_t m0 = (int64_t)mt * BM;
+    const int d = p.d, nk = d / kBK;
+    const int k0 = (int)((int64_t)nk * ks / p.nsplit), k1 = (int)((int64_t)nk * (ks + 1) / p.nsplit);
+    const uint32_t lane = lane_id();
+    const int wave = (int)(threadIdx.x >> 6);
+    const uint16_t *xsrc[XI];
+#pragma unroll
+    for (int u = 0; u < XI; ++u) {
+        const int row = 8 * (wave + NW * u) + (int)(lane >> 3);
+        const int64_t m = m0 + row;
+        int64_t tok = 0;
+        if (m < p.M) {
+            const int32_t t = p.cand[m];
+            if (t >= 0 && (int64_t)t < p.V) tok = t;
+        }
+        xsrc[u] = p.E + tok * d + (((lane & 7) ^ ((row >> 1) & 7)) << 3);
+    }
+    auto issue = [&](int k, int stage) {
+#pragma unroll
+        for (int u = 0; u < XI; ++u)
+            lds_dma16(xsrc[u] + (int64_t)k * kBK, Xs + stage * BM * kBK + (8 * (wave + NW * u)) * kBK);
+    };
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    if (k1 > k0) issue(k0, 0);
+    if (k1 > k0 + 1) issue(k0 + 1, 1);
+    for (int k = k0; k < k1; ++k) {
+        const int st = (k - k0) % 3;
+        if (k + 2 < k1) {
+            issue(k + 2, (k - k0 + 2) % 3);
+            wait_vmcnt<2 * XI>();  // step k landed; k+1 and k+2 may still fly
+        } else {
+            wait_vmcnt<0>();
+        }
+        wg_barrier();
+#pragma unroll
+        for (int j = 0; j < BM * kBK / (256 * 8); ++j)
+            acc ^= *(const u32x4 *)(Xs + st * BM * kBK + (threadIdx.x + 256 * j) * 8);
+        wg_barrier();  // the stage is refilled two steps later
+    }
+    wait_vmcnt<0>();
+    p.out[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
+inline int gather_probe_nsplit(int64_t M, int64_t d) {
+    const int64_t mt = (M + 127) / 128, nk = d / kBK;
+    int64_t s = (512 + mt - 1) / mt;
+    if (s > nk / 4) s = nk / 4;
+    return (int)(s < 1 ? 1 : s);
+}
+
 // K splits of the candidate job: only when its tiles cannot fill the chip,
 // keeping at least DSEL_CAND_MIN_STEPS K steps per split.
 #ifndef DSEL_CAND_MIN_STEPS

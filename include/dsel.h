@@ -251,6 +251,19 @@ size_t dsel_select_path_workspace_bytes(int64_t batch, int64_t block, int64_t vo
 dsel_status dsel_select_path(const dsel_path_args *args, const dsel_walk_args *walk, void *workspace,
                              size_t workspace_bytes, dsel_stream_t stream);
 
+/* gather_probe -- a measurement aid, not a step of the path: the gather of
+ * dsel_project_cand alone.  Rows E[cand_id[m]] (m over batch*block*16) are
+ * moved into LDS with the same LDS-DMA addressing as the candidate GEMM, with
+ * no arithmetic, so the gather's HBM rate can be measured apart from the MFMAs
+ * it feeds.  Each thread folds what it sees into one word of `out` (so no load
+ * can be dropped); the words mean nothing else.
+ *   out        device array of at least dsel_gather_probe_words() uint32.
+ * Requirements: as dsel_project_cand (d % 64 == 0). */
+size_t dsel_gather_probe_words(int64_t batch, int64_t block, int64_t d);
+dsel_status dsel_gather_probe(const uint16_t *E, int64_t vocab, int64_t d, const int32_t *cand_id,
+                              int64_t batch, int64_t block, uint32_t *out, size_t out_words,
+                              dsel_stream_t stream);
+
 /* verify -- lossless verification of the drafted blocks against the target
  * model, the step after the walk ([P1] Method, last paragraph, and Setup:
  * sampling stays lossless through rejection sampling; [P3] "One pass to draft,
