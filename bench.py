@@ -193,28 +193,84 @@ def calibrate_copy():
     print("copied 3 x 1 GiB", flush=True)
 
 
-def cpu_baseline(cfg, inp, budget_s=15.0):
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_stages(oracle, sub, mode, T, acc):
+    """One oracle pass over `sub`, stage by stage, adding seconds to `acc`."""
+    t0 = time.perf_counter()
+    cand_id, cand_u = oracle.select_topk(sub["logits"])
+    t1 = time.perf_counter()
+    A, Bm, G = oracle.project(sub["E"], sub["W_A"], sub["W_B"], sub["W_H"], sub["h"], cand_id, sub["verified"])
+    t2 = time.perf_counter()
+    S = oracle.score_pairs(cand_u, A, Bm, G)
+    t3 = time.perf_counter()
+    oracle.walk(S, cand_id, mode, sub.get("uniforms"), T)
+    t4 = time.perf_counter()
+    for k, dt in zip(("select_topk", "project", "score_pairs", "walk"), (t1 - t0, t2 - t1, t3 - t2, t4 - t3)):
+        acc[k] = acc.get(k, 0.0) + dt
+    return t4 - t0
+
+
+def _omp_threads(n=None):
+    """The OpenMP team size of the oracle's runtime (libgomp, shared by the
+    process), set to `n` if given; returns the previous maximum, or None if
+    libgomp is not there."""
+    import ctypes
+
+    try:
+        gomp = ctypes.CDLL("libgomp.so.1")
+    except OSError:
+        return None
+    prev = gomp.omp_get_max_threads()
+    if n is not None:
+        gomp.omp_set_num_threads(int(n))
+    return prev
+
+
+def cpu_baseline(cfg, inp, budget_s=15.0, single_core_s=3.0):
     """The oracle as it stands, on the host cores, over as many blocks as fit in
-    about `budget_s` seconds (at least one)."""
+    about `budget_s` seconds (at least one), stage by stage; for the smaller
+    workloads also a few blocks on one core."""
     import oracle
     import synth
 
     oracle.build(force=False)
     mode = 1 if cfg.walk == "sampled" else 0
-    done, t_total = 0, 0.0
+    done, t_total, stages = 0, 0.0, {}
     chunk = 1
     while done < cfg.batch and t_total < budget_s:
         n = min(chunk, cfg.batch - done)
         sub = synth.sub_blocks(inp, np.arange(done, done + n))
-        t0 = time.perf_counter()
-        oracle.run(sub, mode, cfg.temperature)
-        t_total += time.perf_counter() - t0
+        t_total += _oracle_stages(oracle, sub, mode, cfg.temperature, stages)
         done += n
         chunk = min(2 * chunk, 16)
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    prev = _omp_threads(1) if cfg.d <= 2560 else None
+    single = None
+    if prev is not None:
+        try:
+            n1, t1 = 0, 0.0
+            while n1 < cfg.batch and t1 < single_core_s:
+                t1 += _oracle_stages(oracle, synth.sub_blocks(inp, np.arange(n1, n1 + 1)), mode, cfg.temperature, {})
+                n1 += 1
+            single = {"value": n1 / t1, "unit": "blocks/s", "blocks": n1, "s": round(t1, 2)}
+        finally:
+            _omp_threads(prev)
+    cores = _omp_threads() or int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": done / t_total, "unit": "blocks/s", "cores": cores, "kind": "oracle",
             "sample": f"{done} of {cfg.batch} blocks of {cfg.name}, whole selector "
-                      f"(top-16, fp64 projections, scores, walk), {t_total:.1f} s"}
+                      f"(top-16, fp64 projections, scores, walk), {t_total:.1f} s",
+            "ms_per_block": {k: round(v * 1e3 / done, 3) for k, v in stages.items()},
+            "single_core": single, "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "build": "gcc -O2 -fopenmp, no fast-math; perf_counter around each stage call"}
 
 
 def time_verify(args, cfg, mode, lib, P, dt, cand_id, wres, stream):
@@ -409,6 +465,18 @@ def time_lmhead(args, cfg, E, stream):
             "shape": f"h [{R}, {dd}] x E [{V}, {dd}]^T", "data": "synthetic h ~ N(0,1), E ~ N(0,0.02) (tied embeddings)"}
 
 
+def stage_pcts(evs):
+    """p10 / p50 / p90 microseconds of every stage and of the step."""
+    names = ("project_gate", "select_topk", "project_cand", "score_pairs_walk")
+    out = {}
+    for i, n in enumerate(names):
+        v = np.array([e[i].elapsed_time(e[i + 1]) for e in evs]) * 1e3
+        out[n] = [round(float(x), 2) for x in np.percentile(v, (10, 50, 90))]
+    v = np.array([e[0].elapsed_time(e[4]) for e in evs]) * 1e3
+    out["step"] = [round(float(x), 2) for x in np.percentile(v, (10, 50, 90))]
+    return out
+
+
 def stage_means(evs):
     """Mean microseconds between consecutive stage events over the steps."""
     names = ("project_gate", "select_topk", "project_cand", "score_pairs_walk")
@@ -600,7 +668,7 @@ def main():
 
     # (3) cold caches: before every step a 1 GiB write evicts L2 and the
     # Infinity Cache; the stage events exclude that write
-    cold = None
+    cold = cold_pct = None
     if not args.no_cold:
         flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
@@ -610,6 +678,7 @@ def main():
         torch.cuda.synchronize()
         del flush
         cold = stage_means(cevs)
+        cold_pct = stage_pcts(cevs)
 
     # (4) a ragged batch: the same step with each block at its own length
     # (the 5 / 8 / 16 mix), one HIP graph replayed K times
@@ -686,6 +755,8 @@ def main():
                   "HIP events on the launch stream (stages_us_cold: after a 1 GiB cache-evicting write)",
         "stages_us": warm,
         "stages_us_cold": cold,
+        "stages_us_p10_p50_p90": stage_pcts(evs),
+        "stages_us_cold_p10_p50_p90": cold_pct,
         "select_topk_hbm": {"GB/s": round(topk_gbs, 1), "frac": round(topk_gbs / HBM_PEAK_GBS, 4)},
         "project_cand_mfma": {"TFLOP/s": round(proj_tfs, 2), "frac": round(proj_tfs / BF16_PEAK_TFLOPS, 4),
                               "counters": mfma_from_profile(cfg.name)},
