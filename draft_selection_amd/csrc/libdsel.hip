@@ -316,7 +316,7 @@ dsel_status plan_cand(const uint16_t *E, int64_t vocab, int64_t d, const uint16_
     p.A_prev = A_prev;
     p.B_cur = B_cur;
     constexpr int BM = 128;
-    c->BN = r % 256 == 0 ? 256 : r % 128 == 0 ? 128 : r % 64 == 0 ? 64 : 32;
+    c->BN = cand_bn(batch, block, r);
     p.nside = (int)(r / c->BN);
     p.mt = (int)((p.M + BM - 1) / BM);
     p.mt_pad = (p.mt + 7) / 8 * 8;

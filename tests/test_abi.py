@@ -158,6 +158,7 @@ def test_select_path_validation(lib):
     assert lib.dsel_select_path(None, C.byref(w), P(f), ws, None) == -1
     assert call(args(), walk=None) == -1
     assert call(args(), wsb=0) == -4 and call(args(), wsp=None) == -4
+    assert call(args(), wsp=f + 8) == -3
     assert call(args(dt=5)) == -2
     assert call(args(d=96)) == -1 and call(args(r=48)) == -1 and call(args(block=33), wsb=1 << 40) == -1
     assert call(args(S=None)) == -1 and call(args(G=None)) == -1
