@@ -477,6 +477,12 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
     const int n0 = (ct % p.nside) * BN;
 #endif
     if (mt >= p.mt) return;
+    // Declaring an AGPR clobber tells the compiler the kernel uses AGPRs, so it
+    // keeps the MFMA accumulators there (the AGPR form of the instruction)
+    // instead of in VGPRs: the LDS fragment reads then land in a register file
+    // the MFMAs do not read and write every cycle (measured 1-3% faster on the
+    // 80- and 96-step K loops, same bits).
+    asm volatile("" ::: "a0");
     const int64_t m0 = (int64_t)mt * BM;
     const int tid = threadIdx.x;
     const int d = p.d, r = p.r;
