@@ -525,8 +525,8 @@ def main():
         calibrate_copy()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the selector is block-parallel and this build runs on "
-              "a single MI355X; run it with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only (the selector shards by draft block with no exchange, "
+              "so one GPU's share is the whole measurement); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
