@@ -90,6 +90,7 @@ def _rand_inputs(seed, B, L, V, d, r, e_std=1.0):
     (70, 9, 9000, 640, 224),  # 79 row tiles (not a multiple of the 8 XCDs), 7 column tiles
     (1, 16, 20000, 2560, 256),  # one block: both GEMMs split along K (10 ways)
     (2, 8, 5000, 1024, 128),  # candidate GEMM split 4 ways
+    (24, 16, 6000, 192, 256),  # 48 row tiles: 64-wide candidate tiles at r = 256 (9, 7: 32-wide; 40, 16: 128-wide)
 ])
 def test_project_matches_oracle(ora, dev, B, L, V, d, r):
     inp, cand = _rand_inputs(B * 1000 + L, B, L, V, d, r)
