@@ -24,6 +24,8 @@ block, int32 on the GPU) and ``stream``.
 from __future__ import annotations
 
 import ctypes as C
+import functools
+import inspect
 import os
 from typing import Optional
 
@@ -118,6 +120,24 @@ def _stream(stream=None):
     return C.c_void_p(s.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run ``fn`` with its ``stream`` argument (when given) as the current
+    stream, so that the outputs and workspaces it allocates belong to the
+    stream its kernels are launched on (the caching allocator then never hands
+    them to other work while those kernels may still use them)."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrap(*args, **kwargs):
+        s = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if s is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(s):
+            return fn(*args, **kwargs)
+
+    return wrap
+
+
 def _check(status: int, what: str):
     if status != 0:
         raise DselError(status, what)
@@ -173,6 +193,7 @@ def _logits_geometry(logits: torch.Tensor, vocab: Optional[int]):
     return B, L, ld, V
 
 
+@_on_stream
 def select_topk(logits: torch.Tensor, vocab: Optional[int] = None, out=None, workspace=None,
                 stream=None, block_len=None):
     """Top-16 of every draft position.  ``logits [batch, block, ld]`` fp32 or bf16
@@ -201,6 +222,7 @@ def select_topk(logits: torch.Tensor, vocab: Optional[int] = None, out=None, wor
     return cand_id, cand_u
 
 
+@_on_stream
 def project(E, W_A, W_B, W_H, h, cand_id, verified, out=None, stream=None, block_len=None):
     """``A_prev [B,L,16,r]``, ``B_cur [B,L,16,r]``, ``G [B,L,r]`` (fp32) from bf16
     ``E [V,d]``, ``W_* [r,d]``, ``h [B,L,d]``, int32 ``cand_id``, ``verified [B]``."""
@@ -219,6 +241,9 @@ def project(E, W_A, W_B, W_H, h, cand_id, verified, out=None, stream=None, block
         G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
     else:
         A_prev, B_cur, G = out
+        _need(A_prev, "A_prev", torch.float32, (B, L, K, r))
+        _need(B_cur, "B_cur", torch.float32, (B, L, K, r))
+        _need(G, "G", torch.float32, (B, L, r))
     ws = _project_workspace(B, L, d, r, dev)
     wsb = 0 if ws is None else ws.numel()
     st = _load().dsel_project(_ptr(E), V, d, _ptr(W_A), _ptr(W_B), _ptr(W_H), r, _ptr(h),
@@ -237,6 +262,7 @@ def _project_workspace(B, L, d, r, dev):
     return torch.empty(n, dtype=torch.uint8, device=dev) if n else None
 
 
+@_on_stream
 def project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=None, stream=None, block_len=None):
     """G and the position-0 predecessor rows of A_prev (needs no candidates)."""
     V, d = E.shape
@@ -256,6 +282,7 @@ def project_gate(E, W_A, W_H, h, verified, A_prev, G, workspace=None, stream=Non
     _check(st, "dsel_project_gate")
 
 
+@_on_stream
 def project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=None, block_len=None):
     """project_gate with one workgroup per output tile and no workspace, for
     running beside select_topk on another stream."""
@@ -272,6 +299,7 @@ def project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=None, block
     _check(st, "dsel_project_gate_overlap")
 
 
+@_on_stream
 def project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=None, stream=None, block_len=None):
     """B_cur and the predecessor rows of A_prev for positions >= 1."""
     V, d = E.shape
@@ -322,6 +350,7 @@ def _walk_args(cand_id, mode, temperature, uniforms, want_q, want_s):
     return a, res
 
 
+@_on_stream
 def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Optional[int] = None,
                 cand_id=None, temperature: float = 1.0, uniforms=None, want_q: bool = False,
                 stream=None, block_len=None):
@@ -348,6 +377,7 @@ def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Option
     return res
 
 
+@_on_stream
 def walk(S, cand_id, mode: int = GREEDY, temperature: float = 1.0, uniforms=None,
          want_q: bool = False, stream=None, block_len=None):
     """The walk alone over ``S [B,L,16,16]`` fp32."""
@@ -359,6 +389,7 @@ def walk(S, cand_id, mode: int = GREEDY, temperature: float = 1.0, uniforms=None
     return res
 
 
+@_on_stream
 def gather_probe(E, cand_id, out=None, stream=None):
     """Measurement aid: the candidate GEMM's gather of ``E[cand_id]`` rows into
     LDS, alone (dsel_gather_probe).  Returns the scratch words it folds its loads
@@ -382,6 +413,7 @@ def device_error(stream=None) -> int:
     return int(v.value)
 
 
+@_on_stream
 def lmhead_topk(h, W, stream=None):
     """The LM head and its top-16 in one pass (logits never written):
     ``h [..., d]`` and ``W [vocab, d]`` bf16; returns ``cand_id [..., 16]``
@@ -405,6 +437,7 @@ def dyn_conv_workspace_bytes(batch: int, block: int, d: int) -> int:
     return int(_load().dsel_dyn_conv_workspace_bytes(batch, block, d))
 
 
+@_on_stream
 def dyn_conv(x, x_prev, base, W_c, y=None, workspace=None, stream=None, block_len=None):
     """Dynamic two-tap short convolution of the drafter over each block's
     positions: ``x [B, L, d]``, ``x_prev [B, d]``, ``base [2, d]``,
@@ -432,6 +465,7 @@ def verify_workspace_bytes(batch: int, block: int, vocab: int) -> int:
     return int(_load().dsel_verify_workspace_bytes(batch, block, vocab))
 
 
+@_on_stream
 def verify(target_logits, cand_id, path_slot, q=None, mode: int = GREEDY, temperature: float = 1.0,
            u_acc=None, u_res=None, vocab: Optional[int] = None, workspace=None, stream=None,
            block_len=None):
@@ -473,35 +507,42 @@ def select_path_workspace_bytes(batch: int, block: int, vocab: int, dtype: torch
     return int(_load().dsel_select_path_workspace_bytes(batch, block, vocab, dt, d, r))
 
 
+@_on_stream
 def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
                 temperature: float = 1.0, uniforms=None, vocab: Optional[int] = None,
-                want_S: bool = False, want_q: bool = False, overlap: bool = False, stream=None,
-                block_len=None, workspace=None):
+                want_S: bool = False, want_q: bool = False, want_AB: bool = False, overlap: bool = False,
+                stream=None, block_len=None, workspace=None):
     """The whole selector: top-16, projections, pair scores and the walk.
 
-    By default one call of dsel_select_path (the gate's reduction rides in the
-    top-16 launch).  With ``overlap`` the steps are separate calls and the gate
-    GEMM (which needs no candidates) runs on a side stream, one workgroup per
-    output tile (dsel_project_gate_overlap), beside the top-16."""
+    By default one call of dsel_select_path.  The intermediates are returned
+    only when asked for: ``S`` with ``want_S``, ``A_prev``, ``B_cur`` and ``G``
+    with ``want_AB`` (not asking lets the library keep the projections on
+    chip).  With ``overlap`` the steps are separate calls and the gate GEMM
+    (which needs no candidates) runs on a side stream, one workgroup per output
+    tile (dsel_project_gate_overlap), beside the top-16."""
     main = torch.cuda.current_stream() if stream is None else stream
     B, L = h.shape[:2]
     r = W_A.shape[0]
     dev = E.device
-    A_prev = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
-    B_cur = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
-    G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
     if overlap:
+        A_prev = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+        B_cur = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+        G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
         ws = _project_workspace(B, L, E.shape[1], r, dev)  # one workspace serves both halves
         side = side_stream(dev)
         side.wait_stream(main)
         project_gate_overlap(E, W_A, W_H, h, verified, A_prev, G, stream=side, block_len=block_len)
+        G.record_stream(side)
+        A_prev.record_stream(side)
         cand_id, cand_u = select_topk(logits, vocab, stream=main, block_len=block_len)
         main.wait_stream(side)
         project_cand(E, W_A, W_B, cand_id, A_prev, B_cur, workspace=ws, stream=main, block_len=block_len)
         res = score_pairs(cand_u, A_prev, B_cur, G, want_S=want_S, walk_mode=mode, cand_id=cand_id,
                           temperature=temperature, uniforms=uniforms, want_q=want_q, stream=main,
                           block_len=block_len)
-        res.update(cand_id=cand_id, cand_u=cand_u, A_prev=A_prev, B_cur=B_cur, G=G)
+        res.update(cand_id=cand_id, cand_u=cand_u)
+        if want_AB:
+            res.update(A_prev=A_prev, B_cur=B_cur, G=G)
         return res
     Bl, Ll, ld, V = _logits_geometry(logits, vocab)
     if (Bl, Ll) != (B, L):
@@ -515,21 +556,32 @@ def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
     _need(verified, "verified", torch.int32, (B,))
     cand_id = torch.empty((B, L, K), dtype=torch.int32, device=dev)
     cand_u = torch.empty((B, L, K), dtype=torch.float32, device=dev)
-    S = torch.empty((B, L, K, K), dtype=torch.float32, device=dev)
+    S = torch.empty((B, L, K, K), dtype=torch.float32, device=dev) if want_S else None
+    if want_AB:
+        A_prev = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+        B_cur = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+        G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
+    else:
+        A_prev = B_cur = G = None
     wa, res = _walk_args(cand_id, mode, temperature, uniforms, want_q, True)
     dt = BF16 if logits.dtype == torch.bfloat16 else F32
+    need = select_path_workspace_bytes(B, L, V, logits.dtype, d, r)
     if workspace is None:
-        workspace = torch.empty(max(select_path_workspace_bytes(B, L, V, logits.dtype, d, r), 16),
-                                dtype=torch.uint8, device=dev)
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     wsb = workspace.numel() * workspace.element_size()
+
+    def addr(t):
+        return None if t is None else t.data_ptr()
+
     pa = PathArgs(logits.data_ptr(), dt, V, ld, E.data_ptr(), d, W_A.data_ptr(), W_B.data_ptr(), W_H.data_ptr(),
                   r, h.data_ptr(), verified.data_ptr(), B, L,
                   _lens(block_len, B).value if block_len is not None else None,
-                  cand_id.data_ptr(), cand_u.data_ptr(), A_prev.data_ptr(), B_cur.data_ptr(), G.data_ptr(),
-                  S.data_ptr())
+                  cand_id.data_ptr(), cand_u.data_ptr(), addr(A_prev), addr(B_cur), addr(G), addr(S))
     _check(_load().dsel_select_path(C.byref(pa), C.byref(wa), _ptr(workspace), wsb, _stream(main)),
            "dsel_select_path")
     if want_S:
         res["S"] = S
-    res.update(cand_id=cand_id, cand_u=cand_u, A_prev=A_prev, B_cur=B_cur, G=G)
+    res.update(cand_id=cand_id, cand_u=cand_u)
+    if want_AB:
+        res.update(A_prev=A_prev, B_cur=B_cur, G=G)
     return res

@@ -9,6 +9,7 @@
 #include "dsel.h"
 #include "common.h"
 #include "conv.h"
+#include "fused.h"
 #include "lmhead.h"
 #include "pairwalk.h"
 #include "path.h"
@@ -213,6 +214,9 @@ dsel_status plan_gate(const uint16_t *E, int64_t vocab, int64_t d, const uint16_
     p.len = block_len;
     p.A_prev = A_prev;
     p.G = G;
+    p.A_ver = A_prev;
+    p.ver_stride = block * kK * r;
+    p.ver_zero = true;
     p.part = (float *)workspace;
     g->BN = gate_bn(batch, block, r);
     p.nside = (int)(r / g->BN);
@@ -513,47 +517,174 @@ DSEL_API size_t dsel_gather_probe_words(int64_t batch, int64_t block, int64_t d)
 
 namespace {
 
-// Workspace of dsel_select_path: the top-16's partial lists, then (256-byte
-// aligned) the projections' workspace.
-size_t path_topk_bytes(int64_t rows, int64_t vocab, dsel_dtype dt) {
-    return (dsel_topk_workspace_bytes(rows, vocab, dt) + 255) / 256 * 256;
+inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of dsel_select_path, in this order (each part 256-byte aligned):
+// the top-16's partial lists; the projections' split-K partials; G; then, on
+// the fused route, A(verified) [B][r] and the pair partials, else A_prev,
+// B_cur [B, L, 16, r] and S [B, L, 16, 16].  The parts for outputs the caller
+// supplies are reserved but unused.
+struct PathLayout {
+    size_t topk = 0, proj = 0, g = 0, aver = 0, part = 0, a = 0, b = 0, s = 0, total = 0;
+    bool fused = false;
+};
+
+bool path_layout(int64_t batch, int64_t block, int64_t vocab, dsel_dtype dt, int64_t d, int64_t r,
+                 PathLayout *l) {
+    if (batch <= 0 || block < 1 || block > DSEL_MAX_BLOCK || batch > (int64_t)INT_MAX / block) return false;
+    if (d < 64 || d % 64 != 0 || r < 32 || r > DSEL_MAX_RANK || r % 32 != 0) return false;
+    const int64_t pos = batch * block;
+    size_t off = align256(dsel_topk_workspace_bytes(pos, vocab, dt));
+    l->topk = 0;
+    l->proj = off;
+    off += align256(dsel_project_workspace_bytes(batch, block, d, r));
+    l->g = off;
+    off += align256((size_t)pos * r * sizeof(float));
+    l->fused = use_fused(batch, block, r);
+    if (l->fused) {
+        l->aver = off;
+        off += align256((size_t)batch * r * sizeof(float));
+        l->part = off;
+        off += align256(fused_partial_bytes(batch, block, r));
+    } else {
+        const size_t ab = align256((size_t)pos * kK * r * sizeof(float));
+        l->a = off;
+        off += ab;
+        l->b = off;
+        off += ab;
+        l->s = off;
+        off += align256((size_t)pos * kK * kK * sizeof(float));
+    }
+    l->total = off;
+    return true;
+}
+
+struct FusedPlan {
+    FusedParams p;
+    int CW = 64;
+};
+
+dsel_status plan_fused(const dsel_path_args *a, const float *G, const float *A_ver, int64_t ver_stride,
+                       float *P, FusedPlan *f) {
+    dsel_status st = check_project_common(a->E, a->vocab, a->d, a->r, a->batch, a->block);
+    if (st != DSEL_OK) return st;
+    if (!a->W_A || !a->W_B || !a->cand_id) return DSEL_E_ARG;
+    if (!aligned(a->W_A, 16) || !aligned(a->W_B, 16) || !aligned(a->cand_id, 4) || !aligned(a->A_prev, 16) ||
+        !aligned(a->B_cur, 16) || !aligned(a->block_len, 4))
+        return DSEL_E_ALIGN;
+    FusedParams &p = f->p;
+    p.E = a->E;
+    p.V = a->vocab;
+    p.d = (int)a->d;
+    p.r = (int)a->r;
+    p.WA = a->W_A;
+    p.WB = a->W_B;
+    p.cand = a->cand_id;
+    p.G = G;
+    p.A_ver = A_ver;
+    p.ver_stride = ver_stride;
+    p.B = (int)a->batch;
+    p.L = (int)a->block;
+    p.len = a->block_len;
+    p.nb = fused_blocks_per_tile(a->block);
+    p.ntile = (int)fused_tiles(a->batch, a->block);
+    f->CW = pair_group_width((int)a->r);
+    p.nq = (int)(a->r / f->CW);
+    p.P = P;
+    p.A_prev = a->A_prev;
+    p.B_cur = a->B_cur;
+    if (fused_grid(a->batch, a->block, a->r) >= (int64_t)INT_MAX) return DSEL_E_ARG;
+    return DSEL_OK;
+}
+
+dsel_status launch_fused(const FusedPlan &f, dsel_stream_t stream) {
+    FusedParams p = f.p;
+    const int64_t grid = fused_grid(p.B, p.L, p.r);
+    const void *k = f.CW == 64 ? (const void *)project_pair_kernel<64> : (const void *)project_pair_kernel<32>;
+    return launch(k, dim3((unsigned)grid), dim3(f.CW == 64 ? FusedTile<64>::NT : FusedTile<32>::NT), &p, 0, stream);
 }
 
 }  // namespace
 
 DSEL_API size_t dsel_select_path_workspace_bytes(int64_t batch, int64_t block, int64_t vocab, dsel_dtype dt,
                                                  int64_t d, int64_t r) {
-    if (batch <= 0 || block < 1 || batch > (int64_t)INT_MAX / block) return 0;
-    return path_topk_bytes(batch * block, vocab, dt) + dsel_project_workspace_bytes(batch, block, d, r);
+    PathLayout l;
+    return path_layout(batch, block, vocab, dt, d, r, &l) ? l.total : 0;
 }
 
 DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_args *walk, void *workspace,
                                       size_t workspace_bytes, dsel_stream_t stream) {
     if (!a || !walk) return DSEL_E_ARG;
-    if (a->batch < 0 || a->block < 1 || a->batch > (int64_t)INT_MAX / a->block) return DSEL_E_ARG;
-    const size_t tb = a->batch ? path_topk_bytes(a->batch * a->block, a->vocab, a->dt) : 0;
-    if (tb > workspace_bytes) return DSEL_E_WORKSPACE;
-    void *pws = workspace ? (char *)workspace + tb : nullptr;
-    const size_t pwsb = workspace_bytes - tb;
+    if (a->batch < 0 || a->block < 1 || a->block > DSEL_MAX_BLOCK || a->batch > (int64_t)INT_MAX / a->block)
+        return DSEL_E_ARG;
+    if ((a->A_prev == nullptr) != (a->B_cur == nullptr)) return DSEL_E_ARG;  // both or neither
+    PathLayout l;
+    if (a->batch > 0) {
+        if (!path_layout(a->batch, a->block, a->vocab, a->dt, a->d, a->r, &l)) return DSEL_E_ARG;
+        if (!workspace || workspace_bytes < l.total) return DSEL_E_WORKSPACE;
+        if (!aligned(workspace, 256)) return DSEL_E_ALIGN;
+    }
+    char *ws = (char *)workspace;
+    float *G = a->G ? a->G : (float *)(ws + l.g);
     // every step is validated before anything is launched
     TopkPlan t;
     GatePlan g;
+    dsel_status st = plan_topk(a->logits, a->dt, a->batch, a->block, a->block_len, a->vocab, a->ld, a->cand_id,
+                               a->cand_u, ws, l.proj, &t);
+    if (st != DSEL_OK || a->batch == 0) return st;
+    if (l.fused) {
+        // gate GEMM; top-16 with the gate's reduction beside it; the fused
+        // candidate projection + pair partials; the walk, which also forms S
+        const bool ab = a->A_prev != nullptr;
+        float *A_ver = ab ? a->A_prev : (float *)(ws + l.aver);
+        st = plan_gate(a->E, a->vocab, a->d, a->W_A, a->W_H, a->r, a->h, a->verified, a->batch, a->block,
+                       a->block_len, ab ? a->A_prev : A_ver, G, ws + l.proj, l.g - l.proj, true, &g);
+        if (st != DSEL_OK) return st;
+        if (!ab) {  // A(verified) to the compact buffer
+            g.p.A_ver = A_ver;
+            g.p.ver_stride = a->r;
+            g.p.ver_zero = false;
+        }
+        FusedPlan f;
+        st = plan_fused(a, G, A_ver, ab ? a->block * kK * a->r : a->r, (float *)(ws + l.part), &f);
+        if (st != DSEL_OK) return st;
+        PairPlan q;
+        if (!a->cand_u || !aligned(a->S, 4)) return !a->cand_u ? DSEL_E_ARG : DSEL_E_ALIGN;
+        st = check_walk(walk, &q.p.w);
+        if (st != DSEL_OK) return st;
+        q.p.cand_u = a->cand_u;
+        q.p.P = f.p.P;
+        q.p.nq = f.p.nq;
+        q.p.B = (int)a->batch;
+        q.p.L = (int)a->block;
+        q.p.len = a->block_len;
+        q.p.r = (int)a->r;
+        q.p.S = a->S;
+        st = launch_gate_gemm(g, stream);
+        if (st == DSEL_OK) {
+            const int64_t ge = gate_reduce_elems(g);
+            st = launch_topk(t, ge ? &g.p : nullptr, ge, stream);
+        }
+        if (st == DSEL_OK) st = launch_fused(f, stream);
+        if (st == DSEL_OK) st = launch_walk(q.p, stream);
+        return st;
+    }
+    // the separate kernels: gate GEMM; top-16 with the gate's reduction beside
+    // it; candidate GEMM; pair scores and the walk (intermediates the caller
+    // does not want live in the workspace)
+    float *A_prev = a->A_prev ? a->A_prev : (float *)(ws + l.a);
+    float *B_cur = a->B_cur ? a->B_cur : (float *)(ws + l.b);
+    float *S = a->S ? a->S : (float *)(ws + l.s);
     CandPlan c;
     PairPlan q;
-    dsel_status st = plan_topk(a->logits, a->dt, a->batch, a->block, a->block_len, a->vocab, a->ld, a->cand_id,
-                               a->cand_u, workspace, workspace_bytes, &t);
-    if (st == DSEL_OK)
-        st = plan_gate(a->E, a->vocab, a->d, a->W_A, a->W_H, a->r, a->h, a->verified, a->batch, a->block,
-                       a->block_len, a->A_prev, a->G, pws, pwsb, true, &g);
+    st = plan_gate(a->E, a->vocab, a->d, a->W_A, a->W_H, a->r, a->h, a->verified, a->batch, a->block,
+                   a->block_len, A_prev, G, ws + l.proj, l.g - l.proj, true, &g);
     if (st == DSEL_OK)
         st = plan_cand(a->E, a->vocab, a->d, a->W_A, a->W_B, a->r, a->cand_id, a->batch, a->block, a->block_len,
-                       a->A_prev, a->B_cur, pws, pwsb, &c);
+                       A_prev, B_cur, ws + l.proj, l.g - l.proj, &c);
     if (st == DSEL_OK)
-        st = plan_pairs(a->cand_u, a->A_prev, a->B_cur, a->G, a->batch, a->block, a->block_len, a->r, a->S, walk,
-                        &q);
-    if (st != DSEL_OK || a->batch == 0) return st;
-    // gate GEMM; top-16 with the gate's reduction beside it; candidate GEMM;
-    // pair scores and the walk
+        st = plan_pairs(a->cand_u, A_prev, B_cur, G, a->batch, a->block, a->block_len, a->r, S, walk, &q);
+    if (st != DSEL_OK) return st;
     st = launch_gate_gemm(g, stream);
     if (st == DSEL_OK) {
         const int64_t ge = gate_reduce_elems(g);

@@ -38,6 +38,8 @@ struct WalkParams {
 struct PairParams {
     const float *cand_u, *A_prev, *B_cur, *G;
     const float *S_in;  // stand-alone walk: scores to walk
+    const float *P;     // or the group partials of the pair term [B * L][nq][16][16] (S_in unused)
+    int nq;
     int B, L, r;
     const int32_t *len;  // ragged batch: valid positions per block (nullptr: all L)
     float *S;  // scores out
@@ -133,18 +135,24 @@ __device__ __forceinline__ void decide_position(const float (&s)[4], int t, cons
     }
 }
 
-// Step 1 for one position: the score table in registers (MFMA layout).
-// One position (b, t) per workgroup of 4 waves.  The rank is cut into 16-wide
-// slices, slice s going to wave s % 4; each wave issues every load of its
-// slices up front (so the whole grid keeps enough bytes in flight for HBM) and
-// accumulates its partial 16 x 16 table with v_mfma_f32_16x16x4_f32: lane
-// (fr, fg) supplies row fr and column 4 fg + c of a slice's c-th MFMA (the
-// order of the sum over the rank is a permutation).  The four partial tables
-// are summed through LDS in wave order.
+// Columns of the rank per group of the pair sum: 64 when r is a multiple of 64
+// and at least 128, else 32.  The pair term of a position is summed group by
+// group (each group one chain of MFMAs over its columns in order), then the
+// groups in order; project_pair_kernel produces the same group partials.
+__host__ __device__ constexpr int pair_cw(int r) { return (r % 64 == 0 && r >= 128) ? 64 : 32; }
+
+// One position (b, t) per workgroup of 4 waves.  Group g of the rank (columns
+// g CW .. g CW + CW - 1) goes to wave g % 4; each wave issues every load of
+// its groups up front (so the whole grid keeps enough bytes in flight for HBM)
+// and accumulates each group's 16 x 16 table with v_mfma_f32_16x16x4_f32: lane
+// (fr, fg) supplies row fr and column 16 s + 4 fg + c of slice s's c-th MFMA
+// (the order of the sum over a group is a permutation of its columns).  The
+// group tables are summed through LDS in group order.
 template <int R>
 __global__ __launch_bounds__(256) void pair_kernel(PairParams p) {
-    constexpr int NS = R / 16;              // 16-wide slices of the rank (R % 32 == 0)
-    constexpr int SPW = (NS + 3) / 4;       // slices per wave (the last waves may get fewer)
+    constexpr int CW = pair_cw(R), NQ = R / CW;  // groups of the rank
+    constexpr int GPW = (NQ + 3) / 4;            // groups per wave (the last waves may get fewer)
+    constexpr int SPG = CW / 16;                 // 16-wide slices per group
     const int64_t bt = blockIdx.x;
     if (!position_live(p.len, blockIdx.x, p.L)) return;  // padding position (ragged batches)
     const int t = (int)(blockIdx.x % (uint32_t)p.L);
@@ -154,36 +162,40 @@ __global__ __launch_bounds__(256) void pair_kernel(PairParams p) {
     const float *Ap = p.A_prev + (bt * kK + fr) * R + 4 * fg;
     const float *Bp = p.B_cur + (bt * kK + fr) * R + 4 * fg;
     const float *Gp = p.G + bt * R + 4 * fg;
-    float4 a[SPW], g[SPW], b[SPW];
+    float4 a[GPW][SPG], g[GPW][SPG], b[GPW][SPG];
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-        const int sl = wave + 4 * q;
-        const int c = (sl < NS ? sl : 0) * 16;  // a wave past the last slice loads slice 0, unused
-        a[q] = *(const float4 *)(Ap + c);
-        g[q] = *(const float4 *)(Gp + c);
-        b[q] = *(const float4 *)(Bp + c);
-    }
-    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < GPW; ++k) {
+        const int grp = wave + 4 * k;
+        const int c0 = (grp < NQ ? grp : 0) * CW;  // a wave past the last group loads group 0, unused
 #pragma unroll
-    for (int q = 0; q < SPW; ++q) {
-        // A wave past the last slice multiplies zeros instead of branching, so
-        // every load above stays ahead of the first MFMA.
-        const bool has = wave + 4 * q < NS;
-        const float4 ag = has ? float4{a[q].x * g[q].x, a[q].y * g[q].y, a[q].z * g[q].z, a[q].w * g[q].w}
-                              : float4{0.f, 0.f, 0.f, 0.f};
-        const float4 bb = has ? b[q] : float4{0.f, 0.f, 0.f, 0.f};
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.x, bb.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.y, bb.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.z, bb.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.w, bb.w, acc, 0, 0, 0);
+        for (int s = 0; s < SPG; ++s) {
+            a[k][s] = *(const float4 *)(Ap + c0 + 16 * s);
+            g[k][s] = *(const float4 *)(Gp + c0 + 16 * s);
+            b[k][s] = *(const float4 *)(Bp + c0 + 16 * s);
+        }
     }
-    __shared__ floatx4 part[4][kWave];
-    part[wave][lane] = acc;
+    __shared__ floatx4 part[NQ][kWave];
+#pragma unroll
+    for (int k = 0; k < GPW; ++k) {
+        const int grp = wave + 4 * k;
+        if (grp >= NQ) break;  // wave-uniform
+        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < SPG; ++s) {
+            const float4 ag = float4{a[k][s].x * g[k][s].x, a[k][s].y * g[k][s].y, a[k][s].z * g[k][s].z,
+                                     a[k][s].w * g[k][s].w};
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.x, b[k][s].x, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.y, b[k][s].y, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.z, b[k][s].z, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(ag.w, b[k][s].w, acc, 0, 0, 0);
+        }
+        part[grp][lane] = acc;
+    }
     __syncthreads();
     if (wave != 0) return;
     floatx4 sum = part[0][lane];
 #pragma unroll
-    for (int w = 1; w < 4; ++w) sum += part[w][lane];
+    for (int k = 1; k < NQ; ++k) sum += part[k][lane];
     // acc layout (16x16x4 f32): lane (fr, fg) holds rows i = 4 fg + v, column fr
     const float u = p.cand_u[bt * kK + fr];
 #pragma unroll
@@ -213,8 +225,31 @@ __global__ __launch_bounds__(1024) void walk_kernel(PairParams p) {
     for (int t = wave; t < n; t += nwave) {
         const int64_t bt = (int64_t)b * L + t;
         float s[4];
+        if (p.P != nullptr) {
+            // S = U + (((P_0 + P_1) + P_2) + ...), the groups in order, as
+            // pair_kernel sums them; rows i >= 1 of position 0 are -inf
+            const int j = (int)(lane & 15);
+            const float u = p.cand_u[bt * kK + j];
+            const float *pp = p.P + bt * p.nq * (kK * kK) + 4 * (lane >> 4) * kK + j;
+            floatx4 sum;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s[v] = p.S_in[(bt * kK + 4 * (lane >> 4) + v) * kK + (lane & 15)];
+            for (int v = 0; v < 4; ++v) sum[v] = pp[v * kK];
+            for (int k = 1; k < p.nq; ++k) {
+                floatx4 x;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) x[v] = pp[k * (kK * kK) + v * kK];
+                sum += x;
+            }
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int i = 4 * (int)(lane >> 4) + v;
+                s[v] = (t == 0 && i >= 1) ? -__builtin_inff() : u + sum[v];
+                if (p.S != nullptr) p.S[(bt * kK + i) * kK + j] = s[v];
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s[v] = p.S_in[(bt * kK + 4 * (lane >> 4) + v) * kK + (lane & 15)];
+        }
         const float u = p.w.mode == 1 ? p.w.uniforms[bt] : 0.0f;
         decide_position(s, t, p.w, u, want_q, sh);
     }

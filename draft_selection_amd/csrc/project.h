@@ -46,6 +46,13 @@ constexpr int kBK = 64;  // K elements per step (128 bytes per row)
 #define DSEL_MMA_RPM 2
 #endif
 constexpr int RPM = DSEL_MMA_RPM;
+// The step's DMA loads go out one per MFMA from MFMA number DSEL_MMA_DMA_AT
+// (default: half way through the step's MFMAs, after the fragment reads of
+// the next step have been issued).  Measured on the 256 x 128 fused tile: 4-5%
+// faster main loop than issuing them from the first MFMA, at every workload.
+#ifndef DSEL_MMA_DMA_AT
+#define DSEL_MMA_DMA_AT (NMF / 2)
+#endif
 
 
 // BM x BN tile computed by GM x GN waves, each owning WM x WN as 32 x 32 MFMA
@@ -111,32 +118,56 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // register set) and runs the MFMAs of step kt from registers while they fly.
 // Keeping a whole step of reads in flight is what lets LDS reach its streaming
 // rate; one slice at a time leaves it latency-bound.
+// The W tile row a lane's u-th DMA load fills (rows 8 (wave + NW u) + lane / 8)
+// and the source offset of its 16-byte chunk within that row: physical chunk
+// lane % 8 of tile row `row` holds logical chunk (lane % 8) ^ key(row).
+template <class T>
+__device__ __forceinline__ int dma_row(int u) {
+    return 8 * ((int)(threadIdx.x >> 6) + T::NW * u) + (int)(lane_id() >> 3);
+}
+__device__ __forceinline__ int dma_chunk_elems(int row) {
+    return (((int)(lane_id() & 7)) ^ ((row >> 1) & 7)) << 3;
+}
+
+template <class T>
+__device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T::DXI],
+                                                 const uint16_t *const (&wsrc)[T::DWI], int k0, int k1,
+                                                 uint16_t *Xs, uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN]);
+
+// W rows from one row-major matrix (row stride wstride); tile rows at or past
+// `wrows` re-read row wrows - 1.
 template <class T>
 __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DXI], const uint16_t *wbase,
                                              int64_t wstride, int k0, int k1, uint16_t *Xs,
                                              uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN],
                                              int wrows = T::BNv) {
+    const uint16_t *wsrc[T::DWI];
+#pragma unroll
+    for (int u = 0; u < T::DWI; ++u) {
+        const int row = dma_row<T>(u);
+        const int srow = row < wrows ? row : wrows - 1;
+        wsrc[u] = wbase + (int64_t)srow * wstride + dma_chunk_elems(row);
+    }
+    mma_tile_dma_src<T>(xsrc, wsrc, k0, k1, Xs, Ws, acc);
+}
+
+// The main loop proper: xsrc / wsrc are the lane's DMA sources at K = 0 (row
+// pointer plus its swizzled chunk offset).
+template <class T>
+__device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T::DXI],
+                                                 const uint16_t *const (&wsrc)[T::DWI], int k0, int k1,
+                                                 uint16_t *Xs, uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN]) {
     constexpr int BM = T::BMv, BN = T::BNv, NW = T::NW;
     constexpr int XI = T::DXI, WI = T::DWI;
     static_assert(XI >= 1 && WI >= 1 && XI * NW * 8 == BM && WI * NW * 8 == BN, "DMA tile shape");
     constexpr int PER = XI + WI;  // loads per wave per step
     constexpr int NS = 3;
     constexpr int KS = kBK / 16;  // 16-deep slices per step
-    const int tid = threadIdx.x;
     const uint32_t lane = lane_id();
-    const int wave = tid >> 6;
+    // wave-uniform, so the LDS-DMA destinations below are scalar arithmetic
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave / T::GNv, wn = wave % T::GNv;
     const int fr = lane & 31, fk = lane >> 5;  // fragment row / column, 8-element K half
-    // this lane's W source rows 8 (wave + NW u) + lane / 8; physical chunk
-    // lane % 8 of row `row` holds logical chunk (lane % 8) ^ key(row).
-    const int lrow = (int)(lane >> 3), pch = (int)(lane & 7);
-    const uint16_t *wsrc[WI];
-#pragma unroll
-    for (int u = 0; u < WI; ++u) {
-        const int row = 8 * (wave + NW * u) + lrow;
-        const int srow = row < wrows ? row : wrows - 1;  // rows past the matrix re-read its last row
-        wsrc[u] = wbase + (int64_t)srow * wstride + ((pch ^ ((row >> 1) & 7)) << 3);
-    }
     // LDS element offsets of the rows of this lane's fragments, relative to a
     // stage; every such row is = fr (mod 32), so chunk (2 s + fk) of it sits
     // at physical chunk (2 s + fk) ^ key(fr)
@@ -210,14 +241,15 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
 #pragma unroll
                     for (int rr = q * RPM; rr < (q + 1) * RPM; ++rr)
                         if (rr < NR) frag_read(rr, xb, wb, std::integral_constant<int, SET ^ 1>());
-                    if (q < PER) dma(q, kk, cur);
+                    if (q >= DSEL_MMA_DMA_AT && q < DSEL_MMA_DMA_AT + PER) dma(q - DSEL_MMA_DMA_AT, kk, cur);
                     __builtin_amdgcn_sched_barrier(0);  // keep this order
                 }
         }
 #pragma unroll
         for (int rr = NMF * RPM; rr < NR; ++rr) frag_read(rr, xb, wb, std::integral_constant<int, SET ^ 1>());
 #pragma unroll
-        for (int q = NMF; q < PER; ++q) dma(q, kk, cur);
+        for (int q = NMF; q < DSEL_MMA_DMA_AT + PER; ++q)
+            if (q >= DSEL_MMA_DMA_AT) dma(q - DSEL_MMA_DMA_AT, kk, cur);
         cur = nxt;
     };
     DSEL_ISSUE(k0, 0);
@@ -226,11 +258,15 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
     wait_vmcnt<2 * PER>();
     wg_barrier();
     DSEL_READ_STEP(0, 0);
-    for (int kt = k0; kt < k1; kt += 2) {
+    // Steps in pairs (register sets 0 then 1), then an odd last step in set 0.
+    // One loop exit: a break between the two steps made the compiler copy
+    // every accumulator on each trip.
+    int kt = k0;
+    for (; kt + 1 < k1; kt += 2) {
         step(kt, std::integral_constant<int, 0>());
-        if (kt + 1 >= k1) break;
         step(kt + 1, std::integral_constant<int, 1>());
     }
+    if (kt < k1) step(kt, std::integral_constant<int, 0>());
     wait_vmcnt<0>();  // drain the redundant tail loads before LDS is released
 #undef DSEL_ISSUE
 #undef DSEL_READ_STEP
@@ -708,6 +744,13 @@ struct GateParams {
     int B, L;
     const int32_t *len;  // ragged batch: valid positions per block (nullptr: all L)
     float *A_prev, *G;
+    // A(verified_b) goes to A_ver + b * ver_stride; with ver_zero the 15 rows
+    // after it (position 0's unused predecessor rows of A_prev) are zeroed.
+    // The separate calls point A_ver at A_prev (stride L * 16 * r, zeroing);
+    // the fused selector at a compact [B][r] buffer.
+    float *A_ver;
+    int64_t ver_stride;
+    bool ver_zero;
     float *part;        // [nsplit][rows_gate + rows_ver][r] partial sums (nsplit > 1)
     int mt_gate, mt_ver, nside, nsplit;  // 128-row tiles of each job, column tiles, K splits
 };
@@ -796,10 +839,10 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
             for (int e = 0; e < 4; ++e) gv[e] = 1.0f / (1.0f + expf(-v[e]));
             *(floatx4 *)(p.G + m * r + n) = gv;
         } else {
-            float *base = p.A_prev + (m * p.L * kK) * r + n;
+            float *base = p.A_ver + m * p.ver_stride + n;
             *(floatx4 *)base = v;
-#pragma unroll
-            for (int z = 1; z < kK; ++z) *(floatx4 *)(base + (int64_t)z * r) = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (p.ver_zero)
+                for (int z = 1; z < kK; ++z) *(floatx4 *)(base + (int64_t)z * r) = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     });
 }
@@ -822,9 +865,10 @@ __device__ __forceinline__ void gate_reduce_elem(const GateParams &p, int64_t e)
         p.G[row * p.r + n] = 1.0f / (1.0f + expf(-sum));
     } else {
         const int64_t b = row - (int64_t)p.B * p.L;
-        float *base = p.A_prev + (b * p.L * kK) * p.r + n;
+        float *base = p.A_ver + b * p.ver_stride + n;
         base[0] = sum;
-        for (int z = 1; z < kK; ++z) base[(int64_t)z * p.r] = 0.0f;
+        if (p.ver_zero)
+            for (int z = 1; z < kK; ++z) base[(int64_t)z * p.r] = 0.0f;
     }
 }
 

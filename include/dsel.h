@@ -221,10 +221,20 @@ dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const int32_
  * as a launch of its own.
  *   Inputs and outputs are those of the separate calls; `vocab` is the
  *   logits' width in use, and E needs at least `vocab` rows (every candidate
- *   id is below it; the projections' id check uses it).  All outputs (cand_id,
- *   cand_u, A_prev, B_cur, G, S) are required.
+ *   id is below it; the projections' id check uses it).  cand_id and cand_u
+ *   are required.  A_prev and B_cur are optional together (both NULL or both
+ *   given), G and S are optional each: a NULL output is not written.
+ *   Route.  For blocks of at most 16 positions and batches large enough to
+ *   fill the chip (ceil(batch / floor(16 / block)) * r / CW >= 128
+ *   workgroups, CW = 64 when r % 64 == 0 and r >= 128, else 32), the
+ *   candidate projections and the pair term run as one kernel per tile of
+ *   whole blocks and column group of the rank: A and B of the group stay on
+ *   chip and only each group's 16 x 16 partial table per position leaves it;
+ *   the walk kernel adds the groups (in order) to the logits.  Otherwise the
+ *   separate kernels run and A_prev, B_cur and S pass through the workspace
+ *   when not asked for.  Either route gives the same bits.
  *   walk       the walk arguments (required), as for dsel_score_pairs.
- *   workspace  at least dsel_select_path_workspace_bytes() bytes (16-byte
+ *   workspace  at least dsel_select_path_workspace_bytes() bytes (256-byte
  *              aligned); contents need no initialisation.
  * Requirements: those of every step (d % 64 == 0; r % 32 == 0, 32 <= r <= 256;
  * 1 <= block <= DSEL_MAX_BLOCK; 16 <= vocab < 2^31; ld >= vocab). */
@@ -242,9 +252,9 @@ typedef struct {
     const int32_t *block_len; /* [batch] or NULL (see "Ragged batches") */
     int32_t *cand_id;     /* out [batch, block, 16] */
     float *cand_u;        /* out [batch, block, 16] */
-    float *A_prev, *B_cur; /* out [batch, block, 16, r] */
-    float *G;             /* out [batch, block, r] */
-    float *S;             /* out [batch, block, 16, 16] */
+    float *A_prev, *B_cur; /* out [batch, block, 16, r], both or neither (nullable) */
+    float *G;             /* out [batch, block, r] (nullable) */
+    float *S;             /* out [batch, block, 16, 16] (nullable) */
 } dsel_path_args;
 size_t dsel_select_path_workspace_bytes(int64_t batch, int64_t block, int64_t vocab, dsel_dtype dt, int64_t d,
                                         int64_t r);

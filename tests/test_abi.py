@@ -161,7 +161,7 @@ def test_select_path_validation(lib):
     assert call(args(), wsp=f + 8) == -3
     assert call(args(dt=5)) == -2
     assert call(args(d=96)) == -1 and call(args(r=48)) == -1 and call(args(block=33), wsb=1 << 40) == -1
-    assert call(args(S=None)) == -1 and call(args(G=None)) == -1
+    assert call(args(A_prev=None)) == -1 and call(args(B_cur=None)) == -1  # both or neither
     assert call(args(h=0x100002)) == -3 and call(args(block_len=0x100002)) == -3
     assert call(args(batch=0, logits=None, E=None)) == 0  # no work
 

@@ -35,7 +35,8 @@ def _lens_dev(lens, dev):
 
 def _select(d, mode, lens, T=1.0):
     res = ds.select_path(d["logits"], d["E"], d["W_A"], d["W_B"], d["W_H"], d["h"], d["verified"], mode=mode,
-                         temperature=T, uniforms=d["uniforms"], want_S=True, want_q=True, block_len=lens)
+                         temperature=T, uniforms=d["uniforms"], want_S=True, want_q=True, want_AB=True,
+                         block_len=lens)
     torch.cuda.synchronize()
     assert ds.device_error() == 0
     return {k: v.cpu().numpy() for k, v in res.items()}
