@@ -12,6 +12,9 @@ Entry points (same names as the C ABI):
   project_gate(...), project_gate_overlap(...), project_cand(...)  (its halves)
   score_pairs(cand_u, A_prev, B_cur, G, ...)        -> S and/or the walk
   walk(S, cand_id, ...)                             -> the walk alone
+  project_pairs(E, W_A, W_B, cand_id, G, A_ver)     -> pair partials (project_cand
+                                                       and the pair term fused)
+  walk_pairs(cand_u, partials, cand_id, ...)        -> S and/or the walk from them
   select_path(logits, E, W_A, W_B, W_H, h, verified, ...)  -> all of the above
                                                        in one dsel_select_path call
   verify(target_logits, cand_id, path_slot, ...)    -> n_accepted, out_tok
@@ -88,6 +91,9 @@ def _load():
             "dsel_gather_probe_words": ([I64, I64, I64], SZ),
             "dsel_gather_probe": ([P, I64, I64, P, I64, I64, P, SZ, P], I32),
             "dsel_select_path": ([C.POINTER(PathArgs), C.POINTER(WalkArgs), P, SZ, P], I32),
+            "dsel_pair_groups": ([I64], I64),
+            "dsel_project_pairs": ([P, I64, I64, P, P, I64, P, P, P, I64, I64, I64, P, P, P, P, P], I32),
+            "dsel_walk_pairs": ([P, P, I64, I64, P, I64, P, C.POINTER(WalkArgs), P], I32),
             "dsel_verify_workspace_bytes": ([I64, I64, I64], SZ),
             "dsel_dyn_conv_workspace_bytes": ([I64, I64, I64], SZ),
             "dsel_lmhead_topk_workspace_bytes": ([I64, I64], SZ),
@@ -372,6 +378,64 @@ def score_pairs(cand_u, A_prev, B_cur, G, want_S: bool = True, walk_mode: Option
     st = _load().dsel_score_pairs(_ptr(cand_u), _ptr(A_prev), _ptr(B_cur), _ptr(G), B, L, _lens(block_len, B), r,
                                   _ptr(S), C.byref(wa) if wa is not None else None, _stream(stream))
     _check(st, "dsel_score_pairs")
+    if want_S:
+        res["S"] = S
+    return res
+
+
+def pair_groups(r: int) -> int:
+    """Column groups of the rank in the pair partials of project_pairs."""
+    return int(_load().dsel_pair_groups(r))
+
+
+@_on_stream
+def project_pairs(E, W_A, W_B, cand_id, G, A_ver, ver_stride: Optional[int] = None, want_AB: bool = False,
+                  stream=None, block_len=None):
+    """Candidate projections and the pair term in one kernel (blocks of at most
+    16 positions): returns ``partials [B, L, nq, 16, 16]`` fp32 (and ``A_prev``,
+    ``B_cur`` with ``want_AB``).  ``A_ver``: A of each block's verified token,
+    ``[B, r]`` (``ver_stride`` r) or the ``A_prev`` written by project_gate
+    (``ver_stride`` = L * 16 * r)."""
+    V, d = E.shape
+    r = W_A.shape[0]
+    B, L = cand_id.shape[:2]
+    for t, n, shp in ((E, "E", (V, d)), (W_A, "W_A", (r, d)), (W_B, "W_B", (r, d))):
+        _need(t, n, torch.bfloat16, shp)
+    _need(cand_id, "cand_id", torch.int32, (B, L, K))
+    _need(G, "G", torch.float32, (B, L, r))
+    _need(A_ver, "A_ver", torch.float32)
+    vs = r if ver_stride is None else int(ver_stride)
+    if B and A_ver.numel() < (B - 1) * vs + r:
+        raise ValueError("A_ver is too small for its stride")
+    nq = pair_groups(r)
+    dev = E.device
+    partials = torch.empty((B, L, nq, K, K), dtype=torch.float32, device=dev)
+    A_prev = B_cur = None
+    if want_AB:
+        A_prev = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+        B_cur = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+    st = _load().dsel_project_pairs(_ptr(E), V, d, _ptr(W_A), _ptr(W_B), r, _ptr(cand_id), _ptr(G), _ptr(A_ver), vs,
+                                    B, L, _lens(block_len, B), _ptr(partials), _ptr(A_prev), _ptr(B_cur),
+                                    _stream(stream))
+    _check(st, "dsel_project_pairs")
+    res = {"partials": partials}
+    if want_AB:
+        res.update(A_prev=A_prev, B_cur=B_cur)
+    return res
+
+
+@_on_stream
+def walk_pairs(cand_u, partials, cand_id, mode: int = GREEDY, temperature: float = 1.0, uniforms=None,
+               want_S: bool = False, want_q: bool = False, stream=None, block_len=None):
+    """The scores from project_pairs' partial tables and the walk over them."""
+    B, L, nq = partials.shape[:3]
+    _need(partials, "partials", torch.float32, (B, L, nq, K, K))
+    _need(cand_u, "cand_u", torch.float32, (B, L, K))
+    _need(cand_id, "cand_id", torch.int32, (B, L, K))
+    S = torch.empty((B, L, K, K), dtype=torch.float32, device=partials.device) if want_S else None
+    wa, res = _walk_args(cand_id, mode, temperature, uniforms, want_q, True)
+    _check(_load().dsel_walk_pairs(_ptr(cand_u), _ptr(partials), B, L, _lens(block_len, B), nq, _ptr(S), C.byref(wa),
+                                   _stream(stream)), "dsel_walk_pairs")
     if want_S:
         res["S"] = S
     return res

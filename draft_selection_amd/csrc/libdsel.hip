@@ -564,36 +564,41 @@ struct FusedPlan {
     int CW = 64;
 };
 
-dsel_status plan_fused(const dsel_path_args *a, const float *G, const float *A_ver, int64_t ver_stride,
-                       float *P, FusedPlan *f) {
-    dsel_status st = check_project_common(a->E, a->vocab, a->d, a->r, a->batch, a->block);
+dsel_status plan_fused(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A, const uint16_t *W_B,
+                       int64_t r, const int32_t *cand_id, const float *G, const float *A_ver, int64_t ver_stride,
+                       int64_t batch, int64_t block, const int32_t *block_len, float *P, float *A_prev,
+                       float *B_cur, FusedPlan *f) {
+    dsel_status st = check_project_common(E, vocab, d, r, batch, block);
     if (st != DSEL_OK) return st;
-    if (!a->W_A || !a->W_B || !a->cand_id) return DSEL_E_ARG;
-    if (!aligned(a->W_A, 16) || !aligned(a->W_B, 16) || !aligned(a->cand_id, 4) || !aligned(a->A_prev, 16) ||
-        !aligned(a->B_cur, 16) || !aligned(a->block_len, 4))
+    if (fused_blocks_per_tile(block) == 0 || batch > (int64_t)INT_MAX / 16) return DSEL_E_ARG;
+    if (!W_A || !W_B || !cand_id || !G || !A_ver || !P || ver_stride < r) return DSEL_E_ARG;
+    if ((A_prev == nullptr) != (B_cur == nullptr)) return DSEL_E_ARG;
+    if (!aligned(W_A, 16) || !aligned(W_B, 16) || !aligned(cand_id, 4) || !aligned(G, 16) || !aligned(A_ver, 16) ||
+        ver_stride % 4 != 0 || !aligned(P, 16) || !aligned(A_prev, 16) || !aligned(B_cur, 16) ||
+        !aligned(block_len, 4))
         return DSEL_E_ALIGN;
     FusedParams &p = f->p;
-    p.E = a->E;
-    p.V = a->vocab;
-    p.d = (int)a->d;
-    p.r = (int)a->r;
-    p.WA = a->W_A;
-    p.WB = a->W_B;
-    p.cand = a->cand_id;
+    p.E = E;
+    p.V = vocab;
+    p.d = (int)d;
+    p.r = (int)r;
+    p.WA = W_A;
+    p.WB = W_B;
+    p.cand = cand_id;
     p.G = G;
     p.A_ver = A_ver;
     p.ver_stride = ver_stride;
-    p.B = (int)a->batch;
-    p.L = (int)a->block;
-    p.len = a->block_len;
-    p.nb = fused_blocks_per_tile(a->block);
-    p.ntile = (int)fused_tiles(a->batch, a->block);
-    f->CW = pair_group_width((int)a->r);
-    p.nq = (int)(a->r / f->CW);
+    p.B = (int)batch;
+    p.L = (int)block;
+    p.len = block_len;
+    p.nb = fused_blocks_per_tile(block);
+    p.ntile = (int)fused_tiles(batch, block);
+    f->CW = pair_group_width((int)r);
+    p.nq = (int)(r / f->CW);
     p.P = P;
-    p.A_prev = a->A_prev;
-    p.B_cur = a->B_cur;
-    if (fused_grid(a->batch, a->block, a->r) >= (int64_t)INT_MAX) return DSEL_E_ARG;
+    p.A_prev = A_prev;
+    p.B_cur = B_cur;
+    if (fused_grid(batch, block, r) >= (int64_t)INT_MAX) return DSEL_E_ARG;
     return DSEL_OK;
 }
 
@@ -610,6 +615,50 @@ DSEL_API size_t dsel_select_path_workspace_bytes(int64_t batch, int64_t block, i
                                                  int64_t d, int64_t r) {
     PathLayout l;
     return path_layout(batch, block, vocab, dt, d, r, &l) ? l.total : 0;
+}
+
+DSEL_API int64_t dsel_pair_groups(int64_t r) {
+    if (r < 32 || r > DSEL_MAX_RANK || r % 32 != 0) return 0;
+    return r / pair_group_width((int)r);
+}
+
+DSEL_API dsel_status dsel_project_pairs(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                                        const uint16_t *W_B, int64_t r, const int32_t *cand_id, const float *G,
+                                        const float *A_ver, int64_t ver_stride, int64_t batch, int64_t block,
+                                        const int32_t *block_len, float *partials, float *A_prev, float *B_cur,
+                                        dsel_stream_t stream) {
+    if (batch == 0 && block >= 1 && block <= 16) {
+        dsel_status st = check_project_common(E, vocab, d, r, batch, block);
+        return st;  // nothing to do; pointers may be NULL
+    }
+    FusedPlan f;
+    dsel_status st = plan_fused(E, vocab, d, W_A, W_B, r, cand_id, G, A_ver, ver_stride, batch, block, block_len,
+                                partials, A_prev, B_cur, &f);
+    if (st != DSEL_OK) return st;
+    return launch_fused(f, stream);
+}
+
+DSEL_API dsel_status dsel_walk_pairs(const float *cand_u, const float *partials, int64_t batch, int64_t block,
+                                     const int32_t *block_len, int64_t nq, float *S, const dsel_walk_args *walk,
+                                     dsel_stream_t stream) {
+    if (!walk) return DSEL_E_ARG;
+    if (batch < 0 || batch >= (int64_t)INT_MAX / DSEL_MAX_BLOCK || block < 1 || block > DSEL_MAX_BLOCK) return DSEL_E_ARG;
+    if (nq < 1 || nq > DSEL_MAX_RANK / 32) return DSEL_E_ARG;
+    if (walk->mode != DSEL_GREEDY && walk->mode != DSEL_SAMPLED) return DSEL_E_DTYPE;
+    if (batch == 0) return DSEL_OK;
+    if (!cand_u || !partials) return DSEL_E_ARG;
+    if (!aligned(cand_u, 4) || !aligned(partials, 16) || !aligned(S, 4) || !aligned(block_len, 4)) return DSEL_E_ALIGN;
+    PairParams p = {};
+    dsel_status st = check_walk(walk, &p.w);
+    if (st != DSEL_OK) return st;
+    p.cand_u = cand_u;
+    p.P = partials;
+    p.nq = (int)nq;
+    p.B = (int)batch;
+    p.L = (int)block;
+    p.len = block_len;
+    p.S = S;
+    return launch_walk(p, stream);
 }
 
 DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_args *walk, void *workspace,
@@ -646,7 +695,9 @@ DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_a
             g.p.ver_zero = false;
         }
         FusedPlan f;
-        st = plan_fused(a, G, A_ver, ab ? a->block * kK * a->r : a->r, (float *)(ws + l.part), &f);
+        st = plan_fused(a->E, a->vocab, a->d, a->W_A, a->W_B, a->r, a->cand_id, G, A_ver,
+                        ab ? a->block * kK * a->r : a->r, a->batch, a->block, a->block_len, (float *)(ws + l.part),
+                        a->A_prev, a->B_cur, &f);
         if (st != DSEL_OK) return st;
         PairPlan q;
         if (!a->cand_u || !aligned(a->S, 4)) return !a->cand_u ? DSEL_E_ARG : DSEL_E_ALIGN;

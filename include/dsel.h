@@ -213,6 +213,50 @@ dsel_status dsel_score_pairs(const float *cand_u, const float *A_prev, const flo
 dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const int32_t *block_len,
                       const dsel_walk_args *walk, dsel_stream_t stream);
 
+/* project_pairs -- dsel_project_cand and the pair term of dsel_score_pairs in
+ * one kernel, for blocks of at most 16 positions ([P1] Method > Lightweight
+ * Path Selector: A and B map tokens to 256-d vectors, eq. S_t scores every
+ * adjacent pair in one parallel pass).  One workgroup per tile of whole blocks
+ * (floor(16 / block) blocks, 256 candidate rows) and column group q of the
+ * rank (CW = 64 columns when r % 64 == 0 and r >= 128, else 32; nq = r / CW
+ * groups, dsel_pair_groups(r)) computes A and B of the group for every
+ * candidate of the tile on bf16 MFMA (fp32 accumulation) and then
+ *     partials[b,t,q,i,j] = sum_{c in group q} A_prev[b,t,i,c] G[b,t,c] B_cur[b,t,j,c]
+ * in fp32 (for position 0 only row i = 0 is meaningful: its one predecessor is
+ * the verified token).  A and B stay on chip unless asked for.
+ *   cand_id    [batch, block, 16] int32 (from dsel_select_topk).
+ *   G          [batch, block, r] fp32 (from dsel_project_gate).
+ *   A_ver, ver_stride  A(verified token of block b) is read at A_ver + b *
+ *              ver_stride (r floats; ver_stride >= r, a multiple of 4): e.g.
+ *              the A_prev written by dsel_project_gate with ver_stride =
+ *              block * 16 * r.
+ *   partials   out [batch, block, nq, 16, 16] fp32.
+ *   A_prev, B_cur  optional outputs (both NULL or both given), written as
+ *              dsel_project_cand writes them (A_prev of position 0 is not).
+ * dsel_walk_pairs then adds the groups in order to cand_u; the result has the
+ * same bits as dsel_project_cand + dsel_score_pairs.  Token ids outside [0,
+ * vocab) read a zero row and set DSEL_DEVERR_TOKEN_RANGE.
+ * Requirements: 1 <= block <= 16; otherwise as dsel_project_cand. */
+int64_t dsel_pair_groups(int64_t r); /* nq for rank r (0 for an invalid r) */
+dsel_status dsel_project_pairs(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
+                               const uint16_t *W_B, int64_t r, const int32_t *cand_id, const float *G,
+                               const float *A_ver, int64_t ver_stride, int64_t batch, int64_t block,
+                               const int32_t *block_len, float *partials, float *A_prev, float *B_cur,
+                               dsel_stream_t stream);
+
+/* walk_pairs -- the scores from dsel_project_pairs' partial tables and the walk
+ * over them: S[b,t,i,j] = cand_u[b,t,j] + (((partials[b,t,0,i,j] +
+ * partials[b,t,1,i,j]) + ...) with S[b,0,i>=1,:] = -inf, then the walk of
+ * dsel_score_pairs (same bits).
+ *   partials  [batch, block, nq, 16, 16] fp32, nq = dsel_pair_groups(r).
+ *   S      out [batch, block, 16, 16] fp32, nullable (the walk does not need it).
+ *   walk   required.
+ * Requirements: 1 <= block <= DSEL_MAX_BLOCK, 1 <= nq <= 8; partials 16-byte
+ * aligned. */
+dsel_status dsel_walk_pairs(const float *cand_u, const float *partials, int64_t batch, int64_t block,
+                            const int32_t *block_len, int64_t nq, float *S, const dsel_walk_args *walk,
+                            dsel_stream_t stream);
+
 /* select_path -- the whole selector in one call ([P1] Method > Lightweight Path
  * Selector, [P3] "Selection beats correction"): dsel_select_topk, dsel_project
  * (gate and candidates), dsel_score_pairs and the walk, on one stream, with the
@@ -225,14 +269,12 @@ dsel_status dsel_walk(const float *S, int64_t batch, int64_t block, const int32_
  *   are required.  A_prev and B_cur are optional together (both NULL or both
  *   given), G and S are optional each: a NULL output is not written.
  *   Route.  For blocks of at most 16 positions and batches large enough to
- *   fill the chip (ceil(batch / floor(16 / block)) * r / CW >= 128
- *   workgroups, CW = 64 when r % 64 == 0 and r >= 128, else 32), the
- *   candidate projections and the pair term run as one kernel per tile of
- *   whole blocks and column group of the rank: A and B of the group stay on
- *   chip and only each group's 16 x 16 partial table per position leaves it;
- *   the walk kernel adds the groups (in order) to the logits.  Otherwise the
- *   separate kernels run and A_prev, B_cur and S pass through the workspace
- *   when not asked for.  Either route gives the same bits.
+ *   fill the chip (ceil(batch / floor(16 / block)) * dsel_pair_groups(r) >=
+ *   128 workgroups), the candidate projections and the pair term run as the
+ *   kernels of dsel_project_pairs and dsel_walk_pairs: A and B stay on chip
+ *   and only each group's 16 x 16 partial table per position leaves it.
+ *   Otherwise the separate kernels run and A_prev, B_cur and S pass through
+ *   the workspace when not asked for.  Either route gives the same bits.
  *   walk       the walk arguments (required), as for dsel_score_pairs.
  *   workspace  at least dsel_select_path_workspace_bytes() bytes (256-byte
  *              aligned); contents need no initialisation.

@@ -52,6 +52,7 @@ def _load():
             "ora_verify_draw": [P, I32, I64, I64, I64, I64, P, P, I32, D, P, I64, I64, I32, P, P],
             "ora_dyn_conv": [P, P, P, P, I64, I64, I64, P, P],
             "ora_lmhead_topk": [P, P, I64, I64, I64, P, P],
+            "ora_time_selector": [P, I32, I64, P, I64, P, P, P, I64, P, P, P, D, I32, I64, I64, P, P, P],
         }
         for name, args in sig.items():
             f = getattr(lib, name)
@@ -339,3 +340,22 @@ def dyn_conv_ragged(x, x_prev, base, W_c, block_len):
         y[b, :n] = yb[0]
         corr[b, :n] = cb[0]
     return y, corr
+
+
+def time_selector(inp: Dict[str, np.ndarray], mode: int = GREEDY, T: float = 1.0):
+    """The whole selector on ``inp`` with each stage timed inside the C library
+    on the monotonic clock.  Returns ``(path_slot, seconds per stage, OpenMP
+    threads)``; the stages are top-16, projections, scores, walk."""
+    logits = np.ascontiguousarray(inp["logits"])
+    B, L, V = logits.shape
+    dt = 1 if logits.dtype == np.uint16 else 0
+    E, W_A, W_B, W_H, h = (np.ascontiguousarray(inp[k]) for k in ("E", "W_A", "W_B", "W_H", "h"))
+    ver = np.ascontiguousarray(inp["verified"], np.int32)
+    u = np.ascontiguousarray(inp["uniforms"], np.float32) if mode == SAMPLED else None
+    slot = np.empty((B, L), np.int32)
+    sec = np.zeros(4, np.float64)
+    nt = C.c_int(0)
+    rc = _load().ora_time_selector(_p(logits), dt, V, _p(E), E.shape[1], _p(W_A), _p(W_B), _p(W_H), W_A.shape[0],
+                                   _p(h), _p(ver), _p(u), float(T), int(mode), B, L, _p(slot), _p(sec), C.byref(nt))
+    _check(rc, "time_selector")
+    return slot, dict(zip(("select_topk", "project", "score_pairs", "walk"), sec.tolist())), int(nt.value)

@@ -6,12 +6,15 @@
  * Plain loops, fp64 throughout, OpenMP over independent rows / positions.
  * No blocking, fusion or reordering beyond the definitions on the pages.
  */
+#define _POSIX_C_SOURCE 199309L /* clock_gettime */
 #include "oracle.h"
 
 #include <math.h>
+#include <omp.h>
 #include <stddef.h>
 #include <stdlib.h>
 #include <string.h>
+#include <time.h>
 
 static double bf16_to_f64(uint16_t u) {
     uint32_t bits = (uint32_t)u << 16;
@@ -463,4 +466,52 @@ int ora_lmhead_topk(const uint16_t *h, const uint16_t *W, int64_t rows, int64_t 
         free(hr);
     }
     return 0;
+}
+
+/* ---------------------------------------------------- timed selector ---- */
+static double mono_s(void) {
+    struct timespec ts;
+    clock_gettime(CLOCK_MONOTONIC, &ts);
+    return (double)ts.tv_sec + 1e-9 * (double)ts.tv_nsec;
+}
+
+int ora_time_selector(const void *logits, int dtype, int64_t V, const uint16_t *E, int64_t d,
+                      const uint16_t *W_A, const uint16_t *W_B, const uint16_t *W_H, int64_t r,
+                      const uint16_t *h, const int32_t *verified, const float *uniforms, double T,
+                      int mode, int64_t B, int64_t L, int32_t *path_slot, double *sec, int *threads) {
+    if (!logits || !path_slot || !sec || B < 1 || L < 1 || r < 1) return -1;
+    const int64_t pos = B * L;
+    int32_t *cand_id = malloc(sizeof(int32_t) * pos * ORA_K);
+    float *cand_u = malloc(sizeof(float) * pos * ORA_K);
+    double *A = malloc(sizeof(double) * pos * ORA_K * r), *Bm = malloc(sizeof(double) * pos * ORA_K * r);
+    double *G = malloc(sizeof(double) * pos * r), *S = malloc(sizeof(double) * pos * ORA_K * ORA_K);
+    int32_t *tok = malloc(sizeof(int32_t) * pos);
+    double *ps = malloc(sizeof(double) * pos), *aux = malloc(sizeof(double) * pos);
+    int rc = -1;
+    if (cand_id && cand_u && A && Bm && G && S && tok && ps && aux) {
+        const double t0 = mono_s();
+        rc = ora_select_topk(logits, dtype, pos, V, V, cand_id, cand_u);
+        const double t1 = mono_s();
+        if (rc == 0) rc = ora_project(E, V, d, W_A, W_B, W_H, r, h, cand_id, verified, B, L, A, Bm, G);
+        const double t2 = mono_s();
+        if (rc == 0) rc = ora_score_pairs(cand_u, A, Bm, G, B, L, r, S);
+        const double t3 = mono_s();
+        if (rc == 0) rc = ora_walk(S, cand_id, uniforms, T, mode, B, L, tok, path_slot, ps, aux, NULL);
+        const double t4 = mono_s();
+        sec[0] = t1 - t0;
+        sec[1] = t2 - t1;
+        sec[2] = t3 - t2;
+        sec[3] = t4 - t3;
+    }
+    if (threads) *threads = omp_get_max_threads();
+    free(cand_id);
+    free(cand_u);
+    free(A);
+    free(Bm);
+    free(G);
+    free(S);
+    free(tok);
+    free(ps);
+    free(aux);
+    return rc;
 }

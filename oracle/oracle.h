@@ -70,6 +70,17 @@ int ora_walk(const double *S, const int32_t *cand_id, const float *uniforms, dou
 int ora_step_table(const double *S, const float *uniforms, double T, int mode,
                    int64_t B, int64_t L, int32_t *choice, double *aux);
 
+/* The whole selector (ora_select_topk, ora_project, ora_score_pairs, ora_walk
+ * in that order) with each stage timed on the monotonic clock
+ * (clock_gettime(CLOCK_MONOTONIC)), for the benchmark's CPU baseline: no
+ * arithmetic of its own.  logits [B*L, V] (dtype as ora_select_topk),
+ * uniforms [B,L] (mode 1).  Outputs path_slot [B,L]; sec[4] receives the
+ * seconds of the four stages; threads receives omp_get_max_threads(). */
+int ora_time_selector(const void *logits, int dtype, int64_t V, const uint16_t *E, int64_t d,
+                      const uint16_t *W_A, const uint16_t *W_B, const uint16_t *W_H, int64_t r,
+                      const uint16_t *h, const int32_t *verified, const float *uniforms, double T,
+                      int mode, int64_t B, int64_t L, int32_t *path_slot, double *sec, int *threads);
+
 /* ------------------------------------------------------ verification ---- */
 /* Lossless verification of a drafted block against the target model ([P1]
  * Method, last paragraph, and Setup: sampling stays lossless through rejection

@@ -165,3 +165,37 @@ def test_select_path_validation(lib):
     assert call(args(h=0x100002)) == -3 and call(args(block_len=0x100002)) == -3
     assert call(args(batch=0, logits=None, E=None)) == 0  # no work
 
+
+
+def test_project_pairs_and_walk_pairs_validation(lib):
+    """dsel_project_pairs / dsel_walk_pairs check their arguments on the host."""
+    import draft_selection_amd as ds
+
+    P = C.c_void_p
+    f = P(0x100000)  # never dereferenced
+    assert lib.dsel_pair_groups(256) == 4 and lib.dsel_pair_groups(32) == 1 and lib.dsel_pair_groups(128) == 2
+    assert lib.dsel_pair_groups(224) == 7 and lib.dsel_pair_groups(48) == 0 and lib.dsel_pair_groups(288) == 0
+
+    def pp(**kw):
+        a = dict(E=f, vocab=1024, d=64, W_A=f, W_B=f, r=32, cand_id=f, G=f, A_ver=f, ver_stride=32, batch=4,
+                 block=8, block_len=None, partials=f, A_prev=None, B_cur=None, stream=None)
+        a.update(kw)
+        return lib.dsel_project_pairs(*a.values())
+
+    assert pp(block=17) == -1  # tiles hold whole blocks of at most 16 positions
+    assert pp(ver_stride=16) == -1 and pp(partials=None) == -1 and pp(G=None) == -1
+    assert pp(A_prev=f) == -1  # A_prev and B_cur go together
+    assert pp(d=96) == -1 and pp(r=48) == -1
+    assert pp(G=P(0x100004)) == -3 and pp(ver_stride=34) == -3
+    assert pp(batch=0, E=None, W_A=None) == 0  # no work
+    w = ds.WalkArgs(0, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)
+
+    def wp(walk=w, **kw):
+        a = dict(cand_u=f, partials=f, batch=4, block=8, block_len=None, nq=1, S=None)
+        a.update(kw)
+        return lib.dsel_walk_pairs(*a.values(), C.byref(walk) if walk else None, None)
+
+    assert wp(walk=None) == -1 and wp(nq=0) == -1 and wp(nq=9) == -1 and wp(block=33) == -1
+    assert wp(partials=None) == -1 and wp(partials=P(0x100004)) == -3
+    assert wp(walk=ds.WalkArgs(5, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)) == -2
+    assert wp(batch=0, cand_u=None, partials=None) == 0

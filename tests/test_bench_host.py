@@ -35,15 +35,22 @@ def test_stage_percentiles():
             t.append(t[-1] + (k + 1) * f * 1e-3)
         evs.append([_Ev(x) for x in t])
     p = bench.stage_pcts(evs)
-    assert p["project_gate"] == [pytest.approx(1.1), pytest.approx(1.5), pytest.approx(1.9)]
+    assert p["gate"] == [pytest.approx(1.1), pytest.approx(1.5), pytest.approx(1.9)]
     assert p["step"][1] == pytest.approx(15.0)
     m = bench.stage_means(evs)
-    assert m["score_pairs_walk"] == pytest.approx(6.0)
+    assert m["pair_walk"] == pytest.approx(6.0)
 
 
 def test_cpu_baseline_report():
     cfg = synth.CONFIGS["c0"]
-    r = bench.cpu_baseline(cfg, synth.make(cfg), budget_s=0.5, single_core_s=0.2)
+    r = bench.cpu_baseline(cfg, synth.make(cfg), run_s=0.2, single_core=True)
     assert r["kind"] == "oracle" and r["unit"] == "blocks/s" and r["value"] > 0 and r["cores"] >= 1
     assert set(r["ms_per_block"]) == {"select_topk", "project", "score_pairs", "walk"}
     assert r["single_core"] is None or r["single_core"]["value"] > 0
+    assert "median of 3" in r["sample"] and r["cpu_model"]
+
+
+def test_headline_is_the_largest_graded_workload():
+    assert bench.GRADED == ("c2", "c3", "c4") and bench.HEADLINE == "c4"
+    assert bench.walk_modes(synth.CONFIGS["c4"]) == [0, 1] and bench.walk_modes(synth.CONFIGS["c3"]) == [1]
+    assert bench.dtype_of(synth.CONFIGS["c4"]) == "f32+bf16" and bench.dtype_of(synth.CONFIGS["c2"]) == "bf16"

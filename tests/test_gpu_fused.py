@@ -138,3 +138,52 @@ def test_fused_route_workloads_equal_separate_calls(dev, name, mode):
     sep = _separate(d, mode)
     got = _path(d, mode)
     _bits_equal(got, sep, ("cand_id", "S", "path_tok", "path_slot", "path_s", "q"))
+
+
+@pytest.mark.parametrize("name,B,L,r,d,mode", [
+    ("c1", 1, 16, 256, 2560, 0), ("c1", 2, 16, 256, 2560, 1), ("c0", 4, 8, 32, 64, 0), ("c0", 3, 1, 32, 64, 1),
+    ("c0", 5, 3, 160, 128, 0), ("c0", 2, 16, 128, 64, 1), ("c0", 7, 9, 64, 192, 0)])
+def test_project_pairs_and_walk_pairs_against_oracle(ora, dev, name, B, L, r, d, mode):
+    """The two stages of the fused route as their own calls, at small batches
+    (few workgroups).  Against the oracle: exact top-16, the score bounds and
+    the walk; A_prev / B_cur within the fp32 accumulation bound
+    gamma_d * sum |x w|.  (Here the separate calls split the candidate GEMM
+    along d, which rounds differently, so the bits are compared only between
+    the two ways of passing A(verified), and with and without S.)"""
+    cfg = synth.CONFIGS[name].replace(batch=B, block=L, r=r, d=d, vocab=min(synth.CONFIGS[name].vocab, 4096))
+    inp = synth.make(cfg, seed=B * L + r)
+    d_ = to_dev(inp, dev)
+    A = torch.empty((B, L, K, r), dtype=torch.float32, device=dev)
+    G = torch.empty((B, L, r), dtype=torch.float32, device=dev)
+    ds.project_gate(d_["E"], d_["W_A"], d_["W_H"], d_["h"], d_["verified"], A, G)
+    cid, cu = ds.select_topk(d_["logits"])
+    pp = ds.project_pairs(d_["E"], d_["W_A"], d_["W_B"], cid, G, A, ver_stride=L * K * r, want_AB=True)
+    assert pp["partials"].shape == (B, L, ds.pair_groups(r), K, K)
+    res = ds.walk_pairs(cu, pp["partials"], cid, mode=mode, uniforms=d_["uniforms"], want_S=True, want_q=True)
+    torch.cuda.synchronize()
+    assert ds.device_error() == 0
+    g = {k: v.cpu().numpy() for k, v in res.items()}
+    g["cand_id"] = cid.cpu().numpy()
+    ref = ora.run(inp, mode, 1.0)
+    np.testing.assert_array_equal(g["cand_id"], ref["cand_id"])
+    eps, tol, eps_p, tol_p = check_scores(g["S"], ref["S"], ref["cand_u"])
+    flagged = check_walk(ora, g, ref["S"], g["S"], ref["cand_id"], mode, inp["uniforms"], 1.0, eps)
+    assert flagged <= 1
+    # A_prev (positions >= 1) and B_cur within the fp32 accumulation bound
+    rA, rB, _ = ora.project(inp["E"], inp["W_A"], inp["W_B"], inp["W_H"], inp["h"], ref["cand_id"],
+                            inp["verified"])
+    E = np.abs(synth.bf16_bits_to_f32(inp["E"]).astype(np.float64))
+    WA = np.abs(synth.bf16_bits_to_f32(inp["W_A"]).astype(np.float64))
+    WB = np.abs(synth.bf16_bits_to_f32(inp["W_B"]).astype(np.float64))
+    gam = d * 2.0 ** -24 / (1 - d * 2.0 ** -24)
+    Ag = pp["A_prev"].cpu().numpy().astype(np.float64)[:, 1:]
+    Bg = pp["B_cur"].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(Ag - rA[:, 1:]) <= gam * (E[ref["cand_id"][:, :-1]] @ WA.T) + 1e-30)
+    assert np.all(np.abs(Bg - rB) <= gam * (E[ref["cand_id"]] @ WB.T) + 1e-30)
+    # compact A(verified) [B, r] and no S: the same partials, the same walk
+    Av = A[:, 0, 0].contiguous()
+    pp2 = ds.project_pairs(d_["E"], d_["W_A"], d_["W_B"], cid, G, Av)
+    res2 = ds.walk_pairs(cu, pp2["partials"], cid, mode=mode, uniforms=d_["uniforms"], want_q=True)
+    torch.cuda.synchronize()
+    assert torch.equal(pp2["partials"].view(torch.int32), pp["partials"].view(torch.int32))
+    _bits_equal({k: v.cpu().numpy() for k, v in res2.items()}, g, ("path_slot", "path_s", "q"))

@@ -27,10 +27,11 @@ def _workload(name):
     return _CACHE[name]
 
 
-def _run(inp, dev, mode, T=1.0):
+def _run(inp, dev, mode, T=1.0, want_AB=False):
     d = to_dev(inp, dev)
     res = ds.select_path(d["logits"], d["E"], d["W_A"], d["W_B"], d["W_H"], d["h"], d["verified"],
-                         mode=mode, temperature=T, uniforms=d["uniforms"], want_S=True, want_q=True)
+                         mode=mode, temperature=T, uniforms=d["uniforms"], want_S=True, want_q=True,
+                         want_AB=want_AB)
     torch.cuda.synchronize()
     assert ds.device_error() == 0
     return {k: v.cpu().numpy() for k, v in res.items()}
@@ -129,8 +130,8 @@ def test_tie_heavy_stress(ora, dev):
 
 def test_pipeline_is_deterministic(dev):
     inp = _workload("c2")
-    a = _run(inp, dev, 0)
-    b = _run(inp, dev, 0)
+    a = _run(inp, dev, 0, want_AB=True)
+    b = _run(inp, dev, 0, want_AB=True)
     for k in ("cand_id", "path_slot", "path_tok"):
         assert np.array_equal(a[k], b[k])
     for k in ("S", "A_prev", "B_cur", "G", "q"):

@@ -125,3 +125,17 @@ def test_step_table_reproduces_walk(ora):
 def test_bad_temperature_is_rejected(ora):
     with pytest.raises(ValueError):
         ora.step(np.zeros((K, K)), 0, 1, 0.5, 0.0)
+
+
+def test_time_selector_runs_the_stages_of_run(ora):
+    """The timed whole-selector entry (the benchmark's CPU baseline) calls the
+    same stages in the same order: its path equals run()'s, in both modes."""
+    import synth
+
+    cfg = synth.CONFIGS["c0"]
+    inp = synth.make(cfg, seed=4)
+    for mode in (0, 1):
+        slot, sec, threads = ora.time_selector(inp, mode, 1.0)
+        assert np.array_equal(slot, ora.run(inp, mode, 1.0)["path_slot"])
+        assert set(sec) == {"select_topk", "project", "score_pairs", "walk"} and all(v >= 0 for v in sec.values())
+        assert threads >= 1
