@@ -91,6 +91,7 @@ def _load():
             "dsel_gather_probe_words": ([I64, I64, I64], SZ),
             "dsel_gather_probe": ([P, I64, I64, P, I64, I64, P, SZ, P], I32),
             "dsel_select_path": ([C.POINTER(PathArgs), C.POINTER(WalkArgs), P, SZ, P], I32),
+            "dsel_select_path_noalloc": ([C.POINTER(PathArgs), C.POINTER(WalkArgs), P], I32),
             "dsel_pair_groups": ([I64], I64),
             "dsel_project_pairs": ([P, I64, I64, P, P, I64, P, P, P, I64, I64, I64, P, P, P, P, P], I32),
             "dsel_walk_pairs": ([P, P, I64, I64, P, I64, P, C.POINTER(WalkArgs), P], I32),

@@ -6,6 +6,8 @@
 
 #include <limits.h>
 
+#include <mutex>
+
 #include "dsel.h"
 #include "common.h"
 #include "conv.h"
@@ -744,6 +746,57 @@ DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_a
     if (st == DSEL_OK) st = launch_cand(c, stream);
     if (st == DSEL_OK) st = launch_pairs(q, stream);
     return st;
+}
+
+// ---- the whole selector without a caller workspace ---------------------------
+
+namespace {
+
+// The workspace of dsel_select_path_noalloc: one array per device, which the
+// HIP runtime places when the library's code is loaded on that device and
+// keeps until the process ends.  Host code never passes `scratch` itself to a
+// kernel (its name is a host-side stand-in, not the device address); it uses
+// the address hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = (size_t)DSEL_NOALLOC_MAX_WORKSPACE;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+dsel_status scratch_for_current_device(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return DSEL_E_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DSEL_E_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSEL_OK;
+}
+
+}  // namespace
+
+DSEL_API dsel_status dsel_select_path_noalloc(const dsel_path_args *a, const dsel_walk_args *walk,
+                                              dsel_stream_t stream) {
+    if (!a || !walk) return DSEL_E_ARG;
+    if (a->batch < 0 || a->block < 1 || a->block > DSEL_MAX_BLOCK || a->batch > (int64_t)INT_MAX / a->block)
+        return DSEL_E_ARG;
+    size_t need = 0;
+    if (a->batch > 0) {
+        PathLayout l;
+        if (!path_layout(a->batch, a->block, a->vocab, a->dt, a->d, a->r, &l)) return DSEL_E_ARG;
+        need = l.total;
+        if (need > kScratchBytes) return DSEL_E_WORKSPACE;  // beyond the fixed scratch array
+    }
+    void *ws = nullptr;
+    if (need) {
+        dsel_status st = scratch_for_current_device(&ws);
+        if (st != DSEL_OK) return st;
+    }
+    return dsel_select_path(a, walk, ws, need ? kScratchBytes : 0, stream);
 }
 
 DSEL_API dsel_status dsel_device_error(int32_t *out_code, dsel_stream_t stream) {

@@ -303,6 +303,23 @@ size_t dsel_select_path_workspace_bytes(int64_t batch, int64_t block, int64_t vo
 dsel_status dsel_select_path(const dsel_path_args *args, const dsel_walk_args *walk, void *workspace,
                              size_t workspace_bytes, dsel_stream_t stream);
 
+/* select_path_noalloc -- dsel_select_path for callers that cannot allocate
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and outputs bit for bit, without a caller
+ * workspace.  Its workspace is a fixed device array of the library, one per
+ * device (DSEL_NOALLOC_MAX_WORKSPACE bytes, 48 MiB: enough for 256 blocks of
+ * 16 positions at vocab 202,048, d 6,144, r 256, which need 33 MiB), looked
+ * up on the device that is current at the call.  The call allocates nothing.
+ * A shape whose dsel_select_path_workspace_bytes() exceeds the array returns
+ * DSEL_E_WORKSPACE before anything is launched.  Every call on one device
+ * shares that device's array: calls that overlap on one device (two streams,
+ * two threads) race and must not be issued; calls in one stream are ordered.
+ * Nothing in the array needs to start at zero.  Returns DSEL_E_HIP when the
+ * array's address cannot be looked up. */
+#define DSEL_NOALLOC_MAX_WORKSPACE (48u << 20)
+dsel_status dsel_select_path_noalloc(const dsel_path_args *args, const dsel_walk_args *walk,
+                                     dsel_stream_t stream);
+
 /* gather_probe -- a measurement aid, not a step of the path: the gather of
  * dsel_project_cand alone.  Rows E[cand_id[m]] (m over batch*block*16) are
  * moved into LDS with the same LDS-DMA addressing as the candidate GEMM, with
