@@ -1,7 +1,7 @@
 // dyn_conv: the dynamic two-tap short convolution of the drafter.
 // ("DFlash 2: Keep Drafting Parallel", Method > Lightweight Local Convolution,
-// eq. Conv_k; "DFlash 2: The Drafter Stopped Guessing Alone", "Suffix decay is
-// local".)  Over the positions of each drafted block,
+// eq. Conv_k; "DFlash 2: The Drafter Stopped Guessing Alone", section "The decay
+// at the end of the block".)  Over the positions of each drafted block,
 //     y_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1},
 //     k_{t,j}[c] = base[j][c] + corr_t[j G + c / 16],  corr_t = W_c x_t,
 // G = d / 16 correction groups per tap; position 0 reads the last verified

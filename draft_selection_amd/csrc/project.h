@@ -113,7 +113,7 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // Schedule of one step kt: the wave waits for its own LDS reads of step kt
 // (issued one step earlier) and its own DMA of step kt+1, then meets the
 // others at the barrier: after it nobody reads step kt's stage any more and
-// step kt+1 is complete in LDS.  It refills kt's stage with step kt+3, issues
+// step kt+1 is complete in LDS.  It refills kt's stage with step kt+NS, issues
 // all fragment reads of step kt+1 (KS x (TM + TN) ds_read_b128, into the other
 // register set) and runs the MFMAs of step kt from registers while they fly.
 // Keeping a whole step of reads in flight is what lets LDS reach its streaming
@@ -129,14 +129,15 @@ __device__ __forceinline__ int dma_chunk_elems(int row) {
     return (((int)(lane_id() & 7)) ^ ((row >> 1) & 7)) << 3;
 }
 
-template <class T>
+template <class T, int NS = 3>
 __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T::DXI],
                                                  const uint16_t *const (&wsrc)[T::DWI], int k0, int k1,
                                                  uint16_t *Xs, uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN]);
 
 // W rows from one row-major matrix (row stride wstride); tile rows at or past
-// `wrows` re-read row wrows - 1.
-template <class T>
+// `wrows` re-read row wrows - 1.  NS: stages of the LDS ring (Xs and Ws hold
+// NS steps each).
+template <class T, int NS = 3>
 __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DXI], const uint16_t *wbase,
                                              int64_t wstride, int k0, int k1, uint16_t *Xs,
                                              uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN],
@@ -148,12 +149,14 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
         const int srow = row < wrows ? row : wrows - 1;
         wsrc[u] = wbase + (int64_t)srow * wstride + dma_chunk_elems(row);
     }
-    mma_tile_dma_src<T>(xsrc, wsrc, k0, k1, Xs, Ws, acc);
+    mma_tile_dma_src<T, NS>(xsrc, wsrc, k0, k1, Xs, Ws, acc);
 }
 
 // The main loop proper: xsrc / wsrc are the lane's DMA sources at K = 0 (row
-// pointer plus its swizzled chunk offset).
-template <class T>
+// pointer plus its swizzled chunk offset).  The ring has NS stages, so the DMA
+// of a step goes out NS - 1 steps ahead of its MFMAs: more stages hide more
+// latency where a step has little MFMA work (small column tiles).
+template <class T, int NS>
 __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T::DXI],
                                                  const uint16_t *const (&wsrc)[T::DWI], int k0, int k1,
                                                  uint16_t *Xs, uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN]) {
@@ -161,7 +164,7 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
     constexpr int XI = T::DXI, WI = T::DWI;
     static_assert(XI >= 1 && WI >= 1 && XI * NW * 8 == BM && WI * NW * 8 == BN, "DMA tile shape");
     constexpr int PER = XI + WI;  // loads per wave per step
-    constexpr int NS = 3;
+    static_assert(NS >= 3 && (NS - 1) * PER < 64, "ring depth");
     constexpr int KS = kBK / 16;  // 16-deep slices per step
     const uint32_t lane = lane_id();
     // wave-uniform, so the LDS-DMA destinations below are scalar arithmetic
@@ -206,7 +209,8 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
     // with the fragment reads of kt+1 (from the next stage) interleaved one or
     // two per MFMA, so the matrix pipe starts at once and LDS serves a steady
     // stream rather than a burst from every wave right after the barrier; the
-    // DMA of kt+3 into kt's stage goes out one load per MFMA from the first.
+    // DMA of kt+NS into kt's stage goes out one load per MFMA from MFMA
+    // DSEL_MMA_DMA_AT on.
     // (Past the last step the reads fetch a stale stage into the unused set:
     // in bounds and harmless.)
     // fragment read rr of a step: slice rr / (TM + TN), then its A fragments
@@ -222,12 +226,12 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
     int cur = 0;
     auto step = [&](int kt, auto setc) {
         constexpr int SET = decltype(setc)::value;
-        wait_vmcnt_lgkm0<PER>();  // own reads of kt done, own DMA of kt+1 landed
+        wait_vmcnt_lgkm0<(NS - 2) * PER>();  // own reads of kt done, own DMA of kt+1 landed
         wg_barrier();             // everyone's: kt's stage is free, kt+1 is complete
         __builtin_amdgcn_sched_barrier(0);
         const int nxt = cur == NS - 1 ? 0 : cur + 1;
         const uint16_t *xb = Xs + nxt * BM * kBK, *wb = Ws + nxt * BN * kBK;
-        const int kk = (kt + 3 < k1 ? kt + 3 : k1 - 1) * kBK;
+        const int kk = (kt + NS < k1 ? kt + NS : k1 - 1) * kBK;
         constexpr int NMF = KS * T::TM * T::TN;
 #pragma unroll
         for (int s_ = 0; s_ < KS; ++s_) {
@@ -252,10 +256,9 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
             if (q >= DSEL_MMA_DMA_AT) dma(q - DSEL_MMA_DMA_AT, kk, cur);
         cur = nxt;
     };
-    DSEL_ISSUE(k0, 0);
-    DSEL_ISSUE(k0 + 1, 1);
-    DSEL_ISSUE(k0 + 2, 2);
-    wait_vmcnt<2 * PER>();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) DSEL_ISSUE(k0 + st, st);
+    wait_vmcnt<(NS - 1) * PER>();
     wg_barrier();
     DSEL_READ_STEP(0, 0);
     // Steps in pairs (register sets 0 then 1), then an odd last step in set 0.
@@ -735,6 +738,10 @@ inline size_t cand_workspace_bytes(int64_t batch, int64_t block, int64_t d, int6
     return s > 1 ? (size_t)s * (size_t)mt * 128 * 2 * (size_t)r * sizeof(float) : 0;
 }
 
+#ifndef DSEL_GATE_STAGES
+#define DSEL_GATE_STAGES 3
+#endif
+
 struct GateParams {
     const uint16_t *E;
     int64_t V;
@@ -761,14 +768,21 @@ struct GateParams {
 // small GEMM (M = batch*block) still fills the chip.  With nsplit == 1 the
 // epilogue is applied here; otherwise the partial tile is stored and
 // project_gate_reduce_kernel sums the splits in a fixed order.
+// Stages of the gate GEMM's LDS ring.  Deeper rings (4 and 6 stages for the
+// narrow tiles, 4 for the 128-wide ones) measured the same at 64-256 blocks
+// and within noise at one block, so the default stays at three.
+template <int BN>
+constexpr int gate_stages() { return BN >= 256 ? 3 : DSEL_GATE_STAGES; }
+
 template <int BN>
 __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GateParams p) {
     constexpr int BM = 128;
     using T = CandTile<BN>;
     constexpr int NW = T::NW;
     constexpr int XI = T::DXI;
-    __shared__ __attribute__((aligned(16))) uint16_t Xs[3 * BM * kBK];
-    __shared__ __attribute__((aligned(16))) uint16_t Ws[3 * BN * kBK];
+    constexpr int NSG = gate_stages<BN>();
+    __shared__ __attribute__((aligned(16))) uint16_t Xs[NSG * BM * kBK];
+    __shared__ __attribute__((aligned(16))) uint16_t Ws[NSG * BN * kBK];
 
     const int tiles = (p.mt_gate + p.mt_ver) * p.nside;
     const int ks = blockIdx.x / tiles;
@@ -821,7 +835,7 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    if (k1 > k0) mma_tile_dma<T>(xsrc, W, d, k0, k1, Xs, Ws, acc);
+    if (k1 > k0) mma_tile_dma<T, NSG>(xsrc, W, d, k0, k1, Xs, Ws, acc);
 
     tile_row_mask<NW, XI>(xok, Xs, xlive);
     const int64_t rows_all = (int64_t)p.B * p.L + p.B;

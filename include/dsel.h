@@ -403,7 +403,7 @@ dsel_status dsel_lmhead_topk(const uint16_t *h, const uint16_t *W, int64_t rows,
                              dsel_stream_t stream);
 
 /* dyn_conv -- [P1] Method > Lightweight Local Convolution (eq. Conv_k), [P3]
- * "Suffix decay is local": the drafter's dynamic two-tap short convolution
+ * section "The decay at the end of the block": the drafter's dynamic two-tap short convolution
  * over the positions of each drafted block,
  *     y_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1},
  *     k_{t,j}[c] = base[j][c] + corr_t[j d/16 + c/16],  corr_t = W_c x_t,

@@ -123,7 +123,7 @@ int ora_verify_draw(const void *tlogits, int dtype, int64_t B, int64_t L, int64_
                     int64_t b, int64_t t, int residual, int32_t *tok, double *margin);
 
 /* Dynamic two-tap short convolution ([P1] Method > Lightweight Local
- * Convolution, eq. Conv_k; [P3] "Suffix decay is local"): a depthwise
+ * Convolution, eq. Conv_k; [P3] section "The decay at the end of the block"): a depthwise
  * convolution over the positions of each drafted block that reaches one
  * position back,
  *     y_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1},

@@ -4,7 +4,7 @@
 eq. Conv_k: y_t = k_{t,0} (.) x_t + k_{t,1} (.) x_{t-1}, every coefficient a
 learned base kernel plus a correction from the current hidden state shared by
 16 channels, the first position reading the last verified token; "DFlash 2:
-The Drafter Stopped Guessing Alone", "Suffix decay is local".)
+The Drafter Stopped Guessing Alone", section "The decay at the end of the block".)
 
 The pages print no worked example.  The form of the correction map is pinned by
 the published parameter count (golden file); the arithmetic by a library
