@@ -400,8 +400,8 @@ int ora_verify(const void *tlogits, int dtype, int64_t B, int64_t L, int64_t V, 
 }
 
 /* ------------------------------------------------- dynamic short conv --- */
-/* [P1 Method > Lightweight Local Convolution, eq. Conv_k; P3 "Suffix decay is
- * local"]: y_t = k_{t,0} x_t + k_{t,1} x_{t-1}, each coefficient the base
+/* [P1 Method > Lightweight Local Convolution, eq. Conv_k; P3 section "The decay
+ * at the end of the block"]: y_t = k_{t,0} x_t + k_{t,1} x_{t-1}, each coefficient the base
  * kernel plus the correction of its 16-channel group, computed from x_t; the
  * block's first position reads the last verified token. */
 int ora_dyn_conv(const uint16_t *x, const uint16_t *x_prev, const uint16_t *base, const uint16_t *W_c,

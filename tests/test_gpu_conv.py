@@ -1,8 +1,8 @@
 """dyn_conv on the GPU against the oracle.
 
 ("DFlash 2: Keep Drafting Parallel", Method > Lightweight Local Convolution,
-eq. Conv_k; "DFlash 2: The Drafter Stopped Guessing Alone", "Suffix decay is
-local".)
+eq. Conv_k; "DFlash 2: The Drafter Stopped Guessing Alone", section "The decay
+at the end of the block".)
 
 Tolerance, derived from the arithmetic.  The GPU forms each correction as an
 fp32 sum of exact bf16 x bf16 products, so it is within gamma_d * sum |w x|
