@@ -203,4 +203,54 @@ __device__ __forceinline__ bool position_live(const int32_t *len, uint32_t i, in
     return (int)(i - b * (uint32_t)L) < block_len_of(len, b, L);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+    const uint32_t lane = lane_id();
+#pragma unroll
+    for (uint32_t o = 1; o < 64; o <<= 1) {
+        const int y = (int)shfl_idx32((uint32_t)x, lane >= o ? lane - o : lane);
+        if (lane >= o) x += y;
+    }
+    return x;
+}
+
+// Compaction of a ragged batch: the flat index b L + t of its w-th real
+// position (flat order), or -1 when it has no more than w.  For a uniform
+// batch (len == nullptr) that is w itself while w < B L.  Called by a whole
+// wave with a wave-uniform w; two rounds of loads and a wave scan (lane k
+// first sums the lengths of blocks [k c, k c + c), c = ceil(B / 64), then the
+// blocks of the one lane range that holds position w are scanned).  Lets a
+// kernel launched for the padded batch put the real positions on its first
+// workgroups, so they spread evenly over the chip and the rest exit at once.
+__device__ __forceinline__ int64_t live_position(const int32_t *len, int64_t B, int L, int64_t w) {
+    if (len == nullptr) return w < B * L ? w : -1;
+    const uint32_t lane = lane_id();
+    const int64_t c = (B + 63) / 64;
+    int s = 0;
+    for (int64_t k = 0; k < c; ++k) {
+        const int64_t b = (int64_t)lane * c + k;
+        if (b < B) s += block_len_of(len, b, L);
+    }
+    const int incl = wave_incl_scan(s);
+    const uint64_t m = ballot((int64_t)incl > w);
+    if (m == 0) return -1;
+    const uint32_t j = (uint32_t)__builtin_ctzll(m);
+    int64_t base = (int64_t)__builtin_amdgcn_readlane(incl - s, (int)j);  // positions before lane j's blocks
+    const int64_t b0 = (int64_t)j * c;
+    if (c == 1) return b0 * L + (w - base);
+    for (int64_t k0 = 0; k0 < c; k0 += 64) {
+        const int64_t k = k0 + lane, b = b0 + k;
+        const int n = (k < c && b < B) ? block_len_of(len, b, L) : 0;
+        const int inc2 = wave_incl_scan(n);
+        const uint64_t m2 = ballot(base + inc2 > w);
+        if (m2) {
+            const uint32_t i = (uint32_t)__builtin_ctzll(m2);
+            const int64_t before = base + __builtin_amdgcn_readlane(inc2 - n, (int)i);
+            return (b0 + k0 + i) * L + (w - before);
+        }
+        base += __builtin_amdgcn_readlane(inc2, 63);
+    }
+    return -1;  // not reached: lane j's blocks hold position w
+}
+
 }  // namespace dsel

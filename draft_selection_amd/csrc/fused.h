@@ -25,6 +25,10 @@
 //
 // Workgroup order is XCD-aware: the nq groups of one tile run on one XCD, so
 // its gathered rows come from HBM once and from that XCD's L2 afterwards.
+//
+// A uniform batch puts floor(16 / L) consecutive blocks in a tile.  A ragged
+// batch packs its blocks by their real lengths (packed_tile), so that the
+// grid's first tiles hold all the work and the padding costs no MFMA time.
 #pragma once
 
 #include "pairwalk.h"
@@ -44,6 +48,69 @@ __host__ __device__ constexpr int pair_group_width(int r) { return (r % 64 == 0 
 template <int CW>
 using FusedTile = TileShape<256, 2 * CW, DSEL_FUSED_GM, 2>;
 
+// Tiles of a ragged batch, by harmonic bin packing (C. C. Lee and D. T. Lee,
+// "A simple on-line bin-packing algorithm", J. ACM 32(3), 1985): a block with
+// n >= 1 real positions has class c = floor(16 / n) and shares its tile with
+// up to c - 1 other blocks of that class; slot k of the tile takes the local
+// positions [k S, k S + n) with S = floor(16 / c) >= n.  Tiles are numbered
+// class by class (c = 1, 2, 3, 4, 5, 8, 16), a class's blocks in index order;
+// empty blocks take no slot.  There are at most floor(B / nb) + 7 tiles when
+// every block has at most L positions (nb = floor(16 / L) <= c).  Called by a
+// whole wave (wave-uniform result): one pass over the lengths for the class
+// sizes, one to collect the tile's blocks.
+struct TileBlocks {
+    int S;      // local positions per slot
+    int nslot;  // blocks in the tile (0: no such tile)
+    int blk;    // lane k < nslot: the block of slot k (other lanes: -1)
+};
+
+__device__ __forceinline__ TileBlocks packed_tile(const int32_t *len, int B, int L, int tile) {
+    constexpr int NC = 7;
+    constexpr int C[NC] = {1, 2, 3, 4, 5, 8, 16};
+    const uint32_t lane = lane_id();
+    const uint64_t below = (1ull << lane) - 1ull;  // lanes under this one
+    int cnt[NC];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) cnt[i] = 0;
+    for (int b0 = 0; b0 < B; b0 += kWave) {
+        const int b = b0 + (int)lane;
+        const int n = b < B ? block_len_of(len, b, L) : 0;
+        const int c = n > 0 ? 16 / n : 0;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) cnt[i] += __popcll(ballot(c == C[i]));
+    }
+    TileBlocks t{1, 0, -1};
+    int cc = 0, first = 0, base = 0;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int nt = (cnt[i] + C[i] - 1) / C[i];
+        if (cc == 0 && tile < base + nt) {
+            cc = C[i];
+            first = (tile - base) * C[i];
+            t.nslot = cnt[i] - first < C[i] ? cnt[i] - first : C[i];
+        }
+        base += nt;
+    }
+    if (cc == 0) return t;
+    t.S = 16 / cc;
+    int r0 = 0;
+    for (int b0 = 0; b0 < B && r0 < first + t.nslot; b0 += kWave) {
+        const int b = b0 + (int)lane;
+        const int n = b < B ? block_len_of(len, b, L) : 0;
+        const bool mine = n > 0 && 16 / n == cc;
+        const uint64_t m = ballot(mine);
+        const int rank = r0 + __popcll(m & below);
+        uint64_t hit = ballot(mine && rank >= first && rank < first + t.nslot);
+        while (hit) {
+            const int src = __builtin_ctzll(hit);
+            hit &= hit - 1;
+            if ((int)lane == __builtin_amdgcn_readlane(rank, src) - first) t.blk = b0 + src;
+        }
+        r0 += __popcll(m);
+    }
+    return t;
+}
+
 struct FusedParams {
     const uint16_t *E;
     int64_t V;
@@ -55,8 +122,8 @@ struct FusedParams {
     int64_t ver_stride;
     int B, L;
     const int32_t *len;     // ragged batch: valid positions per block (nullptr: all L)
-    int nb;                 // blocks per tile (16 / L)
-    int ntile;              // row tiles (ceil(B / nb))
+    int nb;                 // blocks per tile of a uniform batch (16 / L)
+    int ntile;              // row tiles of the grid (ceil(B / nb), + 7 for a ragged batch)
     int nq;                 // column groups (r / CW)
     float *P;               // [B * L][nq][16][16] partial pair tables
     float *A_prev, *B_cur;  // optional [B * L * 16][r] (nullptr: not written)
@@ -76,6 +143,7 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
     // column group, staged before the main loop so their latency hides there
     __shared__ __attribute__((aligned(16))) float Gs[16][CW];
     __shared__ __attribute__((aligned(16))) float Vs[16][CW];
+    __shared__ int gposs[16];  // flat position of each local position (-1: none)
     uint16_t *const Xs = smem;
     uint16_t *const Ws = smem + 3 * BM * kBK;
 
@@ -90,28 +158,41 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
     const uint32_t lane = lane_id();
     const int wave = (int)(threadIdx.x >> 6);
     const int L = p.L, d = p.d, r = p.r;
-    const int b0 = tile * p.nb;
-    const int npos = p.nb * L;  // positions the tile can hold (<= 16)
 
-    // bit pp of validq: local position pp (flat position b0 L + pp) is a real
-    // one; of succq: it also has a successor in its block.  Same in every wave.
+    // The tile's blocks: slot k holds block `blk` of lane k and local positions
+    // [k S, k S + S).  Same in every wave.
+    TileBlocks tb;
+    if (p.len == nullptr) {
+        tb.S = L;
+        tb.nslot = p.B - tile * p.nb < p.nb ? p.B - tile * p.nb : p.nb;
+        tb.blk = (int)lane < tb.nslot ? tile * p.nb + (int)lane : -1;
+    } else {
+        tb = packed_tile(p.len, p.B, L, tile);
+    }
+    if (tb.nslot <= 0) return;  // no such tile (workgroup-uniform, before any barrier)
+    const int S = tb.S;
+
+    // Lane pp < 16: flat position gp of local position pp (slot k, step t).
+    // Bit pp of validq: it is a real position; of succq: it also has a
+    // successor in its block.
     uint32_t validq, succq;
+    int gp = -1;
     {
+        const int k = (int)(lane & 15) / S, t = (int)(lane & 15) - k * S;
+        const int bk = (int)shfl_idx32((uint32_t)tb.blk, (uint32_t)k);
         bool v = false, sc = false;
-        if ((int)lane < npos) {
-            const int b = b0 + (int)lane / L, t = (int)lane % L;
-            if (b < p.B) {
-                const int n = block_len_of(p.len, b, L);
-                v = t < n;
-                sc = t + 1 < n;
-            }
+        if (lane < 16u && k < tb.nslot) {
+            const int n = block_len_of(p.len, bk, L);
+            v = t < n;
+            sc = t + 1 < n;
+            gp = bk * L + t;
         }
         validq = (uint32_t)ballot(v);
         succq = (uint32_t)ballot(sc);
     }
     if (validq == 0) return;  // padding only (workgroup-uniform, before any barrier)
+    if (wave == 0 && lane < 16u) gposs[lane] = (validq >> lane) & 1u ? gp : -1;  // the main loop's barriers publish it
 
-    const int64_t row0 = (int64_t)b0 * L * kK;  // the tile's first candidate row
     // Gathered rows: padding positions and out-of-range ids load E row 0; the
     // latter become zero rows.
     const uint16_t *xsrc[XI];
@@ -119,9 +200,10 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
 #pragma unroll
     for (int u = 0; u < XI; ++u) {
         const int row = dma_row<T>(u);
+        const int gpr = (int)shfl_idx32((uint32_t)gp, (uint32_t)(row >> 4));
         int64_t tok = 0;
         if ((validq >> (row >> 4)) & 1u) {
-            const int32_t t = p.cand[row0 + row];
+            const int32_t t = p.cand[(int64_t)gpr * kK + (row & 15)];
             if (t >= 0 && (int64_t)t < p.V) {
                 tok = t;
                 xok |= 1u << u;
@@ -142,16 +224,18 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
 
     // This thread's share of the epilogue's small operands, loaded now (their
     // latency overlaps the main loop's first DMA steps) and put in LDS after
-    // it: float4 e of G[b0 L + pp][q CW ..] (pp = e / (CW / 4)) for real
-    // positions, and of A(verified of block b0 + pp) for the tile's real blocks.
+    // it: float4 e of G[gp(pp)][q CW ..] (pp = e / (CW / 4)) for real
+    // positions, and of A(verified of the block of slot pp) for its real slots.
     constexpr int NV4 = 16 * CW / 4;  // float4s of a 16 x CW table
     static_assert(NV4 <= T::NT, "one float4 per thread");
     const int e4 = (int)threadIdx.x, epp = e4 / (CW / 4), ec = (e4 % (CW / 4)) * 4;
+    const int gpe = (int)shfl_idx32((uint32_t)gp, (uint32_t)(epp & 15));
+    const int vbk = (int)shfl_idx32((uint32_t)tb.blk, (uint32_t)(epp & 15));
     const bool gload = e4 < NV4 && ((validq >> epp) & 1u);
-    const bool vload = e4 < NV4 && epp < p.nb && ((validq >> (epp * L)) & 1u);
+    const bool vload = e4 < NV4 && epp < tb.nslot && ((validq >> (epp * S)) & 1u);
     float4 gv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-    if (gload) gv = *(const float4 *)(p.G + ((int64_t)b0 * L + epp) * r + q * CW + ec);
-    if (vload) vv = *(const float4 *)(p.A_ver + (int64_t)(b0 + epp) * p.ver_stride + q * CW + ec);
+    if (gload) gv = *(const float4 *)(p.G + (int64_t)gpe * r + q * CW + ec);
+    if (vload) vv = *(const float4 *)(p.A_ver + (int64_t)vbk * p.ver_stride + q * CW + ec);
 
     // Id-validity bits of the 256 rows (word k: rows 32 k .. 32 k + 31); the
     // main loop's barriers publish them
@@ -185,11 +269,12 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
     // side A becomes predecessor row of position t + 1 (output row m + 16),
     // written only where that position exists; side B for every real position.
     if (p.A_prev != nullptr) {
-        float *const out = wn == 0 ? p.A_prev + (row0 + kK) * r : p.B_cur + row0 * r;
+        float *const out = wn == 0 ? p.A_prev + kK * r : p.B_cur;
         const uint32_t wq = wn == 0 ? succq : validq;
         for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) {
             if (!((wq >> (rl >> 4)) & 1u)) return;
-            *(floatx4 *)(out + (int64_t)rl * r + cq + (cl - wn * CW)) =
+            const int64_t grow = (int64_t)gposs[rl >> 4] * kK + (rl & 15);
+            *(floatx4 *)(out + grow * r + cq + (cl - wn * CW)) =
                 row_ok(rl) ? v : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         });
     }
@@ -230,16 +315,16 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
 #pragma unroll
     for (int pr = 0; pr < 16 / (2 * NW); ++pr) {
         int pps[2];
-        const float *ap[2], *bp[2], *gp[2];
+        const float *ap[2], *bp[2], *gsp[2];
         bool arow[2];
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             const int pp = wave + NW * (2 * pr + k);
-            const int t = pp % L;
+            const int t = pp % S;
             pps[k] = pp;
-            gp[k] = &Gs[pp][4 * fg];
+            gsp[k] = &Gs[pp][4 * fg];
             bp[k] = Bs + (kK * pp + fr) * SROW + 4 * fg;
-            ap[k] = t > 0 ? As + (kK * (pp - 1) + fr) * SROW + 4 * fg : &Vs[pp < p.nb * L ? pp / L : 0][4 * fg];
+            ap[k] = t > 0 ? As + (kK * (pp - 1) + fr) * SROW + 4 * fg : &Vs[pp < tb.nslot * S ? pp / S : 0][4 * fg];
             arow[k] = t > 0 || fr == 0;  // position 0 has one predecessor row
         }
         if (!((validq >> pps[0]) & 1u) && !((validq >> pps[1]) & 1u)) continue;  // wave-uniform
@@ -250,7 +335,7 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const float4 a = arow[k] ? *(const float4 *)(ap[k] + 16 * s) : float4{0.f, 0.f, 0.f, 0.f};
-                const float4 g = *(const float4 *)(gp[k] + 16 * s);
+                const float4 g = *(const float4 *)(gsp[k] + 16 * s);
                 b[k] = *(const float4 *)(bp[k] + 16 * s);
                 ag[k] = float4{a.x * g.x, a.y * g.y, a.z * g.z, a.w * g.w};
             }
@@ -266,7 +351,7 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
             if (!((validq >> pps[k]) & 1u)) continue;
-            float *Pp = p.P + (((int64_t)b0 * L + pps[k]) * p.nq + q) * (kK * kK) + fr;
+            float *Pp = p.P + ((int64_t)gposs[pps[k]] * p.nq + q) * (kK * kK) + fr;
 #pragma unroll
             for (int v = 0; v < 4; ++v) Pp[(4 * fg + v) * kK] = pacc[k][v];
         }
@@ -279,8 +364,13 @@ inline int64_t fused_tiles(int64_t batch, int64_t block) {
     const int nb = fused_blocks_per_tile(block);
     return nb ? (batch + nb - 1) / nb : 0;
 }
-inline int64_t fused_grid(int64_t batch, int64_t block, int64_t r) {
+// Tiles of the grid: a ragged batch can need up to 7 more (packed_tile).
+inline int64_t fused_grid_tiles(int64_t batch, int64_t block, bool ragged) {
     const int64_t nt = fused_tiles(batch, block);
+    return nt && ragged ? nt + 7 : nt;
+}
+inline int64_t fused_grid(int64_t batch, int64_t block, int64_t r, bool ragged) {
+    const int64_t nt = fused_grid_tiles(batch, block, ragged);
     return (nt + 7) / 8 * 8 * (r / pair_group_width((int)r));
 }
 

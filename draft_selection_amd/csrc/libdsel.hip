@@ -594,19 +594,19 @@ dsel_status plan_fused(const uint16_t *E, int64_t vocab, int64_t d, const uint16
     p.L = (int)block;
     p.len = block_len;
     p.nb = fused_blocks_per_tile(block);
-    p.ntile = (int)fused_tiles(batch, block);
+    p.ntile = (int)fused_grid_tiles(batch, block, block_len != nullptr);
     f->CW = pair_group_width((int)r);
     p.nq = (int)(r / f->CW);
     p.P = P;
     p.A_prev = A_prev;
     p.B_cur = B_cur;
-    if (fused_grid(batch, block, r) >= (int64_t)INT_MAX) return DSEL_E_ARG;
+    if (fused_grid(batch, block, r, block_len != nullptr) >= (int64_t)INT_MAX) return DSEL_E_ARG;
     return DSEL_OK;
 }
 
 dsel_status launch_fused(const FusedPlan &f, dsel_stream_t stream) {
     FusedParams p = f.p;
-    const int64_t grid = fused_grid(p.B, p.L, p.r);
+    const int64_t grid = fused_grid(p.B, p.L, p.r, p.len != nullptr);
     const void *k = f.CW == 64 ? (const void *)project_pair_kernel<64> : (const void *)project_pair_kernel<32>;
     return launch(k, dim3((unsigned)grid), dim3(f.CW == 64 ? FusedTile<64>::NT : FusedTile<32>::NT), &p, 0, stream);
 }

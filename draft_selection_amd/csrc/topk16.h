@@ -14,6 +14,8 @@
 // registers, so a chunk's HBM latency hides behind the previous chunks'
 // filters.  Waves merge through LDS with a 64-key bitonic sort (DPP and
 // permlane swaps); split rows merge in a second kernel, one workgroup per row.
+// On a ragged batch the real rows are compacted onto the first workgroups of
+// the padded grid (live_position), so that they spread evenly over the chip.
 #pragma once
 
 #include "common.h"
@@ -243,9 +245,11 @@ template <bool BF16, int U>
 __device__ __forceinline__ void topk16_block(const TopkParams &p, int64_t bid) {
     constexpr int ES = BF16 ? 2 : 4;
     constexpr int EPV = 16 / ES;
-    const int64_t row = bid / p.nsplit;
+    // a ragged batch's real rows go to the first workgroups (compaction), so
+    // they spread evenly over the XCDs and the rest exit at once
+    const int64_t row = p.len ? live_position(p.len, p.rows / p.L, p.L, bid / p.nsplit) : bid / p.nsplit;
     const int split = (int)(bid % p.nsplit);
-    if (!position_live(p.len, (uint32_t)row, p.L)) return;  // padding row (ragged batches)
+    if (row < 0) return;  // past the last real row (ragged batches)
     const int wave = (int)(threadIdx.x / kWave);
     const uint32_t lane = lane_id();
     const char *rowp = p.logits + row * p.ld * ES;
@@ -371,8 +375,8 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk16_kernel(TopkParams p) {
 template <bool BF16>
 __global__ __launch_bounds__(256) void topk16_merge_kernel(TopkParams p) {
     constexpr int ES = BF16 ? 2 : 4;
-    const int64_t row = blockIdx.x;
-    if (!position_live(p.len, (uint32_t)row, p.L)) return;  // padding row (ragged batches)
+    const int64_t row = p.len ? live_position(p.len, p.rows / p.L, p.L, blockIdx.x) : (int64_t)blockIdx.x;
+    if (row < 0) return;  // past the last real row (ragged batches)
     const uint32_t lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
     const uint64_t *src = p.partial + row * p.nsplit * kK;
