@@ -92,6 +92,7 @@ def _load():
             "dsel_gather_probe": ([P, I64, I64, P, I64, I64, P, SZ, P], I32),
             "dsel_select_path": ([C.POINTER(PathArgs), C.POINTER(WalkArgs), P, SZ, P], I32),
             "dsel_select_path_noalloc": ([C.POINTER(PathArgs), C.POINTER(WalkArgs), P], I32),
+            "dsel_select_path_route": ([C.POINTER(PathArgs)], I32),
             "dsel_pair_groups": ([I64], I64),
             "dsel_project_pairs": ([P, I64, I64, P, P, I64, P, P, P, I64, I64, I64, P, P, P, P, P], I32),
             "dsel_walk_pairs": ([P, P, I64, I64, P, I64, P, C.POINTER(WalkArgs), P], I32),
@@ -650,3 +651,16 @@ def select_path(logits, E, W_A, W_B, W_H, h, verified, mode: int = GREEDY,
     if want_AB:
         res.update(A_prev=A_prev, B_cur=B_cur, G=G)
     return res
+
+
+ROUTE_SEPARATE, ROUTE_FUSED, ROUTE_SMALL = 0, 1, 2
+
+
+def select_path_route(batch: int, block: int, vocab: int, dtype, d: int, r: int, want_AB: bool = False) -> int:
+    """The route dsel_select_path takes for this shape (dsel_select_path_route):
+    ROUTE_FUSED, ROUTE_SMALL or ROUTE_SEPARATE (-1: empty or invalid)."""
+    dt = BF16 if dtype == torch.bfloat16 else F32
+    mark = 16 if want_AB else None  # only whether the outputs are given is read
+    pa = PathArgs(None, dt, vocab, vocab, None, d, None, None, None, r, None, None, batch, block, None, None, None,
+                  mark, mark, mark, None)
+    return int(_load().dsel_select_path_route(C.byref(pa)))

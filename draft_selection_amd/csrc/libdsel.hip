@@ -12,6 +12,7 @@
 #include "common.h"
 #include "conv.h"
 #include "fused.h"
+#include "latency.h"
 #include "lmhead.h"
 #include "pairwalk.h"
 #include "path.h"
@@ -321,6 +322,13 @@ dsel_status plan_cand(const uint16_t *E, int64_t vocab, int64_t d, const uint16_
     p.M = batch * block * kK;
     p.A_prev = A_prev;
     p.B_cur = B_cur;
+    p.tk_part = nullptr;
+    p.tk_nsplit = 0;
+    p.cand_id = nullptr;
+    p.cand_u = nullptr;
+    p.logits = nullptr;
+    p.ld = p.V_logits = 0;
+    p.logits_bf16 = false;
     constexpr int BM = 128;
     c->BN = cand_bn(batch, block, r);
     p.nside = (int)(r / c->BN);
@@ -333,7 +341,7 @@ dsel_status plan_cand(const uint16_t *E, int64_t vocab, int64_t d, const uint16_
     return DSEL_OK;
 }
 
-dsel_status launch_cand(const CandPlan &c, dsel_stream_t stream) {
+dsel_status launch_cand_gemm(const CandPlan &c, dsel_stream_t stream) {
     CandParams p = c.p;
     const int BN = c.BN;
     const int64_t grid = (int64_t)p.mt_pad * 2 * p.nside * p.nsplit;
@@ -341,7 +349,13 @@ dsel_status launch_cand(const CandPlan &c, dsel_stream_t stream) {
                   : BN == 128 ? (const void *)project_cand_kernel<128>
                   : BN == 64  ? (const void *)project_cand_kernel<64>
                               : (const void *)project_cand_kernel<32>;
-    dsel_status st = launch(k, dim3((unsigned)grid), dim3(tile_threads(BN)), &p, 0, stream);
+    return launch(k, dim3((unsigned)grid), dim3(tile_threads(BN)), &p, 0, stream);
+}
+
+dsel_status launch_cand(const CandPlan &c, dsel_stream_t stream) {
+    CandParams p = c.p;
+    const int BN = c.BN;
+    dsel_status st = launch_cand_gemm(c, stream);
     if (st != DSEL_OK || p.nsplit == 1) return st;
     const int64_t elems = p.M * 2 * p.r;
     const void *kr = BN == 256 ? (const void *)project_cand_reduce_kernel<256>
@@ -527,7 +541,7 @@ inline size_t align256(size_t n) { return (n + 255) / 256 * 256; }
 // B_cur [B, L, 16, r] and S [B, L, 16, 16].  The parts for outputs the caller
 // supplies are reserved but unused.
 struct PathLayout {
-    size_t topk = 0, proj = 0, g = 0, aver = 0, part = 0, a = 0, b = 0, s = 0, total = 0;
+    size_t topk = 0, proj = 0, g = 0, aver = 0, part = 0, a = 0, b = 0, s = 0, lat = 0, cnt = 0, total = 0;
     bool fused = false;
 };
 
@@ -556,6 +570,15 @@ bool path_layout(int64_t batch, int64_t block, int64_t vocab, dsel_dtype dt, int
         off += ab;
         l->s = off;
         off += align256((size_t)pos * kK * kK * sizeof(float));
+        // the small-batch route's decision tables (slot, score, distribution
+        // per predecessor row), group tables and arrival counters (per
+        // position, then per block)
+        l->lat = off;
+        off += align256((size_t)pos * kK) + align256((size_t)pos * kK * sizeof(float)) +
+               align256((size_t)pos * kK * kK * sizeof(float)) +
+               align256((size_t)pos * (r / pair_cw((int)r)) * kK * kK * sizeof(float));
+        l->cnt = off;
+        off += align256((size_t)(pos + batch) * sizeof(int));
     }
     l->total = off;
     return true;
@@ -663,6 +686,156 @@ DSEL_API dsel_status dsel_walk_pairs(const float *cand_u, const float *partials,
     return launch_walk(p, stream);
 }
 
+// ---- the small-batch route (latency.h) ----------------------------------------
+
+// Top-16 workgroups beside the gate GEMM's in the first launch: the gate's LDS
+// ring leaves room for two workgroups per CU, 512 in all.
+#ifndef DSEL_LAT_TOPK_WG
+#define DSEL_LAT_TOPK_WG 448
+#endif
+// Partial lists per top-16 row at most (measured at one block of 16, bf16 rows
+// of 151,936: 8, 16 and 24 lists within 1 us of each other, 24 ahead; 4
+// lists 8 us slower).
+#ifndef DSEL_LAT_TOPK_LISTS
+#define DSEL_LAT_TOPK_LISTS 24
+#endif
+// Partial lists per row that the candidate GEMM's merge can stage in its LDS
+// ring (8 positions per tile, 16 keys of 8 bytes per list).
+constexpr int kLatMaxLists = (int)(3 * 128 * kBK * sizeof(uint16_t) / (8 * kK * sizeof(uint64_t)));
+
+struct LatPlan {
+    TopkPlan t;
+    GatePlan g;
+    CandPlan c;
+    LatParams k;
+    int64_t topk_wgs = 0, gate_wgs = 0;
+    bool use = false;
+};
+
+// The small-batch route serves a call of at most DSEL_LAT_MAX_ROWS positions
+// that is not on the fused route and asks for no intermediates (A_prev,
+// B_cur, G), when the gate GEMM is split with column tiles of at most 64 (its
+// LDS ring then leaves room for the top-16 beside it); otherwise lp->use stays
+// false.
+// Workspace: the top-16 lists, the gate and candidate partials (or, from an
+// unsplit candidate GEMM, A_prev and B_cur) where the separate route keeps
+// them; the decision tables and the arrival counters in regions of their own.
+// Positions up to which the small-batch route runs (beyond, the top-16's HBM
+// stream needs more workgroups in flight than the shared launch leaves it).
+#ifndef DSEL_LAT_MAX_ROWS
+#define DSEL_LAT_MAX_ROWS 128
+#endif
+
+bool latency_route(int64_t batch, int64_t block, int64_t d, int64_t r, bool fused, bool intermediates) {
+    return !fused && !intermediates && batch * block <= DSEL_LAT_MAX_ROWS && gate_bn(batch, block, r) <= 64 &&
+           gate_nsplit(batch, block, d, r) > 1;
+}
+
+dsel_status plan_latency(const dsel_path_args *a, const dsel_walk_args *walk, char *ws, const PathLayout &l,
+                         LatPlan *lp) {
+    lp->use = false;
+    if (!latency_route(a->batch, a->block, a->d, a->r, l.fused, a->A_prev || a->G)) return DSEL_OK;
+    const int64_t rows = a->batch * a->block;
+    float *A_buf = (float *)(ws + l.a), *B_buf = (float *)(ws + l.b);  // written by an unsplit candidate GEMM
+    dsel_status st = plan_topk(a->logits, a->dt, a->batch, a->block, a->block_len, a->vocab, a->ld, a->cand_id,
+                               a->cand_u, ws, l.proj, &lp->t);
+    if (st != DSEL_OK) return st;
+    st = plan_gate(a->E, a->vocab, a->d, a->W_A, a->W_H, a->r, a->h, a->verified, a->batch, a->block,
+                   a->block_len, A_buf, A_buf, ws + l.proj, l.g - l.proj, true, &lp->g);
+    if (st != DSEL_OK) return st;
+    st = plan_cand(a->E, a->vocab, a->d, a->W_A, a->W_B, a->r, a->cand_id, a->batch, a->block, a->block_len,
+                   A_buf, B_buf, ws + l.proj, l.g - l.proj, &lp->c);
+    if (st != DSEL_OK) return st;
+    if (lp->g.BN > 64 || lp->g.p.nsplit < 2) return DSEL_OK;
+    if (!a->cand_u || !aligned(a->S, 4)) return !a->cand_u ? DSEL_E_ARG : DSEL_E_ALIGN;
+    const GateParams &gp = lp->g.p;
+    lp->gate_wgs = (int64_t)(gp.mt_gate + gp.mt_ver) * gp.nside * gp.nsplit;
+    TopkParams &tp = lp->t.p;
+    if (tp.nsplit > 1) {
+        int64_t ns = (DSEL_LAT_TOPK_WG - lp->gate_wgs) / rows;
+        if (ns > tp.nsplit) ns = tp.nsplit;
+        if (ns > DSEL_LAT_TOPK_LISTS) ns = DSEL_LAT_TOPK_LISTS;
+        if (ns > kLatMaxLists) ns = kLatMaxLists;
+        tp.nsplit = (int)(ns < 1 ? 1 : ns);
+    }
+    lp->topk_wgs = rows * tp.nsplit;
+    CandParams &cp = lp->c.p;
+    if (tp.nsplit > 1) {  // the candidate GEMM merges the lists itself
+        cp.tk_part = tp.partial;
+        cp.tk_nsplit = tp.nsplit;
+        cp.cand_id = a->cand_id;
+        cp.cand_u = a->cand_u;
+        cp.logits = (const char *)a->logits;
+        cp.ld = a->ld;
+        cp.V_logits = a->vocab;
+        cp.logits_bf16 = a->dt == DSEL_BF16;
+    }
+    LatParams &k = lp->k;
+    k = LatParams{};
+    st = check_walk(walk, &k.pw.w);
+    if (st != DSEL_OK) return st;
+    k.pw.cand_u = a->cand_u;
+    k.pw.B = (int)a->batch;
+    k.pw.L = (int)a->block;
+    k.pw.r = (int)a->r;
+    k.pw.len = a->block_len;
+    k.pw.S = a->S;
+    k.pw.A_prev = A_buf;
+    k.pw.B_cur = B_buf;
+    k.ch = (uint8_t *)(ws + l.lat);
+    k.sc = (float *)(ws + l.lat + align256((size_t)rows * kK));
+    const size_t qoff = l.lat + align256((size_t)rows * kK) + align256((size_t)rows * kK * sizeof(float));
+    k.Q = walk->q ? (float *)(ws + qoff) : nullptr;
+    k.P = (float *)(ws + qoff + align256((size_t)rows * kK * kK * sizeof(float)));
+    k.pw.nq = (int)(a->r / pair_cw((int)a->r));
+    k.cpart = cp.part;
+    k.c_nsplit = cp.nsplit;
+    k.c_mt = cp.mt;
+    k.c_nside = cp.nside;
+    k.c_BN = lp->c.BN;
+    k.gpart = gp.part;
+    k.g_nsplit = gp.nsplit;
+    k.cand = a->cand_id;
+    k.V = a->vocab;
+    k.pos_count = (int *)(ws + l.cnt);
+    k.count = k.pos_count + rows;
+    if (lp->topk_wgs + lp->gate_wgs >= (int64_t)INT_MAX) return DSEL_OK;
+    lp->use = true;
+    return DSEL_OK;
+}
+
+dsel_status launch_latency(LatPlan &lp, dsel_stream_t stream) {
+    TopkParams tp = lp.t.p;
+    GateParams gp = lp.g.p;
+    int64_t tw = lp.topk_wgs;
+    int *count = lp.k.pos_count;  // then the block counters
+    int ncount = lp.k.pw.B * lp.k.pw.L + lp.k.pw.B;
+    const int BN = lp.g.BN;
+    const void *k1 = lp.t.bf16 ? (BN == 64 ? (const void *)topk16_gate_gemm_kernel<true, kTopkUnroll<true>, 64>
+                                           : (const void *)topk16_gate_gemm_kernel<true, kTopkUnroll<true>, 32>)
+                               : (BN == 64 ? (const void *)topk16_gate_gemm_kernel<false, kTopkUnroll<false>, 64>
+                                           : (const void *)topk16_gate_gemm_kernel<false, kTopkUnroll<false>, 32>);
+    void *args[] = {&tp, &gp, &tw, &count, &ncount};
+    if (hipLaunchKernel(k1, dim3((unsigned)(lp.topk_wgs + lp.gate_wgs)), dim3(64 * kTopkWaves), args, 0,
+                        (hipStream_t)stream) != hipSuccess)
+        return DSEL_E_HIP;
+    dsel_status st = launch_cand_gemm(lp.c, stream);
+    if (st != DSEL_OK) return st;
+    LatParams k = lp.k;
+    const int CW = pair_cw(k.pw.r);
+    const void *k3 = CW == 64 ? (const void *)pair_walk_lat_kernel<64> : (const void *)pair_walk_lat_kernel<32>;
+    return launch(k3, dim3((unsigned)((int64_t)k.pw.B * k.pw.L * k.pw.nq)), dim3(CW / 16 * kWave), &k, 0, stream);
+}
+
+DSEL_API int dsel_select_path_route(const dsel_path_args *a) {
+    if (!a) return -1;
+    PathLayout l;
+    if (a->batch <= 0 || !path_layout(a->batch, a->block, a->vocab, a->dt, a->d, a->r, &l)) return -1;
+    if (l.fused) return DSEL_ROUTE_FUSED;
+    return latency_route(a->batch, a->block, a->d, a->r, false, a->A_prev || a->G) ? DSEL_ROUTE_SMALL
+                                                                                      : DSEL_ROUTE_SEPARATE;
+}
+
 DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_args *walk, void *workspace,
                                       size_t workspace_bytes, dsel_stream_t stream) {
     if (!a || !walk) return DSEL_E_ARG;
@@ -721,6 +894,12 @@ DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_a
         if (st == DSEL_OK) st = launch_fused(f, stream);
         if (st == DSEL_OK) st = launch_walk(q.p, stream);
         return st;
+    }
+    {
+        LatPlan lp;
+        st = plan_latency(a, walk, ws, l, &lp);
+        if (st != DSEL_OK) return st;
+        if (lp.use) return launch_latency(lp, stream);
     }
     // the separate kernels: gate GEMM; top-16 with the gate's reduction beside
     // it; candidate GEMM; pair scores and the walk (intermediates the caller

@@ -205,9 +205,10 @@ __global__ __launch_bounds__(256) void pair_kernel(PairParams p) {
     }
 }
 
-// The walk over scores in global memory: one workgroup per block.
-__global__ __launch_bounds__(1024) void walk_kernel(PairParams p) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// The walk of block b over scores in global memory (S_in, or the group
+// partials P) by the whole workgroup, its tables in `smem`
+// (pair_walk_shmem bytes).
+__device__ __forceinline__ void walk_block(const PairParams &p, int b, unsigned char *smem) {
     const int L = p.L;
     const bool want_q = p.w.q != nullptr;
     BlockShared sh;
@@ -216,7 +217,6 @@ __global__ __launch_bounds__(1024) void walk_kernel(PairParams p) {
     sh.row = (int *)(sh.sc + L * kK);
     sh.ch = (uint8_t *)(sh.row + L);
 
-    const int b = blockIdx.x;
     const int n = block_len_of(p.len, b, L);  // positions to walk (ragged batches: the block's own)
     if (n == 0) return;
     const int nwave = blockDim.x / kWave;
@@ -274,6 +274,12 @@ __global__ __launch_bounds__(1024) void walk_kernel(PairParams p) {
         }
         if (want_q) p.w.q[bt * kK + j] = sh.Q[(t * kK + row) * kK + j];
     }
+}
+
+// The walk over scores in global memory: one workgroup per block.
+__global__ __launch_bounds__(1024) void walk_kernel(PairParams p) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    walk_block(p, blockIdx.x, smem);
 }
 
 inline size_t pair_walk_shmem(int L, bool want_q) {

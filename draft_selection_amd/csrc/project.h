@@ -34,6 +34,7 @@
 #include <type_traits>
 
 #include "common.h"
+#include "topk16.h"
 
 namespace dsel {
 
@@ -464,6 +465,18 @@ struct CandParams {
     int nsplit;       // K splits (small batches); > 1: partial tiles go to `part`
     float *part;      // [nsplit][mt * 2 * nside][128][BN] partial tiles
     float *A_prev, *B_cur;
+    // With tk_part set, the candidates are not in `cand` yet: each workgroup
+    // merges the top-16's partial lists [rows][tk_nsplit][16] of its tile's
+    // positions itself, and the workgroups of split 0, column tile 0 write
+    // cand_id / cand_u (cand_u's two merged codes read back from the logits,
+    // bf16 or fp32 rows ld elements apart).
+    const uint64_t *tk_part;
+    int tk_nsplit;
+    int32_t *cand_id;
+    float *cand_u;
+    const char *logits;
+    int64_t ld, V_logits;
+    bool logits_bf16;
 };
 
 // Column tile BN of one side: BN = 256 on 8 waves (2 x 4, wave tile 64 x 64:
@@ -547,6 +560,45 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
     }
     if (validq == 0) return;  // padding only (workgroup-uniform, before any barrier)
 
+    // The merge of the top-16's partial lists: every list of the tile's real
+    // positions goes into LDS at once (the DMA ring is free until the main
+    // loop), then one position per wave at a time is folded from there.
+    __shared__ int32_t mid[BM];
+    if (p.tk_part != nullptr) {
+        const bool owner = ks == 0 && ct == 0;
+        uint64_t *lists = (uint64_t *)Xs;  // [8][tk_nsplit][16]; the planner keeps it within Xs
+        const int per = p.tk_nsplit * kK, all = (BM / kK) * per;
+        // every load in flight before the first LDS write
+        constexpr int EPT = (3 * BM * kBK * 2 / 8 + NW * kWave - 1) / (NW * kWave);  // keys per thread, at most
+        uint64_t v[EPT];
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = tid + u * NW * kWave, pq = e / per;
+            if (e < all && ((validq >> pq) & 1u)) v[u] = p.tk_part[(m0 / kK + pq) * per + (e - pq * per)];
+        }
+#pragma unroll
+        for (int u = 0; u < EPT; ++u) {
+            const int e = tid + u * NW * kWave, pq = e / per;
+            if (e < all && ((validq >> pq) & 1u)) lists[e] = v[u];
+        }
+        __syncthreads();
+        for (int pq = wave; pq < BM / kK; pq += NW) {
+            if (!((validq >> pq) & 1u)) continue;  // wave-uniform
+            const int64_t bt = m0 / kK + pq;
+            const uint64_t best = wave_merge_lists(lists + pq * per, p.tk_nsplit);
+            if (lane < (uint32_t)kK) {
+                mid[pq * kK + lane] = (int32_t)key_id(best);
+                if (owner) {
+                    p.cand_id[bt * kK + lane] = (int32_t)key_id(best);
+                    p.cand_u[bt * kK + lane] =
+                        p.logits_bf16 ? merged_value<true>(best, p.logits + bt * p.ld * 2, p.V_logits)
+                                      : merged_value<false>(best, p.logits + bt * p.ld * 4, p.V_logits);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
     // Gathered source rows of this lane's DMA loads.  Rows past M, of padding
     // positions or with an out-of-range id load E row 0; the last are written
     // as zeros, the others not at all.
@@ -558,7 +610,7 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_cand_kernel(CandPara
         const int64_t m = m0 + row;
         int64_t tok = 0;
         if (m < p.M && ((validq >> (row >> 4)) & 1u)) {
-            const int32_t t = p.cand[m];
+            const int32_t t = p.tk_part ? mid[row] : p.cand[m];
             if (t >= 0 && (int64_t)t < p.V) {
                 tok = t;
                 xok |= 1u << u;
@@ -774,8 +826,9 @@ struct GateParams {
 template <int BN>
 constexpr int gate_stages() { return BN >= 256 ? 3 : DSEL_GATE_STAGES; }
 
+// The work of workgroup `bid` of the gate job.
 template <int BN>
-__global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GateParams p) {
+__device__ __forceinline__ void gate_gemm_block(const GateParams &p, int bid) {
     constexpr int BM = 128;
     using T = CandTile<BN>;
     constexpr int NW = T::NW;
@@ -785,8 +838,8 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
     __shared__ __attribute__((aligned(16))) uint16_t Ws[NSG * BN * kBK];
 
     const int tiles = (p.mt_gate + p.mt_ver) * p.nside;
-    const int ks = blockIdx.x / tiles;
-    const int tw = blockIdx.x % tiles;
+    const int ks = bid / tiles;
+    const int tw = bid % tiles;
     const bool gate = tw < p.mt_gate * p.nside;
     const int tt = gate ? tw : tw - p.mt_gate * p.nside;
     const int64_t m0 = (int64_t)(tt / p.nside) * BM;
@@ -859,6 +912,11 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
                 for (int z = 1; z < kK; ++z) *(floatx4 *)(base + (int64_t)z * r) = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     });
+}
+
+template <int BN>
+__global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GateParams p) {
+    gate_gemm_block<BN>(p, blockIdx.x);
 }
 
 // Sum the K splits of the gate job in split order, then the epilogue.

@@ -367,6 +367,69 @@ __global__ __launch_bounds__(64 * kTopkWaves) void topk16_kernel(TopkParams p) {
     topk16_block<BF16, U>(p, blockIdx.x);
 }
 
+// Fold lists s0, s0 + 1, s0 + 2, then s0 + step, ... of the nsplit sorted
+// partial lists of a row (16 keys each, at src) into a wave's running best 16
+// (lanes 0..15, sorted): one 64-key sort per 3 lists.
+__device__ __forceinline__ uint64_t wave_fold_lists(const uint64_t *src, int nsplit, int s0, int step,
+                                                    uint64_t best) {
+    const uint32_t lane = lane_id();
+    for (; s0 < nsplit; s0 += step) {
+        uint64_t k = best;
+        if (lane >= (uint32_t)kK) {
+            const int s = s0 + (int)(lane - kK) / kK;
+            k = s < nsplit ? src[s * kK + (lane % kK)] : 0ull;
+        }
+        best = wave_sort64_desc(k);
+    }
+    return best;
+}
+
+// Top 16 of the sorted lists held by 16-lane rows r and r ^ (D / 16) (D = 16
+// or 32), sorted, in both rows.  The elementwise maximum of one list and the
+// other reversed is a bitonic sequence that holds the 16 best of the two; four
+// half-cleaner stages sort it (Batcher's bitonic merge).
+template <int D>
+__device__ __forceinline__ uint64_t merge_row_lists(uint64_t k) {
+    constexpr int kMirror = 0x140;  // DPP row_mirror: lane j of a row reads lane 15 - j
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, kMirror, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), kMirror, 0xF, 0xF, false);
+    const uint64_t other = xor_lane64<D>(((uint64_t)hi << 32) | lo);
+    k = k > other ? k : other;
+    k = bitonic_stage<8>(k, true);
+    k = bitonic_stage<4>(k, true);
+    k = bitonic_stage<2>(k, true);
+    return bitonic_stage<1>(k, true);
+}
+
+// Top 16, sorted, in lanes 0..15, of the nsplit sorted lists of a row (16 keys
+// each, at src, in LDS or global memory): the running best and three new lists
+// sit in the wave's four 16-lane rows and are merged pairwise, then the pairs'
+// results (two bitonic merges per three lists).
+__device__ __forceinline__ uint64_t wave_merge_lists(const uint64_t *src, int nsplit) {
+    const uint32_t lane = lane_id();
+    const int row = (int)(lane >> 4), j = (int)(lane & 15);
+    uint64_t best = 0ull;
+    for (int s0 = 0; s0 < nsplit; s0 += 3) {
+        const int s = s0 + row - 1;
+        uint64_t k = row == 0 ? best : (s < nsplit ? src[s * kK + j] : 0ull);
+        k = merge_row_lists<16>(k);
+        best = merge_row_lists<32>(k);
+    }
+    return best;
+}
+
+// The value of a merged key: from the key itself, or for the two codes that
+// merge several inputs (NaN, and +0.0 with -0.0) the exact bits read back from
+// the row (rowp == nullptr: NaN, or +0.0).
+template <bool BF16>
+__device__ __forceinline__ float merged_value(uint64_t key, const char *rowp, int64_t V) {
+    float u;
+    if (key_value(key, &u)) return u;
+    const uint32_t id = key_id(key);
+    if (rowp) return (int64_t)id < V ? load_elem<BF16>(rowp, id) : __builtin_nanf("");
+    return (uint32_t)(key >> 32) == 0u ? __builtin_nanf("") : 0.0f;
+}
+
 // Merge the nsplit partial lists of a row: one workgroup (4 waves) per row.
 // With logits == nullptr (lists from the LM-head kernel) a zero value comes out
 // as +0.0.
@@ -380,33 +443,15 @@ __global__ __launch_bounds__(256) void topk16_merge_kernel(TopkParams p) {
     const uint32_t lane = lane_id();
     const int wave = (int)(threadIdx.x / kWave);
     const uint64_t *src = p.partial + row * p.nsplit * kK;
-    uint64_t best = 0ull;
-    for (int s0 = 3 * wave; s0 < p.nsplit; s0 += 12) {
-        uint64_t k = best;
-        if (lane >= (uint32_t)kK) {
-            int s = s0 + (int)(lane - kK) / kK;
-            k = s < p.nsplit ? src[s * kK + (lane % kK)] : 0ull;
-        }
-        best = wave_sort64_desc(k);
-    }
+    uint64_t best = wave_fold_lists(src, p.nsplit, 3 * wave, 12, 0ull);
     __shared__ uint64_t sk[4 * kK];
     if (lane < (uint32_t)kK) sk[wave * kK + lane] = best;
     __syncthreads();
     if (wave != 0) return;
     best = wave_sort64_desc(sk[lane]);
     if (lane < (uint32_t)kK) {
-        uint32_t id = key_id(best);
-        p.cand_id[row * kK + lane] = (int32_t)id;
-        float u;
-        if (!key_value(best, &u)) {
-            if (p.logits) {  // the two merged codes: read the exact bits back
-                const char *rowp = p.logits + row * p.ld * ES;
-                u = (int64_t)id < p.V ? load_elem<BF16>(rowp, id) : __builtin_nanf("");
-            } else {         // no logits in memory (the LM-head path): NaN, or a zero
-                u = (uint32_t)(best >> 32) == 0u ? __builtin_nanf("") : 0.0f;
-            }
-        }
-        p.cand_u[row * kK + lane] = u;
+        p.cand_id[row * kK + lane] = (int32_t)key_id(best);
+        p.cand_u[row * kK + lane] = merged_value<BF16>(best, p.logits ? p.logits + row * p.ld * ES : nullptr, p.V);
     }
 }
 

@@ -273,8 +273,16 @@ dsel_status dsel_walk_pairs(const float *cand_u, const float *partials, int64_t 
  *   128 workgroups), the candidate projections and the pair term run as the
  *   kernels of dsel_project_pairs and dsel_walk_pairs: A and B stay on chip
  *   and only each group's 16 x 16 partial table per position leaves it.
- *   Otherwise the separate kernels run and A_prev, B_cur and S pass through
- *   the workspace when not asked for.  Either route gives the same bits.
+ *   Otherwise, for small batches (at most 128 positions) whose gate GEMM is
+ *   split along K with column tiles at most 64 wide, and when
+ *   A_prev, B_cur and G are not asked for, three launches do the work: the
+ *   top-16 in partial lists beside the gate GEMM; the candidate GEMM, each of
+ *   its workgroups merging the lists of its own positions first; and, per
+ *   position and group of the rank, the split sums, the pair table and (by
+ *   the last workgroup of each block to finish, counted with an atomic
+ *   counter) the walk.  Otherwise the separate kernels run and A_prev, B_cur
+ *   and S pass through the workspace when not asked for.  Every route gives
+ *   the same bits; dsel_select_path_route tells which one a call takes.
  *   walk       the walk arguments (required), as for dsel_score_pairs.
  *   workspace  at least dsel_select_path_workspace_bytes() bytes (256-byte
  *              aligned); contents need no initialisation.
@@ -302,6 +310,13 @@ size_t dsel_select_path_workspace_bytes(int64_t batch, int64_t block, int64_t vo
                                         int64_t r);
 dsel_status dsel_select_path(const dsel_path_args *args, const dsel_walk_args *walk, void *workspace,
                              size_t workspace_bytes, dsel_stream_t stream);
+/* The route dsel_select_path takes for these arguments (only the shape and
+ * which outputs are given are read): DSEL_ROUTE_FUSED, DSEL_ROUTE_SMALL or
+ * DSEL_ROUTE_SEPARATE; -1 for an empty batch or an invalid shape. */
+#define DSEL_ROUTE_SEPARATE 0
+#define DSEL_ROUTE_FUSED 1
+#define DSEL_ROUTE_SMALL 2
+int dsel_select_path_route(const dsel_path_args *args);
 
 /* select_path_noalloc -- dsel_select_path for callers that cannot allocate
  * (code under HIP graph capture, tight serving loops, harnesses that forbid

@@ -199,3 +199,23 @@ def test_project_pairs_and_walk_pairs_validation(lib):
     assert wp(partials=None) == -1 and wp(partials=P(0x100004)) == -3
     assert wp(walk=ds.WalkArgs(5, 1.0, None, 0x100000, 0x100000, 0x100000, None, None)) == -2
     assert wp(batch=0, cand_u=None, partials=None) == 0
+
+
+def test_select_path_route_by_shape():
+    """dsel_select_path_route is host logic (no GPU): the fused kernels once
+    the batch fills the chip, the three-launch small-batch route for a few
+    blocks when no intermediates are asked for, the separate kernels
+    otherwise (intermediates wanted, an unsplit gate, more than 128 positions)."""
+    import torch
+    import draft_selection_amd as ds
+    bf, f32 = torch.bfloat16, torch.float32
+    V = 151936
+    assert ds.select_path_route(1, 16, V, bf, 2560, 256) == ds.ROUTE_SMALL
+    assert ds.select_path_route(8, 16, V, bf, 2560, 256) == ds.ROUTE_SMALL
+    assert ds.select_path_route(2, 16, V, f32, 2560, 96) == ds.ROUTE_SMALL
+    assert ds.select_path_route(1, 16, V, bf, 2560, 256, want_AB=True) == ds.ROUTE_SEPARATE
+    assert ds.select_path_route(9, 16, V, bf, 2560, 256) == ds.ROUTE_SEPARATE  # 144 positions
+    assert ds.select_path_route(4, 8, 1024, f32, 64, 32) == ds.ROUTE_SEPARATE  # d 64: one K step, no split
+    assert ds.select_path_route(64, 16, V, bf, 2560, 256) == ds.ROUTE_FUSED
+    assert ds.select_path_route(256, 16, 202048, f32, 6144, 256, want_AB=True) == ds.ROUTE_FUSED
+    assert ds.select_path_route(0, 16, V, bf, 2560, 256) == -1

@@ -45,9 +45,17 @@ def _fused(d, mode, lens, T=1.0):
     return {k: v.cpu().numpy() for k, v in res.items()}
 
 
-def _equal(a, b, lens, L):
+def _small(d, mode, lens, T=1.0):
+    res = ds.select_path(d["logits"], d["E"], d["W_A"], d["W_B"], d["W_H"], d["h"], d["verified"], mode=mode,
+                         temperature=T, uniforms=d["uniforms"], want_S=True, want_q=True, block_len=lens)
+    torch.cuda.synchronize()
+    assert ds.device_error() == 0
+    return {k: v.cpu().numpy() for k, v in res.items()}
+
+
+def _equal(a, b, lens, L, keys=KEYS):
     n_of = [L] * a["cand_id"].shape[0] if lens is None else lens
-    for k in KEYS:
+    for k in keys:
         for blk, n in enumerate(n_of):
             x, y = a[k][blk, :n], b[k][blk, :n]
             if x.dtype.kind == "f":
@@ -68,6 +76,44 @@ def test_path_equals_separate_calls(dev, name, mode, ragged):
     a = _fused(d, mode, lens)
     b = _separate(d, mode, lens)
     _equal(a, b, None if lens_np is None else lens_np, cfg.block)
+
+
+SMALL_CASES = {
+    # one block of 16 (the latency shape), both walks
+    "c1": (synth.CONFIGS["c1"], None),
+    # three blocks, one empty and one short
+    "c1x3": (synth.CONFIGS["c1"].replace(batch=3), [16, 5, 0]),
+    # eight blocks of the 5 / 8 / 16 mix (the top-16 rows split fewer ways)
+    "c1x8": (synth.CONFIGS["c1"].replace(batch=8), "mix"),
+    # blocks of 8 at d 5120, sampled
+    "c3x6": (synth.CONFIGS["c3"].replace(batch=6), None),
+    # rank 96: groups of 32 columns, 32-wide candidate tiles
+    "r96": (synth.CONFIGS["c1"].replace(batch=2, r=96), None),
+    # fp32 logits
+    "f32": (synth.CONFIGS["c1"].replace(batch=2, logits_dtype="f32"), None),
+}
+
+
+@pytest.mark.parametrize("case,mode", [("c1", 0), ("c1", 1), ("c1x3", 0), ("c1x8", 1), ("c3x6", 1), ("r96", 0),
+                                       ("f32", 1)])
+def test_small_batch_route_equals_separate_calls(dev, case, mode):
+    """The three-launch route of small batches (top-16 beside the gate GEMM;
+    candidate GEMM with the list merge; split sums, pair tables and the walk
+    by each block's last workgroup): the bits of the separate calls."""
+    cfg, lens_spec = SMALL_CASES[case]
+    dt = torch.bfloat16 if cfg.logits_dtype == "bf16" else torch.float32
+    assert ds.select_path_route(cfg.batch, cfg.block, cfg.vocab, dt, cfg.d, cfg.r) == ds.ROUTE_SMALL
+    d = to_dev(synth.make(cfg, seed=21), dev)
+    if lens_spec == "mix":
+        lens_np = synth.make_block_len(cfg, seed=21)
+    else:
+        lens_np = None if lens_spec is None else np.asarray(lens_spec, np.int32)
+    lens = None if lens_np is None else torch.from_numpy(lens_np).to(dev)
+    for rep in range(2):  # the arrival counters start from zero on every call
+        a = _small(d, mode, lens)
+        b = _separate(d, mode, lens)
+        _equal(a, b, lens_np, cfg.block,
+               keys=("cand_id", "cand_u", "S", "path_tok", "path_slot", "path_s", "q"))
 
 
 def test_path_large_batch_unsplit_gate(dev):
