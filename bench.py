@@ -8,7 +8,8 @@ one JSON line (one GPU).
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload all|c1|c2|c3|c4]
 
 By default every graded workload is measured in one run (c2, c3, c4; the
-headline line is c4, the largest, with per-workload records for all three).
+headline line is c4, the largest, with per-workload records for all three),
+plus the latency shape c1 in a record of its own.
 Workloads (synthetic, seeded; see synth.CONFIGS): c1 one block of 16 (latency
 shape), c2 64 blocks of 16, c3 128 blocks of 8 with the sampled walk, c4 256
 blocks of 16 with fp32 logits and both walks.
@@ -32,6 +33,7 @@ BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 K = 16
 GRADED = ("c2", "c3", "c4")
 HEADLINE = "c4"
+LATENCY = "c1"  # one block of 16: measured too (its own record), never the headline
 # HBM byte counters against a plain 1 GiB device copy (--calibrate-copy): per
 # copied GiB FETCH_SIZE reads 0.5 GiB and WRITE_SIZE 1 GiB, so the counters'
 # KiB are multiplied by these factors to give bytes moved.
@@ -715,7 +717,10 @@ def bench_workload(args, name, ds, torch):
     prim = res_walks[["greedy", "sampled"][mode]]
     rec = {
         "workload": describe(cfg),
-        "route": "fused (dsel_project_pairs + dsel_walk_pairs kernels)" if fused else "separate kernels",
+        "route": {ds.ROUTE_FUSED: "fused (dsel_project_pairs + dsel_walk_pairs kernels)",
+                  ds.ROUTE_SMALL: "small-batch (three launches: top-16 beside the gate GEMM, candidate GEMM "
+                                  "with the list merge, pair tables and walk)",
+                  ds.ROUTE_SEPARATE: "separate kernels"}[ds.select_path_route(B, L, V, d["logits"].dtype, cfg.d, r)],
         "value": prim["blocks/s"], "unit": "blocks/s", "ms_per_step": prim["ms_per_step"],
         "us_per_block": prim["us_per_block"], "walks": res_walks, "dtype": dtype_of(cfg),
         "config": {"workload": describe(cfg), "batch": B, "block": L, "vocab": V, "d": cfg.d, "r": r,
@@ -782,7 +787,7 @@ def main():
 
     import draft_selection_amd as ds
 
-    names = GRADED if args.workload == "all" else (args.workload,)
+    names = (LATENCY,) + GRADED if args.workload == "all" else (args.workload,)
     head = HEADLINE if args.workload == "all" else args.workload
     recs = {}
     for n in names:

@@ -94,6 +94,22 @@ def test_lmhead_workload_sampled_rows(ora, dev):
     assert flagged <= 1
 
 
+def test_lmhead_largest_workload_sampled_rows(ora, dev):
+    """256 blocks x 16 positions at d 6144 against a vocabulary of 202,048 (the
+    largest workload, 10 TFLOP): all 4,096 rows on the GPU in one call, six of
+    them in the oracle."""
+    cfg = synth.CONFIGS["c4"]
+    E = synth.make_E(cfg)
+    h = synth.make_h(cfg).reshape(cfg.batch * cfg.block, cfg.d)
+    Ed = _dev(E, dev)
+    cid, cu = ds.lmhead_topk(_dev(h, dev), Ed)
+    torch.cuda.synchronize()
+    del Ed
+    rows = [0, 1, 1234, 2047, 3000, 4095]
+    flagged = check_lmhead(ora, h, E, cid.cpu().numpy(), cu.cpu().numpy(), rows)
+    assert flagged <= 1
+
+
 def test_lmhead_ties_and_equals_select_topk_on_the_same_logits(dev):
     """Integer inputs make every logit exact in fp32: the fused result must then
     equal dsel_select_topk over the materialised logits, bit for bit."""
