@@ -113,7 +113,7 @@ dsel_status plan_topk(const void *logits, dsel_dtype dt, int64_t batch, int64_t 
 
 // The top-16 launch; with `gate` (a split gate job) its reduction rides along
 // as extra workgroups (path.h).
-dsel_status launch_topk(const TopkPlan &t, const GateParams *gate, int64_t gate_elems, dsel_stream_t stream) {
+dsel_status launch_topk(const TopkPlan &t, const GateParams *gate, int64_t gate_units, dsel_stream_t stream) {
     TopkParams p = t.p;
     const int64_t wgs = p.rows * p.nsplit;
     dsel_status s;
@@ -121,7 +121,7 @@ dsel_status launch_topk(const TopkPlan &t, const GateParams *gate, int64_t gate_
         GateParams gp = *gate;
         int64_t tw = wgs;
         constexpr int TT = 64 * kTopkWaves;
-        const int64_t grid = wgs + (gate_elems + TT - 1) / TT;
+        const int64_t grid = wgs + (gate_units + TT - 1) / TT;
         if (grid >= (int64_t)INT_MAX) return DSEL_E_ARG;
         const void *k = t.bf16 ? (const void *)topk16_gate_kernel<true, kTopkUnroll<true>>
                                : (const void *)topk16_gate_kernel<false, kTopkUnroll<false>>;
@@ -232,8 +232,9 @@ dsel_status plan_gate(const uint16_t *E, int64_t vocab, int64_t d, const uint16_
 }
 
 // Output elements of the gate's reduction (0 when it is not split).
-int64_t gate_reduce_elems(const GatePlan &g) {
-    return g.p.nsplit > 1 ? ((int64_t)g.p.B * g.p.L + g.p.B) * g.p.r : 0;
+// Work units (four output elements each) of the gate reduction; 0 when unsplit.
+int64_t gate_reduce_units(const GatePlan &g) {
+    return g.p.nsplit > 1 ? ((int64_t)g.p.B * g.p.L + g.p.B) * g.p.r / 4 : 0;
 }
 
 dsel_status launch_gate_gemm(const GatePlan &g, dsel_stream_t stream) {
@@ -248,7 +249,7 @@ dsel_status launch_gate_gemm(const GatePlan &g, dsel_stream_t stream) {
 
 dsel_status launch_gate_reduce(const GatePlan &g, dsel_stream_t stream) {
     GateParams p = g.p;
-    const int64_t elems = gate_reduce_elems(g);
+    const int64_t elems = gate_reduce_units(g);
     if (elems == 0) return DSEL_OK;
     return launch((const void *)project_gate_reduce_kernel, dim3((unsigned)((elems + 255) / 256)), dim3(256), &p,
                   0, stream);
@@ -888,7 +889,7 @@ DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_a
         q.p.S = a->S;
         st = launch_gate_gemm(g, stream);
         if (st == DSEL_OK) {
-            const int64_t ge = gate_reduce_elems(g);
+            const int64_t ge = gate_reduce_units(g);
             st = launch_topk(t, ge ? &g.p : nullptr, ge, stream);
         }
         if (st == DSEL_OK) st = launch_fused(f, stream);
@@ -919,7 +920,7 @@ DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_a
     if (st != DSEL_OK) return st;
     st = launch_gate_gemm(g, stream);
     if (st == DSEL_OK) {
-        const int64_t ge = gate_reduce_elems(g);
+        const int64_t ge = gate_reduce_units(g);
         st = launch_topk(t, ge ? &g.p : nullptr, ge, stream);
     }
     if (st == DSEL_OK) st = launch_cand(c, stream);

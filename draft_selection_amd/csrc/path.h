@@ -19,13 +19,13 @@
 namespace dsel {
 
 // Workgroups [0, topk_wgs) run the top-16, the rest run the gate reduction,
-// one output element per thread.  The branch is per workgroup, so the top-16's
+// four output elements per thread.  The branch is per workgroup, so the top-16's
 // barriers are met by whole workgroups.
 template <bool BF16, int U>
 __global__ __launch_bounds__(64 * kTopkWaves) void topk16_gate_kernel(TopkParams tp, GateParams gp, int64_t topk_wgs) {
     const int64_t bid = blockIdx.x;
     if (bid < topk_wgs) topk16_block<BF16, U>(tp, bid);
-    else gate_reduce_elem(gp, (bid - topk_wgs) * (64 * kTopkWaves) + threadIdx.x);
+    else gate_reduce_unit(gp, (bid - topk_wgs) * (64 * kTopkWaves) + threadIdx.x);
 }
 
 }  // namespace dsel

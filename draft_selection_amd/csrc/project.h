@@ -919,10 +919,12 @@ __global__ __launch_bounds__(CandTile<BN>::NT) void project_gate_kernel(GatePara
     gate_gemm_block<BN>(p, blockIdx.x);
 }
 
-// Sum the K splits of the gate job in split order, then the epilogue.
-// Output element e (row e / r, column e % r).
-__device__ __forceinline__ void gate_reduce_elem(const GateParams &p, int64_t e) {
+// Sum the K splits of the gate job in split order, then the epilogue, for
+// output elements 4u .. 4u + 3 (row 4u / r, columns 4u % r ..; r % 4 == 0):
+// 16-byte loads, with every split's load in flight before the sums.
+__device__ __forceinline__ void gate_reduce_unit(const GateParams &p, int64_t u) {
     const int64_t rows_all = (int64_t)p.B * p.L + p.B;
+    const int64_t e = 4 * u;
     if (e >= rows_all * p.r) return;
     const int64_t row = e / p.r;
     const int n = (int)(e % p.r);
@@ -931,21 +933,34 @@ __device__ __forceinline__ void gate_reduce_elem(const GateParams &p, int64_t e)
         if (gate ? !position_live(p.len, (uint32_t)row, p.L) : block_len_of(p.len, row - (int64_t)p.B * p.L, p.L) == 0)
             return;
     }
-    float sum = 0.0f;
-    for (int ks = 0; ks < p.nsplit; ++ks) sum += p.part[((int64_t)ks * rows_all + row) * p.r + n];
+    const float *src = p.part + row * p.r + n;
+    const int64_t stride = rows_all * p.r;
+    floatx4 sum = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k0 = 0; k0 < p.nsplit; k0 += 8) {
+        floatx4 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (k0 + k < p.nsplit) v[k] = *(const floatx4 *)(src + (k0 + k) * stride);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (k0 + k < p.nsplit) sum += v[k];
+    }
     if (row < (int64_t)p.B * p.L) {
-        p.G[row * p.r + n] = 1.0f / (1.0f + expf(-sum));
+        floatx4 g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[i] = 1.0f / (1.0f + expf(-sum[i]));
+        *(floatx4 *)(p.G + row * p.r + n) = g;
     } else {
         const int64_t b = row - (int64_t)p.B * p.L;
         float *base = p.A_ver + b * p.ver_stride + n;
-        base[0] = sum;
+        *(floatx4 *)base = sum;
         if (p.ver_zero)
-            for (int z = 1; z < kK; ++z) base[(int64_t)z * p.r] = 0.0f;
+            for (int z = 1; z < kK; ++z) *(floatx4 *)(base + (int64_t)z * p.r) = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     }
 }
 
 __global__ __launch_bounds__(256) void project_gate_reduce_kernel(GateParams p) {
-    gate_reduce_elem(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
+    gate_reduce_unit(p, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 // Column tile and K splits of the gate job (M = batch*block + batch rows, a
