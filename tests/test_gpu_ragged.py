@@ -93,6 +93,19 @@ def test_ragged_is_bitwise_the_uniform_batch(dev, name, mode):
     _valid_equal(rag, uni, lens, KEYS)
 
 
+def test_ragged_many_blocks_bitwise_the_uniform_batch(dev):
+    """4,500 blocks of 2 positions (lengths 0, 1 or 2): more than 64 blocks per
+    lane in the compaction scan of the top-16 (its second level runs twice), and
+    thousands of blocks packed into the fused projection's tiles by length
+    class; every valid position equals the uniform batch bit for bit."""
+    cfg = synth.CONFIGS["c0"].replace(batch=4500, block=2)
+    d = to_dev(synth.make(cfg, seed=23), dev)
+    lens = np.random.default_rng(23).integers(0, 3, size=cfg.batch).astype(np.int32)
+    uni = _select(d, 0, None)
+    rag = _select(d, 0, _lens_dev(lens, dev))
+    _valid_equal(rag, uni, lens, KEYS)
+
+
 def test_padding_is_never_read(dev):
     cfg = synth.CONFIGS["c1"].replace(batch=5)
     inp = synth.make(cfg, seed=3)
