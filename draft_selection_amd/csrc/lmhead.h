@@ -8,15 +8,14 @@
 //       rows against a run of 256-column tiles of W.  Per column tile the
 //       logits come from the LDS-DMA MFMA pipeline of project.h (bf16 in, fp32
 //       accumulation), go through LDS (the pipeline's ring, free once the tile
-//       is done), and each wave updates the running top-16 of its 16 rows:
-//       lane l takes columns 4l .. 4l+3.  While a row's list is not full
-//       (its first tile) the 16 best of the 64 lane maxima are sorted in
-//       (64-lane bitonic sort on DPP and row swaps, one ds_bpermute to
-//       reverse it, then a 32-lane bitonic merge with the list);
-//       every other value is screened against the row's 16th key and the rare
-//       survivors are inserted one at a time.  The lists live in LDS
-//       between tiles; at the end they go out as 64-bit keys, one list per
-//       (row, vocab split).
+//       is done), and each wave updates the running top-16 of its 16 rows,
+//       four rows at a time: a 16-lane row of the wave holds one row's sorted
+//       list and screens that row's 256 logits (16 per lane) against the
+//       list's 16th key; each round, every lane offers its best survivor, the
+//       row's 16 offers are sorted and merged into the list (bitonic networks
+//       on DPP lane swaps within the 16-lane row), and survivors below the new
+//       16th drop out.  The lists live in LDS between tiles; at the end they
+//       go out as 64-bit keys, one list per (row, vocab split).
 //   topk16_merge_kernel (topk16.h) merges the splits of every row.
 #pragma once
 
@@ -47,20 +46,34 @@ constexpr int kLmBN = 256;
 constexpr int kLmRingBytes = 3 * (128 + kLmBN) * kBK * 2;
 constexpr int kLmListBytes = 128 * kK * 8;
 
-// Merge a wave-uniform batch of candidate keys (one per lane, 0 = none) into the
-// sorted list held in lanes 0..15 (descending): sort the 64 candidates, put the
-// best 16 reversed beside the list (a bitonic 32-sequence) and merge.
-__device__ __forceinline__ uint64_t list_merge64(uint64_t list, uint64_t cand) {
+// Bitonic sort, descending, of the 16 keys of every 16-lane row of the wave.
+__device__ __forceinline__ uint64_t sort16_rows(uint64_t k) {
     const uint32_t lane = lane_id();
-    const uint64_t srt = wave_sort64_desc(cand);
-    const uint64_t rev = shfl_idx64(srt, lane >= 16 && lane < 32 ? 31 - lane : lane);
-    uint64_t k = lane < 16 ? list : (lane < 32 ? rev : 0ull);
-    k = bitonic_stage<16>(k, true);
+    k = bitonic_stage<1>(k, (lane & 2u) == 0);
+    k = bitonic_stage<2>(k, (lane & 4u) == 0);
+    k = bitonic_stage<1>(k, (lane & 4u) == 0);
+    k = bitonic_stage<4>(k, (lane & 8u) == 0);
+    k = bitonic_stage<2>(k, (lane & 8u) == 0);
+    k = bitonic_stage<1>(k, (lane & 8u) == 0);
     k = bitonic_stage<8>(k, true);
     k = bitonic_stage<4>(k, true);
     k = bitonic_stage<2>(k, true);
-    k = bitonic_stage<1>(k, true);
-    return lane < 16 ? k : 0ull;
+    return bitonic_stage<1>(k, true);
+}
+
+// Top 16, sorted descending, of two sorted 16-lists in the same 16-lane rows:
+// the elementwise max of one and the other reversed is bitonic (Batcher's
+// merge), then four half-cleaner stages.
+__device__ __forceinline__ uint64_t merge16_rows(uint64_t a, uint64_t b) {
+    constexpr int kMirror = 0x140;  // DPP row_mirror: lane j of a row reads lane 15 - j
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, kMirror, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), kMirror, 0xF, 0xF, false);
+    const uint64_t br = ((uint64_t)hi << 32) | lo;
+    uint64_t k = a > br ? a : br;
+    k = bitonic_stage<8>(k, true);
+    k = bitonic_stage<4>(k, true);
+    k = bitonic_stage<2>(k, true);
+    return bitonic_stage<1>(k, true);
 }
 
 __global__ __launch_bounds__(LmTile::NT) void lmhead_topk_kernel(LmheadParams p) {
@@ -111,43 +124,56 @@ __global__ __launch_bounds__(LmTile::NT) void lmhead_topk_kernel(LmheadParams p)
         __syncthreads();  // every wave is done with the ring
         for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) { *(floatx4 *)(tile + rl * BN + cl) = v; });
         __syncthreads();
-        // wave w updates rows 16 w .. 16 w + 15; lane l takes columns 4l .. 4l+3
-        for (int rr = 0; rr < BM / T::NW; ++rr) {
-            const int r = wave * (BM / T::NW) + rr;
-            if (m0 + r >= p.R) break;  // wave-uniform
-            WaveTop st;
-            st.key = lane < 16 ? lists[r * kK + lane] : 0ull;
-            st.refresh();
-            const floatx4 v = *(const floatx4 *)(tile + r * BN + 4 * lane);
-            bool ok[4];
+        // wave w updates rows 16 w .. 16 w + 15, four at a time: 16-lane row g
+        // of the wave holds row r's list (lane j: entry j) and screens the
+        // row's columns 64 i + 4 j .. 64 i + 4 j + 3 (i < 4) against its 16th
+        // key.  Each round every lane offers its best remaining survivor; the
+        // row's 16 offers are sorted and merged with its list (bitonic), the
+        // threshold rises, and survivors below it drop out.
+        const int g = (int)(lane >> 4), j = (int)(lane & 15);
+        for (int pass = 0; pass < BM / T::NW / 4; ++pass) {
+            const int r = wave * (BM / T::NW) + 4 * pass + g;
+            const bool rok = m0 + r < p.R;
+            uint64_t key = lists[r * kK + j];
+            float thr_f = key_threshold(shfl_idx64(key, (lane & ~15u) | 15u));
+            float v[16];
+            uint32_t ob[16];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) ok[e] = (int64_t)(4 * lane + e) < left;
-            const uint32_t cbase = (uint32_t)n0 + 4 * lane;
-            int skip = -1;
-            if (st.thr == 0ull) {
-                // list not full (the row's first tile): seed it with the 16
-                // best of the 64 lane maxima, real values that bound the rest,
-                // beside the entries it already has
-                uint64_t best = 0ull;
+            for (int i = 0; i < 4; ++i) {
+                const floatx4 x = *(const floatx4 *)(tile + r * BN + 64 * i + 4 * j);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint64_t k = ok[e] ? cand_key(v[e], cbase + e) : 0ull;
-                    if (k > best) {
-                        best = k;
-                        skip = e;
+                for (int e = 0; e < 4; ++e) v[4 * i + e] = x[e];
+            }
+            uint32_t bits = 0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int col = 64 * (k >> 2) + 4 * j + (k & 3);  // increases with k
+                ob[k] = order_bits(v[k]);
+                if (rok && (int64_t)col < left && !(v[k] < thr_f)) bits |= 1u << k;
+            }
+            while (ballot(bits != 0) != 0ull) {
+                // the lane's best survivor: highest order, then the lowest column
+                int bk = -1;
+                uint32_t bo = 0;
+#pragma unroll
+                for (int k = 0; k < 16; ++k)
+                    if (((bits >> k) & 1u) && (bk < 0 || ob[k] > bo)) {
+                        bk = k;
+                        bo = ob[k];
                     }
+                uint64_t c = 0ull;
+                if (bk >= 0) {
+                    const uint32_t id = (uint32_t)n0 + 64 * (bk >> 2) + 4 * j + (bk & 3);
+                    c = ((uint64_t)bo << 32) | (uint32_t)(~id);
+                    bits &= ~(1u << bk);
                 }
-                st.key = list_merge64(st.key, best);
-                st.refresh();
-            }
-            // the rest, screened by value against the 16th key, one insertion
-            // per survivor (rare once the list is full)
+                key = merge16_rows(key, sort16_rows(c));
+                thr_f = key_threshold(shfl_idx64(key, (lane & ~15u) | 15u));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool pass = ok[e] && e != skip && !(v[e] < st.thr_f);
-                st.offer(v[e], pass, [&](uint32_t src) { return (uint32_t)n0 + 4 * src + e; });
+                for (int k = 0; k < 16; ++k)
+                    if (v[k] < thr_f) bits &= ~(1u << k);
             }
-            if (lane < 16) lists[r * kK + lane] = st.key;
+            lists[r * kK + j] = key;
         }
     }
     __syncthreads();
