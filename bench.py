@@ -663,9 +663,10 @@ def bench_workload(args, name, ds, torch):
         cold, cold_pct = stage_means(cevs), stage_pcts(cevs)
     warm = stage_means(evs)
 
-    # a ragged batch of the same shape (each block 5, 8 or 16 positions)
+    # a ragged batch of the same shape (each block 5, 8 or 16 positions); a
+    # batch of a few blocks has no mix to speak of
     ragged = None
-    if not args.no_ragged and L > 1:
+    if not args.no_ragged and L > 1 and B >= 8:
         lens_np = synth.make_block_len(cfg)
         lens = torch.from_numpy(lens_np).to(dev)
         revs = new_events(min(args.steps, 50))
