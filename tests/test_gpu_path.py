@@ -91,11 +91,15 @@ SMALL_CASES = {
     "r96": (synth.CONFIGS["c1"].replace(batch=2, r=96), None),
     # fp32 logits
     "f32": (synth.CONFIGS["c1"].replace(batch=2, logits_dtype="f32"), None),
+    # the longest blocks (32 positions) at rank 160: five groups of 32 columns
+    "L32r160": (synth.CONFIGS["c1"].replace(batch=3, block=32, r=160), [32, 7, 19]),
+    # blocks of one position: every step starts from the verified token
+    "L1": (synth.CONFIGS["c1"].replace(batch=100, block=1), None),
 }
 
 
 @pytest.mark.parametrize("case,mode", [("c1", 0), ("c1", 1), ("c1x3", 0), ("c1x8", 1), ("c3x6", 1), ("r96", 0),
-                                       ("f32", 1)])
+                                       ("f32", 1), ("L32r160", 1), ("L1", 0)])
 def test_small_batch_route_equals_separate_calls(dev, case, mode):
     """The three-launch route of small batches (top-16 beside the gate GEMM;
     candidate GEMM with the list merge; split sums, pair tables and the walk
