@@ -26,6 +26,15 @@
 // Workgroup order is XCD-aware: the nq groups of one tile run on one XCD, so
 // its gathered rows come from HBM once and from that XCD's L2 afterwards.
 //
+// Large batches take a wide tile: one workgroup computes two groups (a
+// 256 x 4 CW tile, wave tile 128 x CW instead of 64 x CW), so per MFMA it
+// reads three quarters of the fragments from LDS and moves two thirds of the
+// DMA bytes, and the grid has half as many workgroups, each with its setup and
+// epilogue.  Its K steps are 32 deep, so that a step still has 16 MFMAs per
+// wave between barriers and a four-stage ring (128 KB) fits; the MFMAs of
+// every accumulator run in the same K order, so the bits are those of the
+// narrow tile.
+//
 // A uniform batch puts floor(16 / L) consecutive blocks in a tile.  A ragged
 // batch packs its blocks by their real lengths (packed_tile), so that the
 // grid's first tiles hold all the work and the padding costs no MFMA time.
@@ -40,13 +49,29 @@ namespace dsel {
 // at least 128, else 32.  nq = r / CW groups.
 __host__ __device__ constexpr int pair_group_width(int r) { return (r % 64 == 0 && r >= 128) ? 64 : 32; }
 
-// Wave grid: DSEL_FUSED_GM row slabs x 2 (A side, B side); 4 slabs = 8 waves
-// (two per SIMD, wave tile 64 x CW).
+// Wave grid of the narrow tile (NG = 1 group per workgroup): DSEL_FUSED_GM
+// row slabs x 2 (A side, B side); 4 slabs = 8 waves (two per SIMD, wave tile
+// 64 x CW), 64-deep K steps, a three-stage ring.  The wide tile (NG = 2): 2
+// row slabs x 4 (A and B of each group), wave tile 128 x CW, 32-deep K steps,
+// a four-stage ring.  Per step and wave both run 16 MFMAs; the LDS traffic of
+// a step (DMA writes plus fragment reads) is 176 KB against 128 KB.
 #ifndef DSEL_FUSED_GM
 #define DSEL_FUSED_GM 4
 #endif
+template <int CW, int NG>
+struct FusedShape;
 template <int CW>
-using FusedTile = TileShape<256, 2 * CW, DSEL_FUSED_GM, 2>;
+struct FusedShape<CW, 1> {
+    using T = TileShape<256, 2 * CW, DSEL_FUSED_GM, 2>;
+    static constexpr int NS = 3;
+};
+template <int CW>
+struct FusedShape<CW, 2> {
+    using T = TileShape<256, 4 * CW, 2, 4, 32>;
+    static constexpr int NS = 4;
+};
+template <int CW, int NG = 1>
+using FusedTile = typename FusedShape<CW, NG>::T;
 
 // Tiles of a ragged batch, by harmonic bin packing (C. C. Lee and D. T. Lee,
 // "A simple on-line bin-packing algorithm", J. ACM 32(3), 1985): a block with
@@ -124,35 +149,38 @@ struct FusedParams {
     const int32_t *len;     // ragged batch: valid positions per block (nullptr: all L)
     int nb;                 // blocks per tile of a uniform batch (16 / L)
     int ntile;              // row tiles of the grid (ceil(B / nb), + 7 for a ragged batch)
-    int nq;                 // column groups (r / CW)
+    int nq;                 // column groups (r / CW); a workgroup takes NG of them
     float *P;               // [B * L][nq][16][16] partial pair tables
     float *A_prev, *B_cur;  // optional [B * L * 16][r] (nullptr: not written)
 };
 
-template <int CW>
-__global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedParams p) {
-    using T = FusedTile<CW>;
-    constexpr int BM = 256, BN = 2 * CW, NW = T::NW, XI = T::DXI, WI = T::DWI;
-    static_assert(T::WN == CW, "one wave column per side");
-    constexpr int RING = 3 * (BM + BN) * kBK;  // bf16 elements of the DMA ring
+template <int CW, int NG>
+__global__ __launch_bounds__((FusedTile<CW, NG>::NT)) void project_pair_kernel(FusedParams p) {
+    using T = FusedTile<CW, NG>;
+    constexpr int NS = FusedShape<CW, NG>::NS;
+    constexpr int BM = 256, BN = 2 * NG * CW, NW = T::NW, XI = T::DXI, WI = T::DWI, BK = T::BK;
+    static_assert(T::BNv == BN && T::WN % CW == 0, "wave columns hold whole (side, group) column ranges");
+    constexpr int RING = NS * (BM + BN) * BK;  // bf16 elements of the DMA ring
     constexpr int SROW = CW + 4;               // staged row stride in floats (bank skew)
-    constexpr int STAGE = 2 * BM * SROW * 2;   // bf16-element size of the staged A and B
+    constexpr int STAGE = 2 * BM * SROW * 2;   // bf16-element size of one group's staged A and B
     __shared__ __attribute__((aligned(16))) uint16_t smem[RING > STAGE ? RING : STAGE];
     __shared__ uint32_t okw[BM / 32];
-    // the gate of the tile's positions and A(verified) of its blocks, for this
-    // column group, staged before the main loop so their latency hides there
-    __shared__ __attribute__((aligned(16))) float Gs[16][CW];
-    __shared__ __attribute__((aligned(16))) float Vs[16][CW];
+    // the gate of the tile's positions and A(verified) of its blocks, for the
+    // workgroup's groups (row 16 g + position), staged before the main loop so
+    // their latency hides there
+    __shared__ __attribute__((aligned(16))) float Gs[16 * NG][CW];
+    __shared__ __attribute__((aligned(16))) float Vs[16 * NG][CW];
     __shared__ int gposs[16];  // flat position of each local position (-1: none)
     uint16_t *const Xs = smem;
-    uint16_t *const Ws = smem + 3 * BM * kBK;
+    uint16_t *const Ws = smem + NS * BM * BK;
 
     // XCD-aware order: workgroups w and w + 8 share an XCD; consecutive slots of
-    // one XCD take the column groups of one tile.
+    // one XCD take the column groups of one tile (NG at a time: q0 .. q0 + NG - 1).
     const int w = (int)blockIdx.x;
     const int xcd = w & 7, slot = w >> 3;
-    const int q = slot % p.nq;
-    const int tile = (slot / p.nq) * 8 + xcd;
+    const int nqg = p.nq / NG;
+    const int q0 = (slot % nqg) * NG;
+    const int tile = (slot / nqg) * 8 + xcd;
     if (tile >= p.ntile) return;
     asm volatile("" ::: "a0");  // keep the accumulators in AGPRs (see project_cand_kernel)
     const uint32_t lane = lane_id();
@@ -207,47 +235,57 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
             if (t >= 0 && (int64_t)t < p.V) {
                 tok = t;
                 xok |= 1u << u;
-            } else if ((lane & 7) == 0 && q == 0) {
+            } else if (lane % T::CPR == 0 && q0 == 0) {
                 atomicOr(&g_device_error, 1);
             }
         }
-        xsrc[u] = p.E + tok * d + dma_chunk_elems(row);
+        xsrc[u] = p.E + tok * d + dma_chunk_elems<T>(row);
     }
-    // W tile rows: W_A[q CW + n] for n < CW, then W_B[q CW + n - CW]
+    // W tile rows, CW per side and group: W_A[(q0 + g) CW + c] at n = 2 CW g + c,
+    // W_B[(q0 + g) CW + c] at n = 2 CW g + CW + c
     const uint16_t *wsrc[WI];
 #pragma unroll
     for (int u = 0; u < WI; ++u) {
         const int n = dma_row<T>(u);
-        const uint16_t *base = n < CW ? p.WA + (int64_t)(q * CW + n) * d : p.WB + (int64_t)(q * CW + n - CW) * d;
-        wsrc[u] = base + dma_chunk_elems(n);
+        const int wr = (q0 + n / (2 * CW)) * CW + n % CW;
+        wsrc[u] = ((n / CW) % 2 == 0 ? p.WA : p.WB) + (int64_t)wr * d + dma_chunk_elems<T>(n);
     }
 
-    // This thread's share of the epilogue's small operands, loaded now (their
-    // latency overlaps the main loop's first DMA steps) and put in LDS after
-    // it: float4 e of G[gp(pp)][q CW ..] (pp = e / (CW / 4)) for real
-    // positions, and of A(verified of the block of slot pp) for its real slots.
-    constexpr int NV4 = 16 * CW / 4;  // float4s of a 16 x CW table
-    static_assert(NV4 <= T::NT, "one float4 per thread");
-    const int e4 = (int)threadIdx.x, epp = e4 / (CW / 4), ec = (e4 % (CW / 4)) * 4;
-    const int gpe = (int)shfl_idx32((uint32_t)gp, (uint32_t)(epp & 15));
-    const int vbk = (int)shfl_idx32((uint32_t)tb.blk, (uint32_t)(epp & 15));
-    const bool gload = e4 < NV4 && ((validq >> epp) & 1u);
-    const bool vload = e4 < NV4 && epp < tb.nslot && ((validq >> (epp * S)) & 1u);
-    float4 gv = {0.f, 0.f, 0.f, 0.f}, vv = {0.f, 0.f, 0.f, 0.f};
-    if (gload) gv = *(const float4 *)(p.G + (int64_t)gpe * r + q * CW + ec);
-    if (vload) vv = *(const float4 *)(p.A_ver + (int64_t)vbk * p.ver_stride + q * CW + ec);
+    // This thread's share of the epilogue's small operands, moved into LDS now
+    // by LDS-DMA (no registers held across the main loop; the loop's first
+    // wait covers them, being issued before its loads): float4 e of Gs and Vs
+    // is G[gp(pp)][(q0 + g) CW ..] (g = e / (4 CW), pp = e / (CW / 4) % 16)
+    // for real positions, and A(verified of the block of slot pp) for its
+    // real slots; the other entries are not used.
+    constexpr int NV4 = NG * 16 * CW / 4;  // float4s of NG 16 x CW tables
+#pragma unroll
+    for (int it = 0; it < (NV4 + T::NT - 1) / T::NT; ++it) {
+        const int ew = wave + NW * it;  // the 1 KB piece of each table this wave fills
+        if (ew * kWave < NV4) {         // wave-uniform
+            const int e4 = ew * kWave + (int)lane, egi = e4 / (4 * CW), epp = (e4 / (CW / 4)) % 16;
+            const int ecol = (q0 + egi) * CW + (e4 % (CW / 4)) * 4;
+            const int gpe = (int)shfl_idx32((uint32_t)gp, (uint32_t)epp);
+            const int vbk = (int)shfl_idx32((uint32_t)tb.blk, (uint32_t)epp);
+            // lane l fills float4 64 ew + l
+            if ((validq >> epp) & 1u) lds_dma16(p.G + (int64_t)gpe * r + ecol, (uint16_t *)&Gs[0][0] + 512 * ew);
+            if (epp < tb.nslot && ((validq >> (epp * S)) & 1u))
+                lds_dma16(p.A_ver + (int64_t)vbk * p.ver_stride + ecol, (uint16_t *)&Vs[0][0] + 512 * ew);
+        }
+    }
 
-    // Id-validity bits of the 256 rows (word k: rows 32 k .. 32 k + 31); the
-    // main loop's barriers publish them
+    // Id-validity bits of the 256 rows (word k: rows 32 k .. 32 k + 31), RPI
+    // bits per (wave, DMA load); the main loop's barriers publish them
     {
-        uint8_t *bytes = (uint8_t *)okw;
 #pragma unroll
         for (int u = 0; u < XI; ++u) {
             const uint64_t bl = ballot(((xok >> u) & 1u) != 0);
-            uint32_t byte = 0;
+            uint32_t bits = 0;
 #pragma unroll
-            for (int k = 0; k < 8; ++k) byte |= (uint32_t)((bl >> (8 * k)) & 1u) << k;
-            if (lane == 0) bytes[wave + NW * u] = (uint8_t)byte;
+            for (int k = 0; k < T::RPI; ++k) bits |= (uint32_t)((bl >> (T::CPR * k)) & 1u) << k;
+            if (lane == 0) {
+                if constexpr (T::RPI == 8) ((uint8_t *)okw)[wave + NW * u] = (uint8_t)bits;
+                else ((uint16_t *)okw)[wave + NW * u] = (uint16_t)bits;
+            }
         }
     }
 
@@ -258,102 +296,110 @@ __global__ __launch_bounds__(FusedTile<CW>::NT) void project_pair_kernel(FusedPa
         for (int j = 0; j < T::TN; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    mma_tile_dma_src<T>(xsrc, wsrc, 0, d / kBK, Xs, Ws, acc);
+    mma_tile_dma_src<T, NS>(xsrc, wsrc, 0, d / BK, Xs, Ws, acc);
 
     __syncthreads();  // every wave is done with the ring (its LDS is reused below)
     auto row_ok = [&](int rl) { return ((okw[rl >> 5] >> (rl & 31)) & 1u) != 0; };
-    const int wn = wave % T::GNv;  // 0: A side, 1: B side
-    const int cq = q * CW;
+    const int wn = wave % T::GNv;
+    // tile column n holds side (n / CW) % 2 (A, B) of group q0 + n / (2 CW),
+    // column n % CW of it; a 32-column MFMA block lies in one such range
 
     // Optional outputs, as project_cand_kernel writes them: candidate row m of
     // side A becomes predecessor row of position t + 1 (output row m + 16),
     // written only where that position exists; side B for every real position.
     if (p.A_prev != nullptr) {
-        float *const out = wn == 0 ? p.A_prev + kK * r : p.B_cur;
-        const uint32_t wq = wn == 0 ? succq : validq;
         for_tile_rows4<T>(acc, [&](int rl, int cl, floatx4 v) {
-            if (!((wq >> (rl >> 4)) & 1u)) return;
+            const int side = (cl / CW) & 1;
+            if (!(((side == 0 ? succq : validq) >> (rl >> 4)) & 1u)) return;
+            float *const out = side == 0 ? p.A_prev + kK * r : p.B_cur;
             const int64_t grow = (int64_t)gposs[rl >> 4] * kK + (rl & 15);
-            *(floatx4 *)(out + grow * r + cq + (cl - wn * CW)) =
+            *(floatx4 *)(out + grow * r + (q0 + cl / (2 * CW)) * CW + cl % CW) =
                 row_ok(rl) ? v : floatx4{0.0f, 0.0f, 0.0f, 0.0f};
         });
     }
 
-    if (gload) *(float4 *)&Gs[epp][ec] = gv;
-    if (vload) *(float4 *)&Vs[epp][ec] = vv;
-    // Stage both sides in LDS as fp32 rows (zero rows for out-of-range ids).
     float *const As = (float *)smem;
     float *const Bs = As + BM * SROW;
-    {
-        // straight from the MFMA layout: lane l holds column l % 32 of each
-        // 32 x 32 block, rows 8 g + 4 (l / 32) + e (element 4 g + e); a store
-        // instruction then covers 32 consecutive columns of two rows
-        float *const Ss = wn == 0 ? As : Bs;
-        const int wm = wave / T::GNv;
-        const int c0 = (int)(lane & 31), h4 = 4 * (int)(lane >> 5);
 #pragma unroll
-        for (int i = 0; i < T::TM; ++i)
+    for (int gi = 0; gi < NG; ++gi) {
+        if (gi > 0) __syncthreads();  // the previous group's tables are done with LDS
+        // Stage both sides of group q0 + gi in LDS as fp32 rows (zero rows for
+        // out-of-range ids).
+        {
+            // straight from the MFMA layout: lane l holds column l % 32 of each
+            // 32 x 32 block, rows 8 g + 4 (l / 32) + e (element 4 g + e); a store
+            // instruction then covers 32 consecutive columns of two rows
+            const int wm = wave / T::GNv;
+            const int c0 = (int)(lane & 31), h4 = 4 * (int)(lane >> 5);
 #pragma unroll
-            for (int g = 0; g < 4; ++g)
+            for (int j = 0; j < T::TN; ++j) {
+                const int n0 = wn * T::WN + 32 * j;  // first tile column of block column j
+                if (n0 / (2 * CW) != gi) continue;    // wave-uniform
+                float *const Ss = ((n0 / CW) & 1 ? Bs : As) + n0 % CW + c0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int rl = wm * T::WM + 32 * i + 8 * g + h4 + e;
-                    const bool ok = row_ok(rl);
+                for (int i = 0; i < T::TM; ++i)
 #pragma unroll
-                    for (int j = 0; j < T::TN; ++j) Ss[rl * SROW + 32 * j + c0] = ok ? acc[i][j][4 * g + e] : 0.0f;
-                }
-    }
-    __syncthreads();
-
-    // Pair partials: wave w takes local positions w, w + NW, ..., two at a time
-    // with their MFMA chains interleaved.  Lane (fr, fg) supplies row fr and
-    // columns 16 s + 4 fg + {0..3} of slice s, one v_mfma_f32_16x16x4_f32 per
-    // column; the result holds rows i = 4 fg + v, column j = fr.  A position
-    // that is padding is computed on whatever LDS holds and not stored.
-    const int fr = (int)(lane & 15), fg = (int)(lane >> 4);
-    static_assert(16 % (2 * NW) == 0, "positions in pairs");
+                    for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int pr = 0; pr < 16 / (2 * NW); ++pr) {
-        int pps[2];
-        const float *ap[2], *bp[2], *gsp[2];
-        bool arow[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int pp = wave + NW * (2 * pr + k);
-            const int t = pp % S;
-            pps[k] = pp;
-            gsp[k] = &Gs[pp][4 * fg];
-            bp[k] = Bs + (kK * pp + fr) * SROW + 4 * fg;
-            ap[k] = t > 0 ? As + (kK * (pp - 1) + fr) * SROW + 4 * fg : &Vs[pp < tb.nslot * S ? pp / S : 0][4 * fg];
-            arow[k] = t > 0 || fr == 0;  // position 0 has one predecessor row
+                        for (int e = 0; e < 4; ++e) {
+                            const int rl = wm * T::WM + 32 * i + 8 * g + h4 + e;
+                            Ss[rl * SROW] = row_ok(rl) ? acc[i][j][4 * g + e] : 0.0f;
+                        }
+            }
         }
-        if (!((validq >> pps[0]) & 1u) && !((validq >> pps[1]) & 1u)) continue;  // wave-uniform
-        floatx4 pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+        __syncthreads();
+
+        // Pair partials: wave w takes local positions w, w + NW, ..., two at a time
+        // with their MFMA chains interleaved.  Lane (fr, fg) supplies row fr and
+        // columns 16 s + 4 fg + {0..3} of slice s, one v_mfma_f32_16x16x4_f32 per
+        // column; the result holds rows i = 4 fg + v, column j = fr.  A position
+        // that is padding is computed on whatever LDS holds and not stored.
+        const int fr = (int)(lane & 15), fg = (int)(lane >> 4);
+        static_assert(16 % (2 * NW) == 0, "positions in pairs");
 #pragma unroll
-        for (int s = 0; s < CW / 16; ++s) {
-            float4 ag[2], b[2];
+        for (int pr = 0; pr < 16 / (2 * NW); ++pr) {
+            int pps[2];
+            const float *ap[2], *bp[2], *gsp[2];
+            bool arow[2];
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
-                const float4 a = arow[k] ? *(const float4 *)(ap[k] + 16 * s) : float4{0.f, 0.f, 0.f, 0.f};
-                const float4 g = *(const float4 *)(gsp[k] + 16 * s);
-                b[k] = *(const float4 *)(bp[k] + 16 * s);
-                ag[k] = float4{a.x * g.x, a.y * g.y, a.z * g.z, a.w * g.w};
+                const int pp = wave + NW * (2 * pr + k);
+                const int t = pp % S;
+                pps[k] = pp;
+                gsp[k] = &Gs[16 * gi + pp][4 * fg];
+                bp[k] = Bs + (kK * pp + fr) * SROW + 4 * fg;
+                ap[k] = t > 0 ? As + (kK * (pp - 1) + fr) * SROW + 4 * fg
+                              : &Vs[16 * gi + (pp < tb.nslot * S ? pp / S : 0)][4 * fg];
+                arow[k] = t > 0 || fr == 0;  // position 0 has one predecessor row
+            }
+            if (!((validq >> pps[0]) & 1u) && !((validq >> pps[1]) & 1u)) continue;  // wave-uniform
+            floatx4 pacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+            for (int s = 0; s < CW / 16; ++s) {
+                float4 ag[2], b[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const float4 a = arow[k] ? *(const float4 *)(ap[k] + 16 * s) : float4{0.f, 0.f, 0.f, 0.f};
+                    const float4 g = *(const float4 *)(gsp[k] + 16 * s);
+                    b[k] = *(const float4 *)(bp[k] + 16 * s);
+                    ag[k] = float4{a.x * g.x, a.y * g.y, a.z * g.z, a.w * g.w};
+                }
+#pragma unroll
+                for (int k = 0; k < 2; ++k) pacc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[k].x, b[k].x, pacc[k], 0, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) pacc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[k].y, b[k].y, pacc[k], 0, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) pacc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[k].z, b[k].z, pacc[k], 0, 0, 0);
+#pragma unroll
+                for (int k = 0; k < 2; ++k) pacc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[k].w, b[k].w, pacc[k], 0, 0, 0);
             }
 #pragma unroll
-            for (int k = 0; k < 2; ++k) pacc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[k].x, b[k].x, pacc[k], 0, 0, 0);
+            for (int k = 0; k < 2; ++k) {
+                if (!((validq >> pps[k]) & 1u)) continue;
+                float *Pp = p.P + ((int64_t)gposs[pps[k]] * p.nq + q0 + gi) * (kK * kK) + fr;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) pacc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[k].y, b[k].y, pacc[k], 0, 0, 0);
-#pragma unroll
-            for (int k = 0; k < 2; ++k) pacc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[k].z, b[k].z, pacc[k], 0, 0, 0);
-#pragma unroll
-            for (int k = 0; k < 2; ++k) pacc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(ag[k].w, b[k].w, pacc[k], 0, 0, 0);
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            if (!((validq >> pps[k]) & 1u)) continue;
-            float *Pp = p.P + ((int64_t)gposs[pps[k]] * p.nq + q) * (kK * kK) + fr;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) Pp[(4 * fg + v) * kK] = pacc[k][v];
+                for (int v = 0; v < 4; ++v) Pp[(4 * fg + v) * kK] = pacc[k][v];
+            }
         }
     }
 }
@@ -369,9 +415,24 @@ inline int64_t fused_grid_tiles(int64_t batch, int64_t block, bool ragged) {
     const int64_t nt = fused_tiles(batch, block);
     return nt && ragged ? nt + 7 : nt;
 }
+// Groups per workgroup: the wide tile (2) for a uniform batch whose grid
+// still has DSEL_FUSED_WIDE_MIN workgroups (two rounds over the chip's 256
+// CUs), else the narrow one; at fewer rounds the narrow tile's twice as many
+// workgroups keep more CUs busy.  A ragged batch keeps the narrow tile: its
+// live tiles (not known on the host) can be far fewer than the grid's, and
+// then the finer unit balances better (c4's 5/8/16 mix: 155 live tiles of
+// 263, 620 narrow workgroups against 310 wide).
+#ifndef DSEL_FUSED_WIDE_MIN
+#define DSEL_FUSED_WIDE_MIN 512
+#endif
+inline int fused_groups(int64_t batch, int64_t block, int64_t r, bool ragged) {
+    const int cw = pair_group_width((int)r);
+    const int64_t nq = r / cw;
+    return !ragged && cw == 64 && nq % 2 == 0 && fused_tiles(batch, block) * (nq / 2) >= DSEL_FUSED_WIDE_MIN ? 2 : 1;
+}
 inline int64_t fused_grid(int64_t batch, int64_t block, int64_t r, bool ragged) {
     const int64_t nt = fused_grid_tiles(batch, block, ragged);
-    return (nt + 7) / 8 * 8 * (r / pair_group_width((int)r));
+    return (nt + 7) / 8 * 8 * (r / pair_group_width((int)r) / fused_groups(batch, block, r, ragged));
 }
 
 // Does dsel_select_path run the fused kernel for this shape?  It needs whole

@@ -588,6 +588,7 @@ bool path_layout(int64_t batch, int64_t block, int64_t vocab, dsel_dtype dt, int
 struct FusedPlan {
     FusedParams p;
     int CW = 64;
+    int NG = 1;  // rank groups per workgroup
 };
 
 dsel_status plan_fused(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A, const uint16_t *W_B,
@@ -620,6 +621,7 @@ dsel_status plan_fused(const uint16_t *E, int64_t vocab, int64_t d, const uint16
     p.nb = fused_blocks_per_tile(block);
     p.ntile = (int)fused_grid_tiles(batch, block, block_len != nullptr);
     f->CW = pair_group_width((int)r);
+    f->NG = fused_groups(batch, block, r, block_len != nullptr);
     p.nq = (int)(r / f->CW);
     p.P = P;
     p.A_prev = A_prev;
@@ -631,8 +633,11 @@ dsel_status plan_fused(const uint16_t *E, int64_t vocab, int64_t d, const uint16
 dsel_status launch_fused(const FusedPlan &f, dsel_stream_t stream) {
     FusedParams p = f.p;
     const int64_t grid = fused_grid(p.B, p.L, p.r, p.len != nullptr);
-    const void *k = f.CW == 64 ? (const void *)project_pair_kernel<64> : (const void *)project_pair_kernel<32>;
-    return launch(k, dim3((unsigned)grid), dim3(f.CW == 64 ? FusedTile<64>::NT : FusedTile<32>::NT), &p, 0, stream);
+    const void *k = f.CW == 32 ? (const void *)project_pair_kernel<32, 1>
+                    : f.NG == 2 ? (const void *)project_pair_kernel<64, 2>
+                                : (const void *)project_pair_kernel<64, 1>;
+    const int nt = f.CW == 32 ? FusedTile<32, 1>::NT : f.NG == 2 ? FusedTile<64, 2>::NT : FusedTile<64, 1>::NT;
+    return launch(k, dim3((unsigned)grid), dim3(nt), &p, 0, stream);
 }
 
 }  // namespace

@@ -19,16 +19,18 @@
 //       K over workgroups and summed by project_gate_reduce_kernel.  It does
 //       not depend on select_topk.
 //
-// Main loop (mma_tile_dma): a K step is 64 deep (128 bytes of every row).
-// Tiles move from global memory straight into a three-stage LDS ring
-// (global_load_lds_dwordx4, no staging registers), two steps ahead of the
-// MFMAs.  In LDS the 16-byte chunk c of tile row `row` sits at chunk
-// c ^ key(row), key(row) = (row / 2) % 8: a fragment read serves 16 lanes (16
-// consecutive rows, one chunk each, 256 bytes) per LDS pass, and the 8 even and
-// the 8 odd rows of such a group (lower and upper 32 banks) then hit 8
-// distinct chunks each, free of bank conflicts.  The waves of a workgroup form
-// a GM x GN grid, each owning (BM/GM) x (BN/GN) of the tile as 32 x 32 MFMA
-// blocks.
+// Main loop (mma_tile_dma): a K step is 64 deep (128 bytes of every row), or
+// 32 deep for tiles that set BK = 32.  Tiles move from global memory straight
+// into an LDS ring of three or more stages (global_load_lds_dwordx4, no
+// staging registers), two or more steps ahead of the MFMAs.  In LDS the
+// 16-byte chunk c of tile row `row` sits at chunk c ^ key(row): a fragment
+// read serves 16 lanes (16 consecutive rows, one chunk each, 256 bytes) per
+// LDS pass, and the key spreads them over all 64 banks.  128-byte rows:
+// key(row) = (row / 2) % 8, the 8 even and the 8 odd rows (lower and upper 32
+// banks) hit 8 distinct chunks each; 64-byte rows: key(row) = (row / 4) % 4,
+// the four rows of each 16-bank quarter hit 4 distinct chunks.  The waves of
+// a workgroup form a GM x GN grid, each owning (BM/GM) x (BN/GN) of the tile
+// as 32 x 32 MFMA blocks.
 #pragma once
 
 #include <type_traits>
@@ -59,22 +61,28 @@ constexpr int RPM = DSEL_MMA_RPM;
 // BM x BN tile computed by GM x GN waves, each owning WM x WN as 32 x 32 MFMA
 // blocks (v_mfma_f32_32x32x16_bf16: one wave keeps the matrix core near its
 // peak, which the 16 x 16 shape does not).
-template <int BM, int BN, int GM, int GN>
+template <int BM, int BN, int GM, int GN, int BK_ = kBK>
 struct TileShape {
     static constexpr int BMv = BM, BNv = BN, GMv = GM, GNv = GN;
+    static constexpr int BK = BK_;                         // K elements per step
+    static constexpr int CPR = BK / 8;                     // 16-byte chunks per tile row
+    static constexpr int RPI = 64 / CPR;                   // tile rows one LDS-DMA instruction fills
     static constexpr int NT = 64 * GM * GN;                // threads
     static constexpr int NW = GM * GN;                     // waves
     static constexpr int WM = BM / GM, WN = BN / GN;       // wave tile
     static constexpr int TM = WM / 32, TN = WN / 32;       // MFMA blocks per wave
-    static constexpr int DXI = BM / 8 / NW, DWI = BN / 8 / NW;  // LDS-DMA loads per wave per step
+    static constexpr int DXI = BM / RPI / NW, DWI = BN / RPI / NW;  // LDS-DMA loads per wave per step
+    static_assert(BK == 64 || BK == 32, "K step");
     static_assert(TM >= 1 && TN >= 1 && DXI >= 1 && DWI >= 1, "tile shape");
+    // chunk swizzle of a tile row (depends on row % 16 only)
+    __device__ static __forceinline__ int key(int row) { return BK == 64 ? (row >> 1) & 7 : (row >> 2) & 3; }
 };
 
 // ---- direct-to-LDS pipeline --------------------------------------------------
 // global_load_lds_dwordx4 moves 16 bytes per lane from global memory straight
-// into LDS (64 lanes fill 1 KB = 8 tile rows of 128 bytes), so no registers
-// stage the tiles.  A ring of three LDS stages holds steps k, k+1, k+2 while
-// step k computes.  Waits are explicit: `s_waitcnt vmcnt(n)` with n = the
+// into LDS (64 lanes fill 1 KB = 8 tile rows of 128 bytes, or 16 of 64), so
+// no registers stage the tiles.  A ring of three LDS stages holds steps k,
+// k+1, k+2 while step k computes.  Waits are explicit: `s_waitcnt vmcnt(n)` with n = the
 // loads issued after the awaited step, then `s_barrier` (LDS-DMA completion is
 // tracked by vmcnt; the barrier also tells every wave that nobody still reads
 // the stage about to be refilled).
@@ -107,7 +115,7 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
     __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | ((N >> 4) << 14));
 }
 
-// acc += X * W^T over K steps [k0, k1) (64-deep steps), k1 > k0.  W rows at
+// acc += X * W^T over K steps [k0, k1) (T::BK-deep steps), k1 > k0.  W rows at
 // or past `wrows` (a ragged last tile) load row wrows - 1; their results are
 // the caller's to ignore.
 //
@@ -119,15 +127,17 @@ __device__ __forceinline__ void wait_vmcnt_lgkm0() {
 // register set) and runs the MFMAs of step kt from registers while they fly.
 // Keeping a whole step of reads in flight is what lets LDS reach its streaming
 // rate; one slice at a time leaves it latency-bound.
-// The W tile row a lane's u-th DMA load fills (rows 8 (wave + NW u) + lane / 8)
-// and the source offset of its 16-byte chunk within that row: physical chunk
-// lane % 8 of tile row `row` holds logical chunk (lane % 8) ^ key(row).
+// The tile row a lane's u-th DMA load fills (rows RPI (wave + NW u) +
+// lane / CPR) and the source offset of its 16-byte chunk within that row:
+// physical chunk lane % CPR of tile row `row` holds logical chunk
+// (lane % CPR) ^ key(row).
 template <class T>
 __device__ __forceinline__ int dma_row(int u) {
-    return 8 * ((int)(threadIdx.x >> 6) + T::NW * u) + (int)(lane_id() >> 3);
+    return T::RPI * ((int)(threadIdx.x >> 6) + T::NW * u) + (int)(lane_id() / T::CPR);
 }
+template <class T>
 __device__ __forceinline__ int dma_chunk_elems(int row) {
-    return (((int)(lane_id() & 7)) ^ ((row >> 1) & 7)) << 3;
+    return (((int)(lane_id() % T::CPR)) ^ T::key(row)) << 3;
 }
 
 template <class T, int NS = 3>
@@ -148,7 +158,7 @@ __device__ __forceinline__ void mma_tile_dma(const uint16_t *const (&xsrc)[T::DX
     for (int u = 0; u < T::DWI; ++u) {
         const int row = dma_row<T>(u);
         const int srow = row < wrows ? row : wrows - 1;
-        wsrc[u] = wbase + (int64_t)srow * wstride + dma_chunk_elems(row);
+        wsrc[u] = wbase + (int64_t)srow * wstride + dma_chunk_elems<T>(row);
     }
     mma_tile_dma_src<T, NS>(xsrc, wsrc, k0, k1, Xs, Ws, acc);
 }
@@ -162,11 +172,11 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
                                                  const uint16_t *const (&wsrc)[T::DWI], int k0, int k1,
                                                  uint16_t *Xs, uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN]) {
     constexpr int BM = T::BMv, BN = T::BNv, NW = T::NW;
-    constexpr int XI = T::DXI, WI = T::DWI;
-    static_assert(XI >= 1 && WI >= 1 && XI * NW * 8 == BM && WI * NW * 8 == BN, "DMA tile shape");
+    constexpr int XI = T::DXI, WI = T::DWI, BK = T::BK;
+    static_assert(XI >= 1 && WI >= 1 && XI * NW * T::RPI == BM && WI * NW * T::RPI == BN, "DMA tile shape");
     constexpr int PER = XI + WI;  // loads per wave per step
     static_assert(NS >= 3 && (NS - 1) * PER < 64, "ring depth");
-    constexpr int KS = kBK / 16;  // 16-deep slices per step
+    constexpr int KS = BK / 16;  // 16-deep slices per step
     const uint32_t lane = lane_id();
     // wave-uniform, so the LDS-DMA destinations below are scalar arithmetic
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -177,21 +187,21 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
     // at physical chunk (2 s + fk) ^ key(fr)
     int aoff[T::TM], boff[T::TN];
 #pragma unroll
-    for (int i = 0; i < T::TM; ++i) aoff[i] = (wm * T::WM + i * 32 + fr) * kBK;
+    for (int i = 0; i < T::TM; ++i) aoff[i] = (wm * T::WM + i * 32 + fr) * BK;
 #pragma unroll
-    for (int j = 0; j < T::TN; ++j) boff[j] = (wn * T::WN + j * 32 + fr) * kBK;
-    const int rsw = (fr >> 1) & 7;
+    for (int j = 0; j < T::TN; ++j) boff[j] = (wn * T::WN + j * 32 + fr) * BK;
+    const int rsw = T::key(fr);
 #define DSEL_ISSUE(k, stage)                                                                   \
     do {                                                                                       \
-        const int kk_ = ((k) < k1 ? (k) : k1 - 1) * kBK;                                       \
+        const int kk_ = ((k) < k1 ? (k) : k1 - 1) * BK;                                       \
         _Pragma("unroll") for (int u = 0; u < XI; ++u)                                         \
-            lds_dma16(xsrc[u] + kk_, Xs + (stage) * BM * kBK + (8 * (wave + NW * u)) * kBK);   \
+            lds_dma16(xsrc[u] + kk_, Xs + (stage) * BM * BK + (T::RPI * (wave + NW * u)) * BK);   \
         _Pragma("unroll") for (int u = 0; u < WI; ++u)                                         \
-            lds_dma16(wsrc[u] + kk_, Ws + (stage) * BN * kBK + (8 * (wave + NW * u)) * kBK);   \
+            lds_dma16(wsrc[u] + kk_, Ws + (stage) * BN * BK + (T::RPI * (wave + NW * u)) * BK);   \
     } while (0)
 #define DSEL_READ_STEP(set, stage)                                                             \
     do {                                                                                       \
-        const uint16_t *xb_ = Xs + (stage) * BM * kBK, *wb_ = Ws + (stage) * BN * kBK;         \
+        const uint16_t *xb_ = Xs + (stage) * BM * BK, *wb_ = Ws + (stage) * BN * BK;         \
         _Pragma("unroll") for (int s_ = 0; s_ < KS; ++s_) {                                    \
             const int ch_ = ((s_ * 2 + fk) ^ rsw) << 3;                                        \
             _Pragma("unroll") for (int i = 0; i < T::TM; ++i)                                  \
@@ -203,8 +213,8 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
     bf16x8 fa[2][KS][T::TM], fb[2][KS][T::TN];
     // DMA load q of a step (q < XI: X rows, then W rows) into stage `stage`
     auto dma = [&](int q, int kk, int stage) {
-        if (q < XI) lds_dma16(xsrc[q] + kk, Xs + stage * BM * kBK + (8 * (wave + NW * q)) * kBK);
-        else lds_dma16(wsrc[q - XI] + kk, Ws + stage * BN * kBK + (8 * (wave + NW * (q - XI))) * kBK);
+        if (q < XI) lds_dma16(xsrc[q] + kk, Xs + stage * BM * BK + (T::RPI * (wave + NW * q)) * BK);
+        else lds_dma16(wsrc[q - XI] + kk, Ws + stage * BN * BK + (T::RPI * (wave + NW * (q - XI))) * BK);
     };
     // One step kt whose fragments are in register set SET: the MFMAs of kt
     // with the fragment reads of kt+1 (from the next stage) interleaved one or
@@ -231,8 +241,8 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
         wg_barrier();             // everyone's: kt's stage is free, kt+1 is complete
         __builtin_amdgcn_sched_barrier(0);
         const int nxt = cur == NS - 1 ? 0 : cur + 1;
-        const uint16_t *xb = Xs + nxt * BM * kBK, *wb = Ws + nxt * BN * kBK;
-        const int kk = (kt + NS < k1 ? kt + NS : k1 - 1) * kBK;
+        const uint16_t *xb = Xs + nxt * BM * BK, *wb = Ws + nxt * BN * BK;
+        const int kk = (kt + NS < k1 ? kt + NS : k1 - 1) * BK;
         constexpr int NMF = KS * T::TM * T::TN;
 #pragma unroll
         for (int s_ = 0; s_ < KS; ++s_) {
@@ -279,39 +289,34 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
 
 // The same product with a leaner register footprint: fragments are read one
 // 16-deep slice ahead (two sets of TM + TN fragments instead of two whole K
-// steps), for kernels that keep other state live beside the GEMM.  While
-// slice s multiplies, slice s+1 is read; at a step's last slice the wave waits
-// for its own reads and its DMA of the next step, meets the others at the
-// barrier, refills the stage three steps ahead and reads the next step's
-// first fragments ahead of the last slice's MFMAs.
-template <class T>
-__device__ __forceinline__ void mma_tile_dma_lean(const uint16_t *const (&xsrc)[T::DXI], const uint16_t *wbase,
-                                                  int64_t wstride, int k0, int k1, uint16_t *Xs, uint16_t *Ws,
-                                                  floatx16 (&acc)[T::TM][T::TN], int wrows = T::BNv) {
+// steps), for kernels that keep other state live beside the GEMM or own wide
+// wave tiles.  While slice s multiplies, slice s+1 is read; at a step's last
+// slice the wave waits for its own reads and its DMA of the next step, meets
+// the others at the barrier, refills the stage NS steps ahead and reads the
+// next step's first fragments ahead of the last slice's MFMAs.  NS = 2 (a
+// two-stage ring) leaves one step of lead for the DMA.
+template <class T, int NS = 3>
+__device__ __forceinline__ void mma_tile_dma_lean_src(const uint16_t *const (&xsrc)[T::DXI],
+                                                      const uint16_t *const (&wsrc)[T::DWI], int k0, int k1,
+                                                      uint16_t *Xs, uint16_t *Ws, floatx16 (&acc)[T::TM][T::TN]) {
     constexpr int BM = T::BMv, BN = T::BNv, NW = T::NW;
     constexpr int XI = T::DXI, WI = T::DWI;
     static_assert(XI >= 1 && WI >= 1 && XI * NW * 8 == BM && WI * NW * 8 == BN, "DMA tile shape");
     constexpr int PER = XI + WI;
-    constexpr int NS = 3;
+    static_assert(NS >= 2 && (NS - 1) * PER < 64, "ring depth");
     constexpr int KS = kBK / 16;
+    static_assert(T::BK == kBK, "64-deep steps");
     const uint32_t lane = lane_id();
-    const int wave = threadIdx.x >> 6;
+    // wave-uniform, so the LDS-DMA destinations below are scalar arithmetic
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int wm = wave / T::GNv, wn = wave % T::GNv;
     const int fr = lane & 31, fk = lane >> 5;
-    const int lrow = (int)(lane >> 3), pch = (int)(lane & 7);
-    const uint16_t *wsrc[WI];
-#pragma unroll
-    for (int u = 0; u < WI; ++u) {
-        const int row = 8 * (wave + NW * u) + lrow;
-        const int srow = row < wrows ? row : wrows - 1;
-        wsrc[u] = wbase + (int64_t)srow * wstride + ((pch ^ ((row >> 1) & 7)) << 3);
-    }
     int aoff[T::TM], boff[T::TN];
 #pragma unroll
     for (int i = 0; i < T::TM; ++i) aoff[i] = (wm * T::WM + i * 32 + fr) * kBK;
 #pragma unroll
     for (int j = 0; j < T::TN; ++j) boff[j] = (wn * T::WN + j * 32 + fr) * kBK;
-    const int rsw = (fr >> 1) & 7;
+    const int rsw = T::key(fr);
     auto issue = [&](int k, int stage) {
         const int kk = (k < k1 ? k : k1 - 1) * kBK;
 #pragma unroll
@@ -327,10 +332,9 @@ __device__ __forceinline__ void mma_tile_dma_lean(const uint16_t *const (&xsrc)[
 #pragma unroll
         for (int j = 0; j < T::TN; ++j) b[buf][j] = *(const bf16x8 *)(wb + boff[j] + ch);
     };
-    issue(k0, 0);
-    issue(k0 + 1, 1);
-    issue(k0 + 2, 2);
-    wait_vmcnt<2 * PER>();
+#pragma unroll
+    for (int st = 0; st < NS; ++st) issue(k0 + st, st);
+    wait_vmcnt<(NS - 1) * PER>();
     wg_barrier();
     frag(0, Xs, Ws, 0);
     int cur = 0;
@@ -344,9 +348,9 @@ __device__ __forceinline__ void mma_tile_dma_lean(const uint16_t *const (&xsrc)[
             if (sl + 1 < KS) {
                 frag(n, xb, wb, sl + 1);
             } else {
-                wait_vmcnt_lgkm0<PER>();
+                wait_vmcnt_lgkm0<(NS - 2) * PER>();
                 wg_barrier();
-                issue(kt + 3, cur);
+                issue(kt + NS, cur);
                 frag(n, Xs + nxt * BM * kBK, Ws + nxt * BN * kBK, 0);
             }
 #pragma unroll
@@ -358,6 +362,22 @@ __device__ __forceinline__ void mma_tile_dma_lean(const uint16_t *const (&xsrc)[
         cur = nxt;
     }
     wait_vmcnt<0>();
+}
+
+// W rows from one row-major matrix (row stride wstride); tile rows at or past
+// `wrows` re-read row wrows - 1.
+template <class T>
+__device__ __forceinline__ void mma_tile_dma_lean(const uint16_t *const (&xsrc)[T::DXI], const uint16_t *wbase,
+                                                  int64_t wstride, int k0, int k1, uint16_t *Xs, uint16_t *Ws,
+                                                  floatx16 (&acc)[T::TM][T::TN], int wrows = T::BNv) {
+    const uint16_t *wsrc[T::DWI];
+#pragma unroll
+    for (int u = 0; u < T::DWI; ++u) {
+        const int row = dma_row<T>(u);
+        const int srow = row < wrows ? row : wrows - 1;
+        wsrc[u] = wbase + (int64_t)srow * wstride + dma_chunk_elems<T>(row);
+    }
+    mma_tile_dma_lean_src<T, 3>(xsrc, wsrc, k0, k1, Xs, Ws, acc);
 }
 
 // Valid-row mask of a BM-row tile, shared through LDS.  Rows are loaded by

@@ -7,7 +7,10 @@ S_t scores every adjacent candidate pair in one parallel pass.)
 
 Shapes are chosen so that the fused route runs (blocks of at most 16 positions
 and at least 128 workgroups: ceil(batch / floor(16 / block)) tiles times r / CW
-column groups); the tiny width keeps the oracle fast.  Every case checks the
+column groups); the tiny width keeps the oracle fast.  Uniform batches with
+at least 512 tiles x group pairs (r / CW even, CW = 64) take the wide tile,
+two groups per workgroup with 32-deep K steps; WIDE lists such shapes (their
+ragged form runs the narrow tile and must give the same bits).  Every case checks the
 oracle (exact top-16, |dS| and the stricter |dP| bound, walk with flags) and
 that the fused route gives the same bits as the separate calls, with and
 without the optional intermediates."""
@@ -30,6 +33,11 @@ def _cw(r):
 def _fused_route(B, L, r):
     nb = 16 // L if L <= 16 else 0
     return nb > 0 and -(-B // nb) * (r // _cw(r)) >= 128
+
+
+def _wide(B, L, r):
+    nb = 16 // L
+    return _cw(r) == 64 and (r // 64) % 2 == 0 and -(-B // nb) * (r // 128) >= 512
 
 
 def _cfg(B, L, r, d=64, V=1024, e_std=1.0):
@@ -74,9 +82,16 @@ def _bits_equal(a, b, keys, lens=None):
 SHAPES = [  # (batch, block, r): tiles of 1, 2, 3 and 16 blocks, every column-group width
     (256, 8, 32), (64, 16, 256), (192, 5, 64), (2048, 1, 32), (96, 12, 128), (130, 16, 224), (136, 7, 96),
 ]
+WIDE = [(256, 16, 256), (1536, 5, 128)]  # the wide tile: blocks of 16 at r = 256; 3 blocks per tile at r = 128
 
 
-@pytest.mark.parametrize("B,L,r", SHAPES)
+def test_wide_shapes_take_the_wide_tile():
+    assert all(_fused_route(*s) and _wide(*s) for s in WIDE)
+    assert not any(_wide(*s) for s in SHAPES)
+    assert _wide(256, 16, 256) and not _wide(64, 16, 256) and not _wide(128, 8, 256)  # c4 / c2 / c3
+
+
+@pytest.mark.parametrize("B,L,r", SHAPES + WIDE)
 @pytest.mark.parametrize("mode", [0, 1])
 def test_fused_route_against_oracle(ora, dev, B, L, r, mode):
     assert _fused_route(B, L, r)
@@ -93,7 +108,7 @@ def test_fused_route_against_oracle(ora, dev, B, L, r, mode):
     assert flagged <= max(1, B * L // 500)
 
 
-@pytest.mark.parametrize("B,L,r", SHAPES[:4] + [(64, 16, 256)])
+@pytest.mark.parametrize("B,L,r", SHAPES[:4] + [(64, 16, 256)] + WIDE)
 def test_fused_route_equals_separate_calls(dev, B, L, r):
     """Same bits as dsel_select_topk + dsel_project_gate + dsel_project_cand +
     dsel_score_pairs, with the optional outputs asked for or not."""
@@ -110,7 +125,7 @@ def test_fused_route_equals_separate_calls(dev, B, L, r):
         _bits_equal(bare, sep, ("path_tok", "path_slot", "path_s", "q"))
 
 
-@pytest.mark.parametrize("B,L,r", [(256, 8, 32), (64, 16, 256), (192, 5, 64)])
+@pytest.mark.parametrize("B,L,r", [(256, 8, 32), (64, 16, 256), (192, 5, 64)] + WIDE)
 def test_fused_route_ragged(dev, B, L, r):
     """Ragged batches on the fused route: every block as alone at its own
     length (bits equal to the separate calls at every valid position)."""
@@ -127,11 +142,11 @@ def test_fused_route_ragged(dev, B, L, r):
         _bits_equal(lean, sep, ("S", "path_slot", "q"), lens_np)
 
 
-@pytest.mark.parametrize("name,mode", [("c2", 0), ("c3", 1)])
+@pytest.mark.parametrize("name,mode", [("c2", 0), ("c3", 1), ("c4", 1)])
 def test_fused_route_workloads_equal_separate_calls(dev, name, mode):
-    """The graded workloads (64 x 16 and 128 x 8 positions) run the fused
-    route; the separate calls, pinned to the oracle elsewhere, give the same
-    bits."""
+    """The graded workloads (64 x 16, 128 x 8 and 256 x 16 positions, the
+    last on the wide tile) run the fused route; the separate calls, pinned to
+    the oracle elsewhere, give the same bits."""
     cfg = synth.CONFIGS[name]
     assert _fused_route(cfg.batch, cfg.block, cfg.r)
     d = to_dev(synth.make(cfg, seed=5), dev)

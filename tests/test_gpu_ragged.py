@@ -106,6 +106,19 @@ def test_ragged_many_blocks_bitwise_the_uniform_batch(dev):
     _valid_equal(rag, uni, lens, KEYS)
 
 
+def test_ragged_wide_batch_bitwise_the_uniform_batch(dev):
+    """256 blocks of 16 at r = 256: the uniform batch runs the fused
+    projection's wide tile (two rank groups per workgroup, 32-deep K steps),
+    the ragged batch the narrow tile (one group, 64-deep steps); every valid
+    position has the same bits."""
+    cfg = synth.CONFIGS["c0"].replace(batch=256, block=16, r=256, d=128, vocab=2048)
+    d = to_dev(synth.make(cfg, seed=29), dev)
+    lens = np.random.default_rng(29).integers(0, 17, size=cfg.batch).astype(np.int32)
+    uni = _select(d, 0, None)
+    rag = _select(d, 0, _lens_dev(lens, dev))
+    _valid_equal(rag, uni, lens, KEYS)
+
+
 def test_padding_is_never_read(dev):
     cfg = synth.CONFIGS["c1"].replace(batch=5)
     inp = synth.make(cfg, seed=3)
