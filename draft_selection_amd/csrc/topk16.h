@@ -87,14 +87,52 @@ __device__ __forceinline__ float load_elem(const char *rowp, int64_t i) {
 }
 
 // Running top-16 of one wave: lanes 0..15 of `key` hold the list, best first.
+//
+// The waves of a workgroup share a bound through LDS: each publishes the
+// value half (order bits) of its 4th and 16th keys.  Every list holds
+// distinct elements of the row, so with b = max(max over waves of the 16th,
+// min over waves of the 4th) at least 16 elements of the row have order bits
+// >= b; an element whose order bits are below b is not among the row's 16
+// best, and an element that is passes every wave's filter until the end.  So
+// a wave filters against max(its own 16th key, b << 32), which (the 4th-key
+// term above all) rises far faster than its own 16th key alone.
 struct WaveTop {
     uint64_t key;
-    uint64_t thr;  // key of the 16th entry (wave-uniform)
-    float thr_f;   // its value as a filter threshold (wave-uniform)
+    uint64_t own;       // key of the wave's own 16th entry (wave-uniform)
+    uint64_t thr;       // filter key: max(own, bound << 32) (wave-uniform)
+    float thr_f;        // its value as a filter threshold (wave-uniform)
+    uint32_t bound;     // the workgroup bound last read
+    uint32_t *pub;      // LDS: this wave's two published order halves
+    const uint32_t *all;  // LDS: every wave's, kTopkWaves x {4th, 16th}
 
-    __device__ __forceinline__ void refresh() {
-        thr = readlane64(key, 15);
+    __device__ __forceinline__ void set_thr() {
+        const uint64_t b = (uint64_t)bound << 32;
+        thr = own > b ? own : b;
         thr_f = key_threshold(thr);
+    }
+    __device__ __forceinline__ void refresh() {
+        own = readlane64(key, 15);
+        const uint32_t h3 = (uint32_t)(readlane64(key, 3) >> 32);
+        if (lane_id() == 0u) {
+            pub[0] = h3;
+            pub[1] = (uint32_t)(own >> 32);
+        }
+        set_thr();
+    }
+    // Read the other waves' halves (at most a few chunks old: both only rise).
+    __device__ __forceinline__ void sync() {
+        uint32_t mx16 = 0u, mn4 = 0xFFFFFFFFu;
+#pragma unroll
+        for (int v = 0; v < kTopkWaves; ++v) {
+            const uint32_t a = all[2 * v], b = all[2 * v + 1];
+            mn4 = a < mn4 ? a : mn4;
+            mx16 = b > mx16 ? b : mx16;
+        }
+        const uint32_t nb = (uint32_t)__builtin_amdgcn_readfirstlane((int)(mx16 > mn4 ? mx16 : mn4));
+        if (nb > bound) {
+            bound = nb;
+            set_thr();
+        }
     }
     // Insert a wave-uniform key known to rank above thr.  The list is DPP row
     // 0 (lanes 0..15), so the shift by one slot is a row_shr:1 of both halves
@@ -196,6 +234,7 @@ __device__ __forceinline__ void chunk_offer(WaveTop &st, const u32x4 (&w)[U], in
 template <bool BF16, int U>
 __device__ __forceinline__ void chunk_filter(WaveTop &st, const u32x4 (&w)[U], int64_t v0, int64_t ve,
                                              int64_t h0) {
+    st.sync();
     if constexpr (BF16) {
         if (st.thr_f > 0.0f) {  // wave-uniform; thr_f is itself a bf16 value
             const uint32_t floor = bf16_pk_floor(st.thr_f);
@@ -273,10 +312,17 @@ __device__ __forceinline__ void topk16_block(const TopkParams &p, int64_t bid) {
     const int64_t vb = nvec * gw / nw, ve = nvec * (gw + 1) / nw;
 #endif
 
+    // published order halves of every wave (0: nothing yet, below every key)
+    __shared__ uint32_t s_bound[2 * kTopkWaves];
+    if (lane < 2u) s_bound[2 * wave + lane] = 0u;
+    __syncthreads();
     WaveTop st;
     st.key = 0ull;
-    st.thr = 0ull;
-    st.thr_f = -__builtin_inff();
+    st.own = 0ull;
+    st.bound = 0u;
+    st.pub = &s_bound[2 * wave];
+    st.all = s_bound;
+    st.set_thr();
 
     // Stream the wave's range chunk by chunk, the next chunks' loads always in
     // flight while the current one is filtered (DSEL_TOPK_DEPTH register buffers).
