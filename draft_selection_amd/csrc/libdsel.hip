@@ -726,10 +726,13 @@ struct LatPlan {
 // Workspace: the top-16 lists, the gate and candidate partials (or, from an
 // unsplit candidate GEMM, A_prev and B_cur) where the separate route keeps
 // them; the decision tables and the arrival counters in regions of their own.
-// Positions up to which the small-batch route runs (beyond, the top-16's HBM
-// stream needs more workgroups in flight than the shared launch leaves it).
+// Positions up to which the small-batch route runs.  Beyond, the separate
+// kernels are faster: the top-16 rows split fewer ways in the shared launch,
+// and the last-arrival hand-offs grow with the positions (MI355X, blocks of 16
+// at d 2560: 1 and 2 blocks 48.5 / 53.2 us against 52.6 / 54.1 separate; 4 and
+// 8 blocks 65.4 / 87.7 us against 59.8 / 64.7).
 #ifndef DSEL_LAT_MAX_ROWS
-#define DSEL_LAT_MAX_ROWS 128
+#define DSEL_LAT_MAX_ROWS 32
 #endif
 
 bool latency_route(int64_t batch, int64_t block, int64_t d, int64_t r, bool fused, bool intermediates) {

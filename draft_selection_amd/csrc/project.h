@@ -775,9 +775,11 @@ inline int gather_probe_nsplit(int64_t M, int64_t d) {
 }
 
 // K splits of the candidate job: only when its tiles cannot fill the chip,
-// keeping at least DSEL_CAND_MIN_STEPS K steps per split.
+// keeping at least DSEL_CAND_MIN_STEPS K steps per split (one block of 16 at
+// d 2560: 5 splits 47.8 us per step, 10 splits 48.4-49.0, 20 splits 64, 40
+// splits 81; 2 to 16 blocks level between 5 and 10 splits).
 #ifndef DSEL_CAND_MIN_STEPS
-#define DSEL_CAND_MIN_STEPS 4
+#define DSEL_CAND_MIN_STEPS 8
 #endif
 // Column tile of the candidate job: the widest that divides r and still
 // gives at least 256 tiles (one per CU), else 32.  Narrow tiles re-read the

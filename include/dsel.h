@@ -273,7 +273,7 @@ dsel_status dsel_walk_pairs(const float *cand_u, const float *partials, int64_t 
  *   128 workgroups), the candidate projections and the pair term run as the
  *   kernels of dsel_project_pairs and dsel_walk_pairs: A and B stay on chip
  *   and only each group's 16 x 16 partial table per position leaves it.
- *   Otherwise, for small batches (at most 128 positions) whose gate GEMM is
+ *   Otherwise, for small batches (at most 32 positions) whose gate GEMM is
  *   split along K with column tiles at most 64 wide, and when
  *   A_prev, B_cur and G are not asked for, three launches do the work: the
  *   top-16 in partial lists beside the gate GEMM; the candidate GEMM, each of

@@ -211,10 +211,13 @@ def test_select_path_route_by_shape():
     bf, f32 = torch.bfloat16, torch.float32
     V = 151936
     assert ds.select_path_route(1, 16, V, bf, 2560, 256) == ds.ROUTE_SMALL
-    assert ds.select_path_route(8, 16, V, bf, 2560, 256) == ds.ROUTE_SMALL
+    assert ds.select_path_route(2, 16, V, bf, 2560, 256) == ds.ROUTE_SMALL  # 32 positions
+    assert ds.select_path_route(32, 1, V, bf, 2560, 256) == ds.ROUTE_SMALL
+    assert ds.select_path_route(3, 16, V, bf, 2560, 256) == ds.ROUTE_SEPARATE  # 48 positions
+    assert ds.select_path_route(8, 16, V, bf, 2560, 256) == ds.ROUTE_SEPARATE
     assert ds.select_path_route(2, 16, V, f32, 2560, 96) == ds.ROUTE_SMALL
     assert ds.select_path_route(1, 16, V, bf, 2560, 256, want_AB=True) == ds.ROUTE_SEPARATE
-    assert ds.select_path_route(9, 16, V, bf, 2560, 256) == ds.ROUTE_SEPARATE  # 144 positions
+    assert ds.select_path_route(9, 16, V, bf, 2560, 256) == ds.ROUTE_SEPARATE
     assert ds.select_path_route(4, 8, 1024, f32, 64, 32) == ds.ROUTE_SEPARATE  # d 64: one K step, no split
     assert ds.select_path_route(64, 16, V, bf, 2560, 256) == ds.ROUTE_FUSED
     assert ds.select_path_route(256, 16, 202048, f32, 6144, 256, want_AB=True) == ds.ROUTE_FUSED

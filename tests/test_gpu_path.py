@@ -81,24 +81,24 @@ def test_path_equals_separate_calls(dev, name, mode, ragged):
 SMALL_CASES = {
     # one block of 16 (the latency shape), both walks
     "c1": (synth.CONFIGS["c1"], None),
-    # three blocks, one empty and one short
-    "c1x3": (synth.CONFIGS["c1"].replace(batch=3), [16, 5, 0]),
-    # eight blocks of the 5 / 8 / 16 mix (the top-16 rows split fewer ways)
-    "c1x8": (synth.CONFIGS["c1"].replace(batch=8), "mix"),
+    # four blocks of 8, one empty and one short
+    "c1x4": (synth.CONFIGS["c1"].replace(batch=4, block=8), [8, 5, 0, 3]),
+    # two blocks at lengths of the 5 / 8 / 16 mix (the top-16 rows split fewer ways)
+    "c1x2": (synth.CONFIGS["c1"].replace(batch=2), [8, 5]),
     # blocks of 8 at d 5120, sampled
-    "c3x6": (synth.CONFIGS["c3"].replace(batch=6), None),
+    "c3x4": (synth.CONFIGS["c3"].replace(batch=4), None),
     # rank 96: groups of 32 columns, 32-wide candidate tiles
     "r96": (synth.CONFIGS["c1"].replace(batch=2, r=96), None),
     # fp32 logits
     "f32": (synth.CONFIGS["c1"].replace(batch=2, logits_dtype="f32"), None),
-    # the longest blocks (32 positions) at rank 160: five groups of 32 columns
-    "L32r160": (synth.CONFIGS["c1"].replace(batch=3, block=32, r=160), [32, 7, 19]),
+    # the longest block (32 positions) at rank 160: five groups of 32 columns
+    "L32r160": (synth.CONFIGS["c1"].replace(batch=1, block=32, r=160), [29]),
     # blocks of one position: every step starts from the verified token
-    "L1": (synth.CONFIGS["c1"].replace(batch=100, block=1), None),
+    "L1": (synth.CONFIGS["c1"].replace(batch=32, block=1), None),
 }
 
 
-@pytest.mark.parametrize("case,mode", [("c1", 0), ("c1", 1), ("c1x3", 0), ("c1x8", 1), ("c3x6", 1), ("r96", 0),
+@pytest.mark.parametrize("case,mode", [("c1", 0), ("c1", 1), ("c1x4", 0), ("c1x2", 1), ("c3x4", 1), ("r96", 0),
                                        ("f32", 1), ("L32r160", 1), ("L1", 0)])
 def test_small_batch_route_equals_separate_calls(dev, case, mode):
     """The three-launch route of small batches (top-16 beside the gate GEMM;
