@@ -10,9 +10,9 @@
 // against the value of its 16th key: almost every chunk fails that single
 // compare, and the rare survivors are inserted one at a time (a DPP shift of
 // the list).  The first chunk of a wave seeds the list with its sorted lane
-// maxima (the 16 best of them bound the rest).  Loads are triple-buffered in
-// registers, so a chunk's HBM latency hides behind the previous chunks'
-// filters.  Waves merge through LDS with a 64-key bitonic sort (DPP and
+// maxima (the 16 best of them bound the rest).  Loads are buffered three or
+// four deep in registers, so a chunk's HBM latency hides behind the previous
+// chunks' filters.  Waves merge through LDS with a 64-key bitonic sort (DPP and
 // permlane swaps); split rows merge in a second kernel, one workgroup per row.
 // On a ragged batch the real rows are compacted onto the first workgroups of
 // the padded grid (live_position), so that they spread evenly over the chip.
@@ -25,9 +25,13 @@
 #endif
 // Register buffers per wave: DEPTH - 1 chunks in flight while one is filtered
 // (MI355X, 1,024 bf16 rows of 151,936: 3 is 1-2 us faster than 2, and 4-5 us
-// faster on ragged batches of the 5 / 8 / 16 mix).
-#ifndef DSEL_TOPK_DEPTH
-#define DSEL_TOPK_DEPTH 3
+// faster on ragged batches of the 5 / 8 / 16 mix; 4 is 1.2 us faster again,
+// 2.2 us at 1,024 rows of 152,064; fp32 rows of 202,048 level between 3 and 4).
+#ifndef DSEL_TOPK_DEPTH_BF16
+#define DSEL_TOPK_DEPTH_BF16 4
+#endif
+#ifndef DSEL_TOPK_DEPTH_F32
+#define DSEL_TOPK_DEPTH_F32 3
 #endif
 // Waves per row workgroup, 4 or 8 (MI355X, 1,024 bf16 rows of 151,936: 54.5 us
 // at 4 waves against 60.3 at 8, which doubles each row's loads in flight).
@@ -337,38 +341,61 @@ __device__ __forceinline__ void topk16_block(const TopkParams &p, int64_t bid) {
     if (vb < ve) {
         const int64_t nch = (ve - vb + CS - 1) / CS;
 #endif
-#if DSEL_TOPK_DEPTH == 3
-        // three register buffers: two chunks in flight while one is filtered
-        u32x4 wa[U], wb2[U], wc[U];
-        load_chunk<U>(wa, vbase, vb, ve);
-        load_chunk<U>(wb2, vbase, vb + CS, ve);
-        load_chunk<U>(wc, vbase, vb + 2 * CS, ve);
-        chunk_seed<BF16, U>(st, wa, vb, ve, h0);
-        for (int64_t c = 1; c < nch; c += 3) {
-            const int64_t v0 = vb + c * CS;
-            load_chunk<U>(wa, vbase, v0 + 2 * CS, ve);
-            chunk_filter<BF16, U>(st, wb2, v0, ve, h0);
-            if (c + 1 >= nch) break;
-            load_chunk<U>(wb2, vbase, v0 + 3 * CS, ve);
-            chunk_filter<BF16, U>(st, wc, v0 + CS, ve, h0);
-            if (c + 2 >= nch) break;
-            load_chunk<U>(wc, vbase, v0 + 4 * CS, ve);
-            chunk_filter<BF16, U>(st, wa, v0 + 2 * CS, ve, h0);
+        constexpr int DEPTH = BF16 ? DSEL_TOPK_DEPTH_BF16 : DSEL_TOPK_DEPTH_F32;
+        static_assert(DEPTH >= 2 && DEPTH <= 4, "top-16 stream depth");
+        if constexpr (DEPTH == 4) {
+            u32x4 wa[U], wb2[U], wc[U], wd[U];
+            load_chunk<U>(wa, vbase, vb, ve);
+            load_chunk<U>(wb2, vbase, vb + CS, ve);
+            load_chunk<U>(wc, vbase, vb + 2 * CS, ve);
+            load_chunk<U>(wd, vbase, vb + 3 * CS, ve);
+            chunk_seed<BF16, U>(st, wa, vb, ve, h0);
+            for (int64_t c = 1; c < nch; c += 4) {
+                const int64_t v0 = vb + c * CS;
+                load_chunk<U>(wa, vbase, v0 + 3 * CS, ve);
+                chunk_filter<BF16, U>(st, wb2, v0, ve, h0);
+                if (c + 1 >= nch) break;
+                load_chunk<U>(wb2, vbase, v0 + 4 * CS, ve);
+                chunk_filter<BF16, U>(st, wc, v0 + CS, ve, h0);
+                if (c + 2 >= nch) break;
+                load_chunk<U>(wc, vbase, v0 + 5 * CS, ve);
+                chunk_filter<BF16, U>(st, wd, v0 + 2 * CS, ve, h0);
+                if (c + 3 >= nch) break;
+                load_chunk<U>(wd, vbase, v0 + 6 * CS, ve);
+                chunk_filter<BF16, U>(st, wa, v0 + 3 * CS, ve, h0);
+            }
+        } else if constexpr (DEPTH == 3) {
+            // three register buffers: two chunks in flight while one is filtered
+            u32x4 wa[U], wb2[U], wc[U];
+            load_chunk<U>(wa, vbase, vb, ve);
+            load_chunk<U>(wb2, vbase, vb + CS, ve);
+            load_chunk<U>(wc, vbase, vb + 2 * CS, ve);
+            chunk_seed<BF16, U>(st, wa, vb, ve, h0);
+            for (int64_t c = 1; c < nch; c += 3) {
+                const int64_t v0 = vb + c * CS;
+                load_chunk<U>(wa, vbase, v0 + 2 * CS, ve);
+                chunk_filter<BF16, U>(st, wb2, v0, ve, h0);
+                if (c + 1 >= nch) break;
+                load_chunk<U>(wb2, vbase, v0 + 3 * CS, ve);
+                chunk_filter<BF16, U>(st, wc, v0 + CS, ve, h0);
+                if (c + 2 >= nch) break;
+                load_chunk<U>(wc, vbase, v0 + 4 * CS, ve);
+                chunk_filter<BF16, U>(st, wa, v0 + 2 * CS, ve, h0);
+            }
+        } else {
+            u32x4 wa[U], wb2[U];
+            load_chunk<U>(wa, vbase, vb, ve);
+            load_chunk<U>(wb2, vbase, vb + CS, ve);
+            chunk_seed<BF16, U>(st, wa, vb, ve, h0);
+            for (int64_t c = 1; c < nch; c += 2) {
+                const int64_t v0 = vb + c * CS;
+                load_chunk<U>(wa, vbase, v0 + CS, ve);
+                chunk_filter<BF16, U>(st, wb2, v0, ve, h0);
+                if (c + 1 >= nch) break;
+                load_chunk<U>(wb2, vbase, v0 + 2 * CS, ve);
+                chunk_filter<BF16, U>(st, wa, v0 + CS, ve, h0);
+            }
         }
-#else
-        u32x4 wa[U], wb2[U];
-        load_chunk<U>(wa, vbase, vb, ve);
-        load_chunk<U>(wb2, vbase, vb + CS, ve);
-        chunk_seed<BF16, U>(st, wa, vb, ve, h0);
-        for (int64_t c = 1; c < nch; c += 2) {
-            const int64_t v0 = vb + c * CS;
-            load_chunk<U>(wa, vbase, v0 + CS, ve);
-            chunk_filter<BF16, U>(st, wb2, v0, ve, h0);
-            if (c + 1 >= nch) break;
-            load_chunk<U>(wb2, vbase, v0 + 2 * CS, ve);
-            chunk_filter<BF16, U>(st, wa, v0 + CS, ve, h0);
-        }
-#endif
     }
     if (gw == 0) {  // head and tail elements outside the whole vectors
         int64_t idx = -1;
