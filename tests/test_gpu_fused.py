@@ -82,7 +82,9 @@ def _bits_equal(a, b, keys, lens=None):
 SHAPES = [  # (batch, block, r): tiles of 1, 2, 3 and 16 blocks, every column-group width
     (256, 8, 32), (64, 16, 256), (192, 5, 64), (2048, 1, 32), (96, 12, 128), (130, 16, 224), (136, 7, 96),
 ]
-WIDE = [(256, 16, 256), (1536, 5, 128)]  # the wide tile: blocks of 16 at r = 256; 3 blocks per tile at r = 128
+# the wide tile: blocks of 16 at r = 256; 3 blocks per tile at r = 128; 386 tiles (the grid
+# rounds up to 392 for the XCD order) whose last holds one block of two
+WIDE = [(256, 16, 256), (1536, 5, 128), (771, 8, 256)]
 
 
 def test_wide_shapes_take_the_wide_tile():
