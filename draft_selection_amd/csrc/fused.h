@@ -4,7 +4,8 @@
 // every adjacent candidate pair in one parallel pass.)
 //
 // A workgroup owns whole draft blocks (a tile of up to 16 positions, 256
-// gathered candidate rows E[cand]) and one group of CW columns of the rank.
+// gathered candidate rows E[cand]) and one group of CW columns of the rank
+// (two on the wide tile, below).
 // It computes, on bf16 MFMA with fp32 accumulation, both sides of that group:
 //     A(x)[c] = W_A[c] . E[x]   and   B(x)[c] = W_B[c] . E[x],  c in the group,
 // for every candidate x of the tile (a 256 x 2 CW tile; the main loop is the
@@ -26,7 +27,7 @@
 // Workgroup order is XCD-aware: the nq groups of one tile run on one XCD, so
 // its gathered rows come from HBM once and from that XCD's L2 afterwards.
 //
-// Large batches take a wide tile: one workgroup computes two groups (a
+// Large uniform batches take a wide tile: one workgroup computes two groups (a
 // 256 x 4 CW tile, wave tile 128 x CW instead of 64 x CW), so per MFMA it
 // reads three quarters of the fragments from LDS and moves two thirds of the
 // DMA bytes, and the grid has half as many workgroups, each with its setup and

@@ -289,12 +289,11 @@ __device__ __forceinline__ void mma_tile_dma_src(const uint16_t *const (&xsrc)[T
 
 // The same product with a leaner register footprint: fragments are read one
 // 16-deep slice ahead (two sets of TM + TN fragments instead of two whole K
-// steps), for kernels that keep other state live beside the GEMM or own wide
-// wave tiles.  While slice s multiplies, slice s+1 is read; at a step's last
-// slice the wave waits for its own reads and its DMA of the next step, meets
-// the others at the barrier, refills the stage NS steps ahead and reads the
-// next step's first fragments ahead of the last slice's MFMAs.  NS = 2 (a
-// two-stage ring) leaves one step of lead for the DMA.
+// steps), for kernels that keep other state live beside the GEMM.  While
+// slice s multiplies, slice s+1 is read; at a step's last slice the wave
+// waits for its own reads and its DMA of the next step, meets the others at
+// the barrier, refills the stage NS steps ahead and reads the next step's
+// first fragments ahead of the last slice's MFMAs.
 template <class T, int NS = 3>
 __device__ __forceinline__ void mma_tile_dma_lean_src(const uint16_t *const (&xsrc)[T::DXI],
                                                       const uint16_t *const (&wsrc)[T::DWI], int k0, int k1,
