@@ -255,6 +255,25 @@ dsel_status launch_gate_reduce(const GatePlan &g, dsel_stream_t stream) {
                   0, stream);
 }
 
+// The gate's split-K reduction and the top-16 (the reduction is needed only
+// after the top-16).  Where the top-16 is one round of workgroups (at most
+// DSEL_FOLD_MAX_TOPK_WG: four rows per CU), the reduction rides in its
+// launch as extra workgroups, beside it; beyond, those workgroups would land
+// on the last round, so the reduction is a launch of its own before it
+// (MI355X: 1,024 bf16 rows, folded 120.8 / 160.8 us per step against
+// 124.6 / 164.1 at the two shapes of 1,024 rows; 4,096 fp32 rows, 912.1 us
+// separate against 921.0 folded).
+#ifndef DSEL_FOLD_MAX_TOPK_WG
+#define DSEL_FOLD_MAX_TOPK_WG 1024
+#endif
+dsel_status launch_topk_and_gate_reduce(const TopkPlan &t, const GatePlan &g, dsel_stream_t stream) {
+    const int64_t ge = gate_reduce_units(g);
+    if (ge == 0 || t.p.rows * t.p.nsplit <= DSEL_FOLD_MAX_TOPK_WG)
+        return launch_topk(t, ge ? &g.p : nullptr, ge, stream);
+    dsel_status st = launch_gate_reduce(g, stream);
+    return st == DSEL_OK ? launch_topk(t, nullptr, 0, stream) : st;
+}
+
 dsel_status project_gate_impl(const uint16_t *E, int64_t vocab, int64_t d, const uint16_t *W_A,
                               const uint16_t *W_H, int64_t r, const uint16_t *h, const int32_t *verified,
                               int64_t batch, int64_t block, const int32_t *block_len, float *A_prev, float *G,
@@ -896,10 +915,7 @@ DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_a
         q.p.r = (int)a->r;
         q.p.S = a->S;
         st = launch_gate_gemm(g, stream);
-        if (st == DSEL_OK) {
-            const int64_t ge = gate_reduce_units(g);
-            st = launch_topk(t, ge ? &g.p : nullptr, ge, stream);
-        }
+        if (st == DSEL_OK) st = launch_topk_and_gate_reduce(t, g, stream);
         if (st == DSEL_OK) st = launch_fused(f, stream);
         if (st == DSEL_OK) st = launch_walk(q.p, stream);
         return st;
@@ -927,10 +943,7 @@ DSEL_API dsel_status dsel_select_path(const dsel_path_args *a, const dsel_walk_a
         st = plan_pairs(a->cand_u, A_prev, B_cur, G, a->batch, a->block, a->block_len, a->r, S, walk, &q);
     if (st != DSEL_OK) return st;
     st = launch_gate_gemm(g, stream);
-    if (st == DSEL_OK) {
-        const int64_t ge = gate_reduce_units(g);
-        st = launch_topk(t, ge ? &g.p : nullptr, ge, stream);
-    }
+    if (st == DSEL_OK) st = launch_topk_and_gate_reduce(t, g, stream);
     if (st == DSEL_OK) st = launch_cand(c, stream);
     if (st == DSEL_OK) st = launch_pairs(q, stream);
     return st;
